@@ -1,0 +1,179 @@
+"""Benchmark of the block-causal attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload magi4.5b]
+
+One step = the whole hot path over one batch of synthetic input already
+resident in HBM: mask -> AttnSlices (host), atomic-free schedule (host) and
+its upload, the QK-Norm + 3D-RoPE prologue kernel on Q and K, and the
+Flex-Flash-Attention forward kernel.  The metric counts masked FLOPs,
+4 * head_dim * query_heads * (visible query-key pairs), per second.
+
+Prints ONE JSON line.  ``roofline`` describes the attention kernel (the
+dominant one) from HIP events recorded around each of its launches on the
+stream it runs on; ``cpu_baseline`` times the float64 oracle on a bounded
+sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-causal attn fwd TFLOPS (masked FLOPs) and % of MI355X bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def visible_pairs(wl) -> int:
+    """Visible (query, key) pairs per head, from the chunk arithmetic."""
+    total = 0
+    for s in wl.seqs:
+        first = s.num_kv_chunks - s.num_q_chunks
+        for j in range(s.num_q_chunks):
+            c = first + j
+            r = s.kv_range[j]
+            lo = 0 if r < 0 else max(0, c - r)
+            total += s.chunk_len * s.chunk_len * (c + 1 - lo)
+    return total
+
+
+def masked_flops(wl) -> float:
+    return 4.0 * wl.head_dim * wl.hq * visible_pairs(wl)
+
+
+def run_gpu(wl, steps, warmup, seed=0):
+    import torch
+    import workloads as W
+    from block_causal_attention_amd import ops
+
+    dev = "cuda"
+    inp = W.make_inputs(wl, seed)
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    gq, gk, pq, pk = (t.to(dev) for t in (inp.gain_q, inp.gain_k, inp.pos_q, inp.pos_k))
+    base = torch.tensor(wl.rope_base, dtype=torch.float32, device=dev)
+    tdt = q.dtype
+    qh, kh = torch.empty_like(q), torch.empty_like(k)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(record):
+        plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, tdt, dev)
+        ops.qknorm_rope(q, k, gq, gk, pq, pk, base, wl.eps, q_out=qh, k_out=kh)
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+        ops.ffa_fwd(qh, kh, v, plan, out=out, lse=lse)
+        if record:
+            b.record(stream)
+            ev.append((a, b))
+        return plan
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan = step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    return (t1 - t0) * 1e3 / steps, float(np.mean(kernel_ms)), plan.num_work
+
+
+def cpu_baseline(wl, target_s=15.0, seed=0):
+    """Time the float64 oracle on a seeded row sample (all heads) of the workload."""
+    import oracle
+    import workloads as W
+    from threadpoolctl import threadpool_info
+
+    inp = W.make_inputs(wl, seed)
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    K, V, gk = f64(inp.k), f64(inp.v), f64(inp.gain_k)
+    gq = f64(inp.gain_q)
+
+    def run(rows):
+        mask = oracle.video_mask(wl.seqs, wl.nq, wl.nk, rows)
+        t = time.perf_counter()
+        oracle.forward(f64(inp.q[rows]), K, V, gq, gk, inp.pos_q[rows].numpy(), inp.pos_k.numpy(),
+                       wl.rope_base, wl.eps, mask, wl.softmax_scale)
+        return time.perf_counter() - t, int(mask.sum())
+
+    rng = np.random.Generator(np.random.PCG64(seed))
+    probe = np.sort(rng.choice(wl.nq, 16, replace=False))
+    dt, _ = run(probe)
+    n = int(np.clip(16 * target_s / max(dt, 1e-3), 16, wl.nq))
+    rows = np.sort(rng.choice(wl.nq, n, replace=False))
+    dt, pairs = run(rows)
+    flops = 4.0 * wl.head_dim * wl.hq * pairs
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} random query rows x {wl.hq} heads of {wl.name} (float64 numpy, "
+                      f"{dt:.1f} s, incl. QK-Norm+RoPE of all {wl.nk} keys)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="magi4.5b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the attention path has no "
+              "multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    wl = W.make_workload(args.workload)
+    flops = masked_flops(wl)
+    ms_step, ms_kernel, nwork = run_gpu(wl, args.steps, args.warmup)
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "fp32",
+        "data": "synthetic (seeded N(0,1) Q/K/V, U(0.8,1.2) QK-Norm gains; no weights)",
+        "config": {"workload": wl.name, "description": wl.description, "tokens": wl.nq,
+                   "query_heads": wl.hq, "kv_groups": wl.hkv, "head_dim": wl.head_dim,
+                   "masked_flops_per_step": flops, "work_items": nwork, "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "ffa_fwd_bf16", "avg_launch_ms": round(ms_kernel, 5)},
+    }
+    if not args.no_secondary and wl.name == "magi4.5b":
+        wl2 = W.make_workload("magi24b")
+        f2 = masked_flops(wl2)
+        s2, k2, _ = run_gpu(wl2, max(3, args.steps // 2), 2)
+        rec["secondary"] = {"workload": wl2.name, "ms_per_step": round(s2, 4),
+                            "value": round(f2 / (s2 * 1e-3) / 1e12, 2), "kernel_tflops": round(f2 / (k2 * 1e-3) / 1e12, 2),
+                            "pct_of_bf16_peak": round(100.0 * f2 / (k2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

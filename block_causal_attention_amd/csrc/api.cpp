@@ -1,0 +1,129 @@
+// C entry points of the device half of libmagi_bca: argument validation on
+// the host (before any HIP call), then one kernel launch on the caller's
+// stream.  The library allocates nothing and never synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+#include "status.h"
+
+using namespace magi;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(int32_t dtype) { return dtype == MAGI_DTYPE_BF16 ? 2 : 4; }
+
+int32_t check_common(int32_t head_dim, int32_t dtype) {
+  if (dtype != MAGI_DTYPE_BF16 && dtype != MAGI_DTYPE_FP32) return fail(MAGI_ERR_INVALID_ARG, "bad dtype %d", dtype);
+  if (head_dim != 24 && head_dim != 48)
+    return fail(MAGI_ERR_UNSUPPORTED, "head_dim %d unsupported (24 or 48)", head_dim);
+  return MAGI_OK;
+}
+
+int32_t check_tensor(const char* name, const void* p, int64_t n, int32_t heads, int64_t stride, int32_t head_dim,
+                     int32_t dtype) {
+  if (n < 0 || n > INT32_MAX) return fail(MAGI_ERR_INVALID_ARG, "%s: row count %lld not in [0, 2^31)", name, (long long)n);
+  if (heads < 1) return fail(MAGI_ERR_INVALID_ARG, "%s: heads %d < 1", name, heads);
+  if (stride < (int64_t)heads * head_dim)
+    return fail(MAGI_ERR_INVALID_ARG, "%s: row stride %lld < heads*head_dim = %lld", name, (long long)stride,
+                (long long)heads * head_dim);
+  if ((stride * elem_size(dtype)) % 16)
+    return fail(MAGI_ERR_INVALID_ARG, "%s: row stride must be a multiple of 16 bytes", name);
+  if (n > 0 && p == nullptr) return fail(MAGI_ERR_INVALID_ARG, "%s is NULL", name);
+  if (n > 0 && !aligned16(p)) return fail(MAGI_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return MAGI_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, int32_t hq, int64_t q_tok_stride,
+                                    const void* k_in, void* k_out, int64_t nk, int32_t hkv, int64_t k_tok_stride,
+                                    int32_t head_dim, int32_t dtype, const float* gain_q, const float* gain_k,
+                                    int32_t gain_head_stride, float eps, const int32_t* pos_q,
+                                    const int32_t* pos_k, const float* rope_base, void* stream) {
+  int32_t st;
+  if ((st = check_common(head_dim, dtype)) != MAGI_OK) return st;
+  if ((st = check_tensor("q_in", q_in, nq, hq, q_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
+  if ((st = check_tensor("q_out", q_out, nq, hq, q_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
+  if (nk > 0) {
+    if ((st = check_tensor("k_in", k_in, nk, hkv, k_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
+    if ((st = check_tensor("k_out", k_out, nk, hkv, k_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
+    if (gain_k == nullptr || pos_k == nullptr) return fail(MAGI_ERR_INVALID_ARG, "gain_k / pos_k is NULL");
+  } else if (nk < 0) {
+    return fail(MAGI_ERR_INVALID_ARG, "nk < 0");
+  }
+  if (nq > 0 && (gain_q == nullptr || pos_q == nullptr)) return fail(MAGI_ERR_INVALID_ARG, "gain_q / pos_q is NULL");
+  if (gain_head_stride != 0 && gain_head_stride != head_dim)
+    return fail(MAGI_ERR_INVALID_ARG, "gain_head_stride must be 0 or head_dim");
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MAGI_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (rope_base == nullptr) return fail(MAGI_ERR_INVALID_ARG, "rope_base is NULL");
+
+  QkArgs a{};
+  a.side[0] = {q_in, q_out, nq, hq, q_tok_stride, gain_q, pos_q};
+  a.side[1] = {k_in, k_out, nk > 0 ? nk : 0, nk > 0 ? hkv : 1, k_tok_stride, gain_k, pos_k};
+  a.head_dim = head_dim;
+  a.dtype = dtype;
+  a.gain_head_stride = gain_head_stride;
+  a.eps = eps;
+  a.rope_base = rope_base;
+  const hipError_t e = launch_qknorm_rope(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MAGI_ERR_HIP, "qknorm_rope launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t nq,
+                                int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
+                                int64_t q_tok_stride, int64_t kv_tok_stride, int64_t o_tok_stride,
+                                float softmax_scale, const magi_attn_slice* slices, int32_t num_slices,
+                                const magi_work_item* work, int32_t num_work, const int32_t* tile_slices,
+                                int32_t num_tile_slices, void* stream) {
+  int32_t st;
+  if ((st = check_common(head_dim, dtype)) != MAGI_OK) return st;
+  if (hq < 1 || hkv < 1) return fail(MAGI_ERR_INVALID_ARG, "hq and hkv must be >= 1");
+  if (hq % hkv) return fail(MAGI_ERR_INVALID_ARG, "hq %% hkv != 0 (hq=%d hkv=%d)", hq, hkv);
+  if (hq / hkv > 256) return fail(MAGI_ERR_UNSUPPORTED, "group size %d > 256", hq / hkv);
+  if ((st = check_tensor("q", q, nq, hq, q_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
+  if ((st = check_tensor("out", out, nq, hq, o_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
+  if ((st = check_tensor("k", k, nk, hkv, kv_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
+  if ((st = check_tensor("v", v, nk, hkv, kv_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(MAGI_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
+    return fail(MAGI_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (num_slices < 0 || num_work < 0 || num_tile_slices < 0)
+    return fail(MAGI_ERR_INVALID_ARG, "negative list length");
+  if ((num_slices > 0 && slices == nullptr) || (num_work > 0 && work == nullptr) ||
+      (num_tile_slices > 0 && tile_slices == nullptr))
+    return fail(MAGI_ERR_INVALID_ARG, "a non-empty list pointer is NULL");
+  if (num_work > 0 && nq == 0) return fail(MAGI_ERR_INVALID_ARG, "work items given for an empty query tensor");
+
+  FfaArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.nq = nq;
+  a.nk = nk;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.head_dim = head_dim;
+  a.dtype = dtype;
+  a.q_stride = q_tok_stride;
+  a.kv_stride = kv_tok_stride;
+  a.o_stride = o_tok_stride;
+  a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  a.slices = slices;
+  a.num_slices = num_slices;
+  a.work = work;
+  a.num_work = num_work;
+  a.tile_slices = tile_slices;
+  a.num_tile_slices = num_tile_slices;
+  const hipError_t e = launch_ffa_fwd(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MAGI_ERR_HIP, "ffa_fwd launch: %s", hipGetErrorString(e));
+  return ok();
+}

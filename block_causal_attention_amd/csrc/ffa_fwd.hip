@@ -1,0 +1,352 @@
+// Flex-Flash-Attention forward for gfx950 (MI355X).
+//
+// What is computed: softmax attention over the union of AttnSlices listed by
+// each work item (the FFA formulation on the MAGI-1 pages: study notes on
+// zhao9797.github.io, "训练 Infra"; 量子位 article on dakule.com,
+// "Flex-Flash-Attention"), with 128 query heads over 8 KV groups (study notes,
+// "模型规格（Table 2）").  The pages' kernel is built on FlashAttention-3 for
+// Hopper (TMA, slice-level parallelism, atomics); this one is designed for
+// CDNA4 and needs no atomics because every work item owns its output rows.
+//
+// bf16 kernel layout (one workgroup = one work item = up to 256 query rows):
+//  * GQA packing: the 16 query heads of a KV group share K and V, so a query
+//    "row" is a (token, head) pair and the item's rows are tile_q tokens x 16
+//    heads.  Each of the 4 waves owns 64 rows as two 32-row MFMA column blocks.
+//  * Scores are computed transposed, S^T = K . Q^T, with
+//    v_mfma_f32_32x32x16_bf16: keys run along the MFMA M axis and rows along
+//    N, so every lane holds 16 scores of one row.  The row max needs only
+//    in-register max plus one exchange between the two lane halves.
+//  * The output is also kept transposed, O^T = V^T . P^T: P^T is exactly the
+//    B operand layout of the next MFMA (the score accumulator of one lane
+//    half holds keys {4h..4h+3, 8+4h..8+4h+3} of each 16-key step, which is a
+//    valid k-slot assignment), so P never leaves registers.  The V^T operand
+//    is read from a row-major V tile in LDS with ds_read_b64_tr_b16.
+//  * head_dim is padded for the MFMA: the Q.K contraction to a multiple of 16
+//    (24 -> 32, 48 stays 48), the V rows to a multiple of 32 (24 -> 32,
+//    48 -> 64).  The first padding column of V holds 1.0, so the same MFMA
+//    that accumulates P.V also accumulates the softmax denominator sum(P)
+//    (of the bf16-rounded P actually used), at no VALU cost.
+//  * K/V tiles of 64 keys are staged in LDS once and read by all 4 waves
+//    (64 query heads x tokens).  Tiles wholly outside the visible range are
+//    never visited; only tiles crossing a range end or a causal diagonal pay
+//    for element masking.
+//  * Online softmax in fp32 in the log2 domain (scale * log2(e) folded into
+//    one multiply), exp via v_exp_f32.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace magi {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kThreads = 256;
+constexpr int kRows = 256;  // query rows per work item
+constexpr int TK = 64;      // keys per LDS tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -1e30f;  // finite "minus infinity" for the running max
+
+template <int D>
+struct Cfg {
+  static constexpr int DK = (D + 15) / 16 * 16;       // Q.K contraction length
+  static constexpr int KS = DK / 16;                  // MFMA k-steps for Q.K
+  static constexpr int DV = (D + 1 + 31) / 32 * 32;   // V columns incl. the ones column
+  static constexpr int MB = DV / 32;                  // 32-row blocks of O^T
+  static constexpr int KROW = DK + 8;                 // LDS pitch of a K row (elements)
+  static constexpr int VROW = DV + 8;                 // LDS pitch of a V row (elements)
+  static constexpr int CH = D / 8;                    // 16-byte chunks per K/V row
+  // position of the denominator (the ones column, V column D) in the O^T
+  // accumulator of lane half 0: block D/32, index 4*((D%32)/8) + D%4
+  static constexpr int LMB = D / 32;
+  static constexpr int LIDX = 4 * ((D % 32) / 8) + (D % 4);
+  static_assert(((D % 32) / 4) % 2 == 0, "ones column must fall in lane half 0");
+};
+
+__device__ inline int64_t causal_end(const magi_attn_slice& s, int64_t ke, int64_t row) {
+  // bottom-right aligned causal: row r sees k with k - k_end <= r - q_end
+  const int64_t e = (int64_t)s.k_end - (int64_t)s.q_end + row + 1;
+  return e < ke ? e : ke;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void ffa_fwd_bf16(FfaArgs a) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[TK * C::KROW];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[TK * C::VROW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, ln = lane & 31;
+  const magi_work_item wi = a.work[blockIdx.x];
+  const int G = a.hq / a.hkv;
+  const int cap = kRows / G;
+  if (wi.q_start < 0 || wi.q_len <= 0 || (int64_t)wi.q_start + wi.q_len > a.nq || wi.kv_group < 0 ||
+      wi.kv_group >= a.hkv)
+    return;
+  const int qlen = wi.q_len < cap ? wi.q_len : cap;
+  const int g = wi.kv_group;
+  const __bf16* __restrict__ qp = reinterpret_cast<const __bf16*>(a.q);
+  const __bf16* __restrict__ kp = reinterpret_cast<const __bf16*>(a.k);
+  const __bf16* __restrict__ vp = reinterpret_cast<const __bf16*>(a.v);
+
+  // constant padding columns of the LDS tiles: K columns D..DK-1 are 0, V
+  // column D is 1 (denominator), V columns D+1..DV-1 are 0
+  if constexpr (C::DK > D)
+    for (int i = tid; i < TK * (C::DK - D); i += kThreads)
+      Ks[(i / (C::DK - D)) * C::KROW + D + i % (C::DK - D)] = (__bf16)0.0f;
+  for (int i = tid; i < TK * (C::DV - D); i += kThreads) {
+    const int c = D + i % (C::DV - D);
+    Vs[(i / (C::DV - D)) * C::VROW + c] = (__bf16)(c == D ? 1.0f : 0.0f);
+  }
+
+  // this lane's two query rows (one per 32-row column block)
+  int64_t qi[2];
+  int hg[2];
+  bool rvalid[2];
+  bf16x8 qreg[2][C::KS];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = wave * 64 + nb * 32 + ln;
+    const int t = n / G;
+    hg[nb] = n % G;
+    rvalid[nb] = (t < qlen);
+    qi[nb] = (int64_t)wi.q_start + (rvalid[nb] ? t : 0);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int d0 = 16 * ks + 8 * h;
+      bf16x8 x = {};
+      if (rvalid[nb] && d0 < D)
+        x = *reinterpret_cast<const bf16x8*>(qp + qi[nb] * a.q_stride + (int64_t)(g * G + hg[nb]) * D + d0);
+      qreg[nb][ks] = x;
+    }
+  }
+
+  const float c = a.scale * kLog2e;
+  float m[2] = {kNegBig, kNegBig};
+  f32x16 o[2][C::MB];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) o[nb][mb] = (f32x16){};
+
+  const int64_t first_tok = wi.q_start, last_tok = (int64_t)wi.q_start + qlen - 1;
+  for (int si = wi.slice_begin; si < wi.slice_end; ++si) {
+    if (si < 0 || si >= a.num_tile_slices) break;
+    const int sidx = a.tile_slices[si];
+    if (sidx < 0 || sidx >= a.num_slices) continue;
+    const magi_attn_slice sl = a.slices[sidx];
+    const int64_t ks = sl.k_start > 0 ? sl.k_start : 0;
+    const int64_t ke = sl.k_end < a.nk ? sl.k_end : a.nk;
+    if (ks >= ke) continue;
+    const bool causal = sl.mask_type == MAGI_MASK_CAUSAL;
+    const bool inq_first = first_tok >= sl.q_start && first_tok < sl.q_end;
+    const bool inq_last = last_tok >= sl.q_start && last_tok < sl.q_end;
+    if (!inq_first || !inq_last) continue;  // a well-formed schedule never does this
+    const int64_t khi = causal ? causal_end(sl, ke, last_tok) : ke;
+    const int64_t kfull = causal ? causal_end(sl, ke, first_tok) : ke;
+    int64_t re[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) re[nb] = !rvalid[nb] ? ks : (causal ? causal_end(sl, ke, qi[nb]) : ke);
+
+    for (int64_t kt = ks; kt < khi; kt += TK) {
+      __syncthreads();  // previous tile fully consumed (and padding columns written)
+      for (int ci = tid; ci < TK * C::CH; ci += kThreads) {
+        const int r = ci / C::CH, part = ci % C::CH;
+        const int64_t key = kt + r;
+        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+        if (key < khi) {
+          const int64_t off = key * a.kv_stride + (int64_t)g * D + part * 8;
+          kv = *reinterpret_cast<const uint4*>(kp + off);
+          vv = *reinterpret_cast<const uint4*>(vp + off);
+        }
+        *reinterpret_cast<uint4*>(&Ks[r * C::KROW + part * 8]) = kv;
+        *reinterpret_cast<uint4*>(&Vs[r * C::VROW + part * 8]) = vv;
+      }
+      __syncthreads();
+      const bool masked = (kt + TK > kfull);
+
+      // S^T = K . Q^T for 64 keys x 64 rows: s[kb][nb], lane holds 16 keys of one row
+      f32x16 s[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 kop[C::KS];
+#pragma unroll
+        for (int ks2 = 0; ks2 < C::KS; ++ks2)
+          kop[ks2] = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + ln) * C::KROW + 16 * ks2 + 8 * h]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          f32x16 acc = {};
+#pragma unroll
+          for (int ks2 = 0; ks2 < C::KS; ++ks2)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks2], qreg[nb][ks2], acc, 0, 0, 0);
+          s[kb][nb] = acc;
+        }
+      }
+
+      // online softmax (log2 domain)
+      bf16x8 pb[2][2][2];  // [kb][16-key half][nb]
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float x = s[kb][nb][i] * c;
+            if (masked) {
+              const int64_t key = kt + kb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+              if (key >= re[nb]) x = -INFINITY;
+            }
+            s[kb][nb][i] = x;
+            mx = fmaxf(mx, x);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m[nb], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[nb] - mnew);
+        m[nb] = mnew;
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) o[nb][mb] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              pb[kb][i2][nb][e] = (__bf16)__builtin_amdgcn_exp2f(s[kb][nb][8 * i2 + e] - mnew);
+      }
+
+      // O^T += V^T . P^T ; V^T operand through the LDS transpose read
+      const int li = lane & 15;
+      const int dgrp = ((lane >> 4) & 1) * 16;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+          const int krow = kb * 32 + 16 * i2 + 4 * h + li / 4;
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb) {
+            const int dcol = mb * 32 + dgrp + 4 * (li % 4);
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)((__attribute__((address_space(3))) __bf16*)Vs + krow * C::VROW + dcol));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)((__attribute__((address_space(3))) __bf16*)Vs + (krow + 8) * C::VROW + dcol));
+            const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+              o[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb][i2][nb], o[nb][mb], 0, 0, 0);
+          }
+        }
+    }
+  }
+
+  // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
+  __bf16* __restrict__ op = reinterpret_cast<__bf16*>(a.out);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const float mine = o[nb][C::LMB][C::LIDX];
+    const float other = __shfl_xor(mine, 32);
+    const float l = h == 0 ? mine : other;
+    if (!rvalid[nb]) continue;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const int64_t obase = qi[nb] * a.o_stride + (int64_t)(g * G + hg[nb]) * D;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const int d = mb * 32 + 8 * grp + 4 * h;
+        if (d < D) {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 w;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[r] = (__bf16)(o[nb][mb][4 * grp + r] * inv);
+          *reinterpret_cast<bf16x4*>(op + obase + d) = w;
+        }
+      }
+    if (a.lse != nullptr && h == 0)
+      a.lse[qi[nb] * a.hq + g * G + hg[nb]] = l > 0.f ? (m[nb] + __log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+// fp32 path (small shapes): one thread per query row, keys streamed from
+// global memory, fp32 online softmax.  Same work list and masking rules.
+template <int D>
+__global__ __launch_bounds__(kThreads) void ffa_fwd_f32(FfaArgs a) {
+  const magi_work_item wi = a.work[blockIdx.x];
+  const int G = a.hq / a.hkv;
+  const int cap = kRows / G;
+  if (wi.q_start < 0 || wi.q_len <= 0 || (int64_t)wi.q_start + wi.q_len > a.nq || wi.kv_group < 0 ||
+      wi.kv_group >= a.hkv)
+    return;
+  const int qlen = wi.q_len < cap ? wi.q_len : cap;
+  const int n = threadIdx.x, t = n / G, hgi = n % G, g = wi.kv_group;
+  if (t >= qlen) return;
+  const int64_t qi = (int64_t)wi.q_start + t;
+  const int head = g * G + hgi;
+  const float* qp = reinterpret_cast<const float*>(a.q) + qi * a.q_stride + (int64_t)head * D;
+  const float* kp = reinterpret_cast<const float*>(a.k);
+  const float* vp = reinterpret_cast<const float*>(a.v);
+  const float c = a.scale * kLog2e;
+  float qv[D], o[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    qv[i] = qp[i];
+    o[i] = 0.f;
+  }
+  float m = kNegBig, l = 0.f;
+  for (int si = wi.slice_begin; si < wi.slice_end; ++si) {
+    if (si < 0 || si >= a.num_tile_slices) break;
+    const int sidx = a.tile_slices[si];
+    if (sidx < 0 || sidx >= a.num_slices) continue;
+    const magi_attn_slice sl = a.slices[sidx];
+    if (qi < sl.q_start || qi >= sl.q_end) continue;
+    const int64_t ks = sl.k_start > 0 ? sl.k_start : 0;
+    const int64_t ke = sl.k_end < a.nk ? sl.k_end : a.nk;
+    const int64_t re = sl.mask_type == MAGI_MASK_CAUSAL ? causal_end(sl, ke, qi) : ke;
+    for (int64_t key = ks; key < re; ++key) {
+      const float* kr = kp + key * a.kv_stride + (int64_t)g * D;
+      const float* vr = vp + key * a.kv_stride + (int64_t)g * D;
+      float sdot = 0.f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) sdot = fmaf(qv[i], kr[i], sdot);
+      const float x = sdot * c;
+      const float mnew = fmaxf(m, x);
+      const float alpha = exp2f(m - mnew);
+      const float p = exp2f(x - mnew);
+      l = l * alpha + p;
+#pragma unroll
+      for (int i = 0; i < D; ++i) o[i] = fmaf(p, vr[i], o[i] * alpha);
+      m = mnew;
+    }
+  }
+  float* op = reinterpret_cast<float*>(a.out) + qi * a.o_stride + (int64_t)head * D;
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+  for (int i = 0; i < D; ++i) op[i] = o[i] * inv;
+  if (a.lse != nullptr) a.lse[qi * a.hq + head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_ffa_fwd(const FfaArgs& a, hipStream_t stream) {
+  if (a.num_work == 0) return hipSuccess;
+  const dim3 grid(a.num_work), block(kThreads);
+  if (a.dtype == MAGI_DTYPE_BF16) {
+    if (a.head_dim == 24)
+      hipLaunchKernelGGL(ffa_fwd_bf16<24>, grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL(ffa_fwd_bf16<48>, grid, block, 0, stream, a);
+  } else {
+    if (a.head_dim == 24)
+      hipLaunchKernelGGL(ffa_fwd_f32<24>, grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL(ffa_fwd_f32<48>, grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace magi

@@ -1,0 +1,53 @@
+// Launch interfaces of the HIP kernels of libmagi_bca (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "magi_bca.h"
+
+namespace magi {
+
+struct QkSide {
+  const void* in;
+  void* out;
+  int64_t n;           // tokens
+  int32_t heads;
+  int64_t tok_stride;  // elements between consecutive tokens
+  const float* gain;
+  const int32_t* pos;  // [n][3]
+};
+
+struct QkArgs {
+  QkSide side[2];  // Q, then K (side[1].n == 0 to skip)
+  int32_t head_dim;
+  int32_t dtype;
+  int32_t gain_head_stride;
+  float eps;
+  const float* rope_base;
+};
+
+hipError_t launch_qknorm_rope(const QkArgs& a, hipStream_t stream);
+
+struct FfaArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  int64_t nq, nk;
+  int32_t hq, hkv, head_dim, dtype;
+  int64_t q_stride, kv_stride, o_stride;
+  float scale;
+  const magi_attn_slice* slices;
+  int32_t num_slices;
+  const magi_work_item* work;
+  int32_t num_work;
+  const int32_t* tile_slices;
+  int32_t num_tile_slices;
+};
+
+hipError_t launch_ffa_fwd(const FfaArgs& a, hipStream_t stream);
+
+}  // namespace magi

@@ -1,0 +1,241 @@
+// Host half of libmagi_bca: the mask -> AttnSlice builder and the atomic-free
+// slice scheduler.  Pure C++17, no HIP calls.
+//
+// The AttnSlice formulation (a mask as a union of (q range, k range, full or
+// causal) rectangles) follows the Flex-Flash-Attention description on the
+// MAGI-1 pages (study notes on zhao9797.github.io, "训练 Infra"; 量子位 article
+// on dakule.com, "Flex-Flash-Attention").  The work estimate of a piece of the
+// mask is its visible area, the measure MagiAttention's dispatch solver
+// balances (interview with Zhang Zheng, answer on load balancing).
+#include <algorithm>
+#include <climits>
+#include <cstdint>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "status.h"
+
+namespace magi {
+
+std::string& last_error_slot() {
+  thread_local std::string msg;
+  return msg;
+}
+
+namespace {
+
+constexpr int kRowsPerTile = 256;  // query rows (tokens x heads of a group) per work item
+
+// Visible keys of row r under slice s: [s.k_start, row_end).
+inline int64_t row_end(const magi_attn_slice& s, int64_t r) {
+  if (s.mask_type == MAGI_MASK_FULL) return s.k_end;
+  int64_t e = (int64_t)s.k_end - (int64_t)s.q_end + r + 1;
+  return std::min<int64_t>(s.k_end, e);
+}
+
+inline int64_t row_count(const magi_attn_slice& s, int64_t r) {
+  return std::max<int64_t>(0, row_end(s, r) - s.k_start);
+}
+
+}  // namespace
+}  // namespace magi
+
+using namespace magi;
+
+extern "C" const char* magi_version(void) { return "magi_bca 0.1.0 (gfx950)"; }
+
+extern "C" const char* magi_last_error(void) { return last_error_slot().c_str(); }
+
+extern "C" int32_t magi_slices_build(const magi_seq_desc* seqs, int32_t num_seqs,
+                                     magi_attn_slice* slices, int32_t slice_cap,
+                                     int32_t* num_slices) {
+  if (num_slices == nullptr) return fail(MAGI_ERR_INVALID_ARG, "num_slices is NULL");
+  if (num_seqs < 0) return fail(MAGI_ERR_INVALID_ARG, "num_seqs < 0");
+  if (num_seqs > 0 && seqs == nullptr) return fail(MAGI_ERR_INVALID_ARG, "seqs is NULL");
+  if (slice_cap < 0) return fail(MAGI_ERR_INVALID_ARG, "slice_cap < 0");
+  if (slices == nullptr && slice_cap != 0) return fail(MAGI_ERR_INVALID_ARG, "slices is NULL but slice_cap > 0");
+
+  struct Span { int64_t a, b; int idx; };
+  std::vector<Span> qs, ks;
+  int64_t need = 0;
+  for (int i = 0; i < num_seqs; ++i) {
+    const magi_seq_desc& s = seqs[i];
+    if (s.chunk_len < 1) return fail(MAGI_ERR_INVALID_ARG, "seq %d: chunk_len %d < 1", i, s.chunk_len);
+    if (s.num_kv_chunks < 1) return fail(MAGI_ERR_INVALID_ARG, "seq %d: num_kv_chunks < 1", i);
+    if (s.num_q_chunks < 1 || s.num_q_chunks > s.num_kv_chunks)
+      return fail(MAGI_ERR_INVALID_ARG, "seq %d: num_q_chunks %d not in [1, num_kv_chunks]", i, s.num_q_chunks);
+    if (s.q_offset < 0 || s.k_offset < 0) return fail(MAGI_ERR_INVALID_ARG, "seq %d: negative offset", i);
+    int64_t qe = (int64_t)s.q_offset + (int64_t)s.num_q_chunks * s.chunk_len;
+    int64_t ke = (int64_t)s.k_offset + (int64_t)s.num_kv_chunks * s.chunk_len;
+    if (qe > INT32_MAX || ke > INT32_MAX) return fail(MAGI_ERR_INVALID_ARG, "seq %d: ranges exceed int32", i);
+    bool unlimited = true;
+    if (s.kv_range) {
+      for (int j = 0; j < s.num_q_chunks; ++j) {
+        if (s.kv_range[j] < -1) return fail(MAGI_ERR_INVALID_ARG, "seq %d: kv_range[%d] = %d < -1", i, j, s.kv_range[j]);
+        if (s.kv_range[j] >= 0) unlimited = false;
+      }
+    }
+    need += (s.chunk_len == 1 && unlimited) ? 1 : s.num_q_chunks;
+    qs.push_back({s.q_offset, qe, i});
+    ks.push_back({s.k_offset, ke, i});
+  }
+  for (auto* v : {&qs, &ks}) {
+    std::sort(v->begin(), v->end(), [](const Span& x, const Span& y) { return x.a < y.a; });
+    for (size_t j = 1; j < v->size(); ++j)
+      if ((*v)[j].a < (*v)[j - 1].b)
+        return fail(MAGI_ERR_OVERLAP, "videos %d and %d overlap in the %s index space", (*v)[j - 1].idx,
+                    (*v)[j].idx, v == &qs ? "query" : "key");
+  }
+  if (need > INT32_MAX) return fail(MAGI_ERR_INVALID_ARG, "too many slices");
+  *num_slices = (int32_t)need;
+  if (slices == nullptr && slice_cap == 0) return ok();
+  if (slice_cap < need) return fail(MAGI_ERR_BUFFER_TOO_SMALL, "slice_cap %d < %lld", slice_cap, (long long)need);
+
+  int32_t n = 0;
+  for (int i = 0; i < num_seqs; ++i) {
+    const magi_seq_desc& s = seqs[i];
+    const int32_t C = s.chunk_len;
+    const int32_t first = s.num_kv_chunks - s.num_q_chunks;
+    bool unlimited = true;
+    if (s.kv_range)
+      for (int j = 0; j < s.num_q_chunks; ++j) unlimited &= (s.kv_range[j] < 0);
+    if (C == 1 && unlimited) {
+      // one-token chunks with no KV limit: plain causal attention, which the
+      // bottom-right alignment also gives for a streaming query tail
+      slices[n++] = {s.q_offset, s.q_offset + s.num_q_chunks, s.k_offset, s.k_offset + s.num_kv_chunks,
+                     MAGI_MASK_CAUSAL};
+      continue;
+    }
+    for (int j = 0; j < s.num_q_chunks; ++j) {
+      const int32_t c = first + j;
+      const int32_t r = s.kv_range ? s.kv_range[j] : -1;
+      const int32_t lo = r < 0 ? 0 : std::max(0, c - r);
+      slices[n++] = {s.q_offset + j * C, s.q_offset + (j + 1) * C, s.k_offset + lo * C, s.k_offset + (c + 1) * C,
+                     MAGI_MASK_FULL};
+    }
+  }
+  return ok();
+}
+
+extern "C" int32_t magi_default_tile_q(int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype) {
+  if (hq <= 0 || hkv <= 0) return fail(MAGI_ERR_INVALID_ARG, "hq and hkv must be positive");
+  if (hq % hkv) return fail(MAGI_ERR_INVALID_ARG, "hq %% hkv != 0 (hq=%d hkv=%d)", hq, hkv);
+  if (dtype != MAGI_DTYPE_BF16 && dtype != MAGI_DTYPE_FP32) return fail(MAGI_ERR_INVALID_ARG, "bad dtype %d", dtype);
+  if (head_dim != 24 && head_dim != 48)
+    return fail(MAGI_ERR_UNSUPPORTED, "head_dim %d unsupported (24 or 48)", head_dim);
+  const int G = hq / hkv;
+  if (G > kRowsPerTile) return fail(MAGI_ERR_UNSUPPORTED, "group size %d > %d", G, kRowsPerTile);
+  return kRowsPerTile / G;
+}
+
+extern "C" int32_t magi_schedule(const magi_attn_slice* slices, int32_t num_slices, int64_t nq, int64_t nk,
+                                 int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype, int32_t tile_q,
+                                 magi_work_item* work, int32_t work_cap, int32_t* num_work, int32_t* tile_slices,
+                                 int32_t ts_cap, int32_t* num_tile_slices) {
+  if (num_work == nullptr || num_tile_slices == nullptr)
+    return fail(MAGI_ERR_INVALID_ARG, "num_work / num_tile_slices is NULL");
+  if (num_slices < 0) return fail(MAGI_ERR_INVALID_ARG, "num_slices < 0");
+  if (num_slices > 0 && slices == nullptr) return fail(MAGI_ERR_INVALID_ARG, "slices is NULL");
+  if (nq < 0 || nk < 0 || nq > INT32_MAX || nk > INT32_MAX)
+    return fail(MAGI_ERR_INVALID_ARG, "nq/nk must be in [0, 2^31)");
+  if (work_cap < 0 || ts_cap < 0) return fail(MAGI_ERR_INVALID_ARG, "negative capacity");
+  if ((work == nullptr) != (work_cap == 0) || (tile_slices == nullptr) != (ts_cap == 0))
+    return fail(MAGI_ERR_INVALID_ARG, "output array and capacity disagree (NULL needs cap 0)");
+  const int32_t dflt = magi_default_tile_q(hq, hkv, head_dim, dtype);
+  if (dflt < 0) return dflt;
+  if (tile_q < 0 || tile_q > dflt)
+    return fail(MAGI_ERR_INVALID_ARG, "tile_q %d not in [0, %d] for this shape", tile_q, dflt);
+  if (tile_q == 0) tile_q = dflt;
+
+  // validate slices
+  for (int i = 0; i < num_slices; ++i) {
+    const magi_attn_slice& s = slices[i];
+    if (s.mask_type != MAGI_MASK_FULL && s.mask_type != MAGI_MASK_CAUSAL)
+      return fail(MAGI_ERR_INVALID_ARG, "slice %d: unknown mask type %d", i, s.mask_type);
+    if (s.q_start < 0 || s.q_start > s.q_end || s.q_end > nq || s.k_start < 0 || s.k_start > s.k_end ||
+        s.k_end > nk)
+      return fail(MAGI_ERR_INVALID_ARG, "slice %d: range q[%d,%d) k[%d,%d) outside [0,%lld)x[0,%lld)", i,
+                  s.q_start, s.q_end, s.k_start, s.k_end, (long long)nq, (long long)nk);
+  }
+
+  // cut the query axis at every slice boundary
+  std::vector<int64_t> cuts = {0, nq};
+  for (int i = 0; i < num_slices; ++i)
+    if (slices[i].q_start < slices[i].q_end && slices[i].k_start < slices[i].k_end) {
+      cuts.push_back(slices[i].q_start);
+      cuts.push_back(slices[i].q_end);
+    }
+  std::sort(cuts.begin(), cuts.end());
+  cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+  const size_t nseg = cuts.size() - 1;
+  std::vector<std::vector<int32_t>> cover(nseg);
+  for (int i = 0; i < num_slices; ++i) {
+    const magi_attn_slice& s = slices[i];
+    if (s.q_start >= s.q_end || s.k_start >= s.k_end) continue;
+    size_t a = std::lower_bound(cuts.begin(), cuts.end(), (int64_t)s.q_start) - cuts.begin();
+    for (size_t g = a; g < nseg && cuts[g] < s.q_end; ++g) cover[g].push_back(i);
+  }
+
+  // overlap check: key ranges only grow with the row, so two slices that
+  // share a (q, k) pair anywhere in a segment share one on its last row
+  for (size_t g = 0; g < nseg; ++g) {
+    if (cover[g].size() < 2) continue;
+    const int64_t r = cuts[g + 1] - 1;
+    std::vector<std::pair<int64_t, int64_t>> iv;
+    std::vector<int32_t> who;
+    for (int32_t i : cover[g]) {
+      int64_t e = row_end(slices[i], r);
+      if (e > slices[i].k_start) iv.push_back({slices[i].k_start, e});
+    }
+    std::vector<size_t> ord(iv.size());
+    std::iota(ord.begin(), ord.end(), 0);
+    std::sort(ord.begin(), ord.end(), [&](size_t x, size_t y) { return iv[x] < iv[y]; });
+    for (size_t j = 1; j < ord.size(); ++j)
+      if (iv[ord[j]].first < iv[ord[j - 1]].second)
+        return fail(MAGI_ERR_OVERLAP, "slices overlap at query row %lld (key ranges [%lld,%lld) and [%lld,%lld))",
+                    (long long)r, (long long)iv[ord[j - 1]].first, (long long)iv[ord[j - 1]].second,
+                    (long long)iv[ord[j]].first, (long long)iv[ord[j]].second);
+  }
+  for (auto& c : cover)
+    std::sort(c.begin(), c.end(), [&](int32_t x, int32_t y) {
+      return slices[x].k_start != slices[y].k_start ? slices[x].k_start < slices[y].k_start : x < y;
+    });
+
+  // tiles
+  struct Tile { int64_t q0, len, cost; size_t seg; };
+  std::vector<Tile> tiles;
+  int64_t ts_total = 0;
+  for (size_t g = 0; g < nseg; ++g) {
+    for (int64_t t0 = cuts[g]; t0 < cuts[g + 1]; t0 += tile_q) {
+      const int64_t len = std::min<int64_t>(tile_q, cuts[g + 1] - t0);
+      int64_t cost = 0;
+      for (int32_t i : cover[g])
+        for (int64_t r = t0; r < t0 + len; ++r) cost += row_count(slices[i], r);
+      tiles.push_back({t0, len, cost, g});
+      ts_total += (int64_t)cover[g].size();
+    }
+  }
+  const int64_t nwork = (int64_t)tiles.size() * hkv;
+  if (nwork > INT32_MAX || ts_total > INT32_MAX) return fail(MAGI_ERR_INVALID_ARG, "work list exceeds int32");
+  *num_work = (int32_t)nwork;
+  *num_tile_slices = (int32_t)ts_total;
+  if (work == nullptr && tile_slices == nullptr) return ok();
+  if (work_cap < nwork || ts_cap < ts_total)
+    return fail(MAGI_ERR_BUFFER_TOO_SMALL, "need work_cap >= %lld and ts_cap >= %lld", (long long)nwork,
+                (long long)ts_total);
+
+  // heaviest tiles first; ties keep query order (deterministic)
+  std::vector<size_t> ord(tiles.size());
+  std::iota(ord.begin(), ord.end(), 0);
+  std::stable_sort(ord.begin(), ord.end(), [&](size_t x, size_t y) { return tiles[x].cost > tiles[y].cost; });
+  int32_t ts = 0, w = 0;
+  for (size_t rank = 0; rank < ord.size(); ++rank) {
+    const Tile& t = tiles[ord[rank]];
+    const int32_t sb = ts;
+    for (int32_t i : cover[t.seg]) tile_slices[ts++] = i;
+    for (int32_t g = 0; g < hkv; ++g)
+      work[w++] = {(int32_t)t.q0, (int32_t)t.len, sb, ts, g, (int32_t)std::min<int64_t>(t.cost, INT32_MAX)};
+  }
+  return ok();
+}

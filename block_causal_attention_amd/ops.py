@@ -1,0 +1,190 @@
+"""Thin torch binding over libmagi_bca's C ABI: argument marshalling only.
+
+Every step of the attention path runs in the library (host builder and
+scheduler in C++, prologue and attention in HIP kernels).  PyTorch supplies
+device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import AttnSlice, SeqDesc, WorkItem, check, lib
+
+__all__ = ["build_slices", "schedule", "Plan", "make_plan", "plan_for_videos", "qknorm_rope",
+           "ffa_fwd", "default_tile_q", "dtype_code"]
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return _lib.DTYPE_BF16
+    if dt == torch.float32:
+        return _lib.DTYPE_FP32
+    raise TypeError(f"unsupported dtype {dt} (bfloat16 or float32)")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def build_slices(seqs: Sequence) -> np.ndarray:
+    """magi_slices_build: packed-video descriptors -> int32 [n, 5] slices
+    (q_start, q_end, k_start, k_end, mask_type).  ``seqs`` items need the
+    fields chunk_len, num_kv_chunks, num_q_chunks, q_offset, k_offset and
+    kv_range (sequence of ints, or None)."""
+    n = len(seqs)
+    descs = (SeqDesc * max(n, 1))()
+    keep = []
+    for i, s in enumerate(seqs):
+        kvr = getattr(s, "kv_range", None)
+        arr = None
+        if kvr is not None:
+            arr = (C.c_int32 * max(len(kvr), 1))(*kvr)
+            keep.append(arr)
+        descs[i] = SeqDesc(s.chunk_len, s.num_kv_chunks, s.num_q_chunks, s.q_offset, s.k_offset,
+                           C.cast(arr, C.POINTER(C.c_int32)) if arr is not None else None)
+    cnt = C.c_int32(0)
+    check(lib().magi_slices_build(descs, n, None, 0, C.byref(cnt)))
+    out = (AttnSlice * max(cnt.value, 1))()
+    check(lib().magi_slices_build(descs, n, out, cnt.value, C.byref(cnt)))
+    return np.ctypeslib.as_array(C.cast(out, C.POINTER(C.c_int32)), shape=(max(cnt.value, 1), 5))[:cnt.value].copy()
+
+
+def default_tile_q(hq: int, hkv: int, head_dim: int, dtype: int) -> int:
+    return check(lib().magi_default_tile_q(hq, hkv, head_dim, dtype))
+
+
+def schedule(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim: int, dtype: int,
+             tile_q: int = 0):
+    """magi_schedule: slices -> (work int32 [m, 6], tile_slices int32 [t])."""
+    s = np.ascontiguousarray(np.asarray(slices, np.int32).reshape(-1, 5))
+    sp = s.ctypes.data_as(C.POINTER(AttnSlice)) if len(s) else None
+    nw, nt = C.c_int32(0), C.c_int32(0)
+    L = lib()
+    check(L.magi_schedule(sp, len(s), nq, nk, hq, hkv, head_dim, dtype, tile_q, None, 0, C.byref(nw),
+                          None, 0, C.byref(nt)))
+    work = np.zeros((max(nw.value, 1), 6), np.int32)
+    ts = np.zeros(max(nt.value, 1), np.int32)
+    check(L.magi_schedule(sp, len(s), nq, nk, hq, hkv, head_dim, dtype, tile_q,
+                          work.ctypes.data_as(C.POINTER(WorkItem)), work.shape[0], C.byref(nw),
+                          ts.ctypes.data_as(C.POINTER(C.c_int32)), ts.shape[0], C.byref(nt)))
+    return work[:nw.value], ts[:nt.value]
+
+
+@dataclass
+class Plan:
+    """Device copies of a schedule, ready for ffa_fwd."""
+    nq: int
+    nk: int
+    hq: int
+    hkv: int
+    head_dim: int
+    dtype: int
+    slices: torch.Tensor
+    work: torch.Tensor
+    tile_slices: torch.Tensor
+    host: dict = field(default_factory=dict)
+
+    @property
+    def num_work(self) -> int:
+        return self.work.shape[0]
+
+
+def _to_device(a: np.ndarray, device) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a, np.int32))
+    if t.numel() == 0:
+        return torch.zeros(1, dtype=torch.int32, device=device)
+    return t.pin_memory().to(device, non_blocking=True)
+
+
+def make_plan(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim: int, dtype,
+              device="cuda", tile_q: int = 0) -> Plan:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    slices = np.asarray(slices, np.int32).reshape(-1, 5)
+    work, ts = schedule(slices, nq, nk, hq, hkv, head_dim, code, tile_q)
+    return Plan(nq, nk, hq, hkv, head_dim, code, _to_device(slices, device), _to_device(work, device),
+                _to_device(ts, device), {"slices": slices, "work": work, "tile_slices": ts})
+
+
+def plan_for_videos(seqs: Sequence, nq: int, nk: int, hq: int, hkv: int, head_dim: int, dtype,
+                    device="cuda", tile_q: int = 0) -> Plan:
+    """build_slices + schedule + upload."""
+    return make_plan(build_slices(seqs), nq, nk, hq, hkv, head_dim, dtype, device, tile_q)
+
+
+def _check_3d(name, t, heads, d):
+    if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != d:
+        raise ValueError(f"{name}: expected [n, {heads}, {d}], got {list(t.shape)}")
+    if t.stride(2) != 1 or t.stride(1) != d:
+        raise ValueError(f"{name}: heads and channels must be contiguous (strides {t.stride()})")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def qknorm_rope(q: torch.Tensor, k: Optional[torch.Tensor], gain_q: torch.Tensor,
+                gain_k: Optional[torch.Tensor], pos_q: torch.Tensor, pos_k: Optional[torch.Tensor],
+                rope_base: torch.Tensor, eps: float = 1e-6, q_out: Optional[torch.Tensor] = None,
+                k_out: Optional[torch.Tensor] = None):
+    """magi_qknorm_rope: QK-Norm then 3D RoPE; returns (q_out, k_out)."""
+    d = q.shape[-1]
+    _check_3d("q", q, q.shape[1], d)
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    _check_3d("q_out", q_out, q.shape[1], d)
+    if q_out.stride(0) != q.stride(0):
+        raise ValueError("q and q_out must share the row stride")
+    ghs = 0 if gain_q.dim() == 1 else d
+    nk, hkv, ks = 0, 1, q.shape[1] * d
+    if k is not None:
+        _check_3d("k", k, k.shape[1], d)
+        k_out = torch.empty_like(k) if k_out is None else k_out
+        if k_out.stride(0) != k.stride(0):
+            raise ValueError("k and k_out must share the row stride")
+        nk, hkv, ks = k.shape[0], k.shape[1], k.stride(0)
+    for t in (gain_q, gain_k, rope_base):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("gains and rope_base must be contiguous float32")
+    for t in (pos_q, pos_k):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise ValueError("positions must be contiguous int32 [n, 3]")
+    check(lib().magi_qknorm_rope(
+        _ptr(q), _ptr(q_out), q.shape[0], q.shape[1], q.stride(0),
+        _ptr(k), _ptr(k_out), nk, hkv, ks, d, dtype_code(q.dtype),
+        _ptr(gain_q), _ptr(gain_k), ghs, float(eps), _ptr(pos_q), _ptr(pos_k), _ptr(rope_base),
+        _stream(q)))
+    return q_out, k_out
+
+
+def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
+            softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, return_lse: bool = True):
+    """magi_ffa_fwd over ``plan``; returns (out [nq, hq, d], lse [nq, hq] fp32 or None)."""
+    d = q.shape[-1]
+    hq, hkv = q.shape[1], k.shape[1]
+    _check_3d("q", q, hq, d)
+    _check_3d("k", k, hkv, d)
+    _check_3d("v", v, hkv, d)
+    if k.stride(0) != v.stride(0):
+        raise ValueError("k and v must share the row stride")
+    if (plan.nq, plan.nk, plan.hq, plan.hkv, plan.head_dim, plan.dtype) != \
+            (q.shape[0], k.shape[0], hq, hkv, d, dtype_code(q.dtype)):
+        raise ValueError("plan was made for a different shape or dtype")
+    out = torch.empty_like(q) if out is None else out
+    _check_3d("out", out, hq, d)
+    if lse is None and return_lse:
+        lse = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
+    check(lib().magi_ffa_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q.shape[0], k.shape[0], hq, hkv, d,
+        dtype_code(q.dtype), q.stride(0), k.stride(0), out.stride(0),
+        0.0 if softmax_scale is None else float(softmax_scale),
+        _ptr(plan.slices), int(plan.host["slices"].shape[0]), _ptr(plan.work), plan.num_work,
+        _ptr(plan.tile_slices), int(plan.host["tile_slices"].shape[0]), _stream(q)))
+    return out, lse

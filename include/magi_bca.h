@@ -1,0 +1,204 @@
+/*
+ * magi_bca.h -- block-causal GQA attention forward for AMD MI355X (gfx950).
+ *
+ * C ABI of libmagi_bca.so.  Plain pointers and sizes only.  Every pointer
+ * argument is marked [host] or [device].  Device buffers are always owned by
+ * the caller; the library never allocates device memory, never synchronises a
+ * stream, and launches its kernels on the caller's hipStream_t (passed as
+ * void*; NULL = the default stream).  Every argument is validated on the host
+ * before the first HIP call, so argument errors never touch the GPU.
+ *
+ * Errors: each entry point returns MAGI_OK (0) or a negative magi_status;
+ * magi_last_error() then returns a message for the calling thread.
+ *
+ * The operation is MAGI-1's attention as described on the MAGI-1 pages:
+ *   - block-causal attention: full attention inside a chunk, causal across
+ *     chunks (MAGI-1 study notes, zhao9797.github.io, "自回归去噪 DiT" and
+ *     "整体 pipeline"; 量子位 article on dakule.com, "Block-Causal Attention");
+ *   - GQA with 128 query heads over 8 KV groups and QK-Norm (study notes,
+ *     "模型规格（Table 2）"; 量子位 article, "QK-Norm和GQA");
+ *   - a 3D RoPE over (t, h, w) with a learnable base frequency (study notes,
+ *     "自回归去噪 DiT"; 量子位 article, "Block-Causal Attention");
+ *   - the mask written as a union of AttnSlices (q range, k range, full or
+ *     causal), the Flex-Flash-Attention formulation (study notes, "训练
+ *     Infra"; 量子位 article, "Flex-Flash-Attention"; interview with Zhang
+ *     Zheng on zhengguannews.cn, answer on q_range / k_range);
+ *   - packed videos that must not see each other, and a KV range that limits
+ *     a chunk to its most recent predecessors (interview, same answer; study
+ *     notes, "推理技巧", KV Cache bullet).
+ */
+#ifndef MAGI_BCA_H
+#define MAGI_BCA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MAGI_OK = 0,
+  MAGI_ERR_INVALID_ARG = -1,      /* null pointer, negative size, bad range, bad enum */
+  MAGI_ERR_UNSUPPORTED = -2,      /* valid but not implemented (head_dim, group size, dtype) */
+  MAGI_ERR_BUFFER_TOO_SMALL = -3, /* a host output array is shorter than needed */
+  MAGI_ERR_OVERLAP = -4,          /* two slices list the same (q, k) pair */
+  MAGI_ERR_HIP = -5               /* a HIP call failed (message has the HIP error) */
+} magi_status;
+
+typedef enum {
+  MAGI_MASK_FULL = 0,   /* every (q, k) pair of the rectangle is visible */
+  MAGI_MASK_CAUSAL = 1  /* lower triangle aligned at the bottom-right corner:
+                           row r of [q_start, q_end) sees k in [k_start, k_end)
+                           with k - k_end <= r - q_end */
+} magi_mask_type;
+
+typedef enum { MAGI_DTYPE_BF16 = 0, MAGI_DTYPE_FP32 = 1 } magi_dtype;
+
+/* One AttnSlice: half-open token ranges in the packed Q and K index spaces. */
+typedef struct {
+  int32_t q_start, q_end, k_start, k_end, mask_type;
+} magi_attn_slice;
+
+/* One unit of kernel work: a tile of q_len <= tile_q query tokens and one KV
+ * group.  It owns those output rows for every query head of the group, so no
+ * two items ever write the same output (no atomics).  [slice_begin,
+ * slice_end) indexes the tile-slice list, whose entries index the slice
+ * array.  cost = visible (q, k) pairs of the tile per head (load estimate). */
+typedef struct {
+  int32_t q_start, q_len, slice_begin, slice_end, kv_group, cost;
+} magi_work_item;
+
+/* One packed video of equal-length chunks. */
+typedef struct {
+  int32_t chunk_len;       /* tokens per chunk, >= 1 */
+  int32_t num_kv_chunks;   /* chunks present in K/V (KV cache + in flight), >= 1 */
+  int32_t num_q_chunks;    /* the last num_q_chunks of them carry queries, 1..num_kv_chunks */
+  int32_t q_offset;        /* first row of this video in the packed Q index space */
+  int32_t k_offset;        /* first row of this video in the packed K index space */
+  const int32_t* kv_range; /* [host] [num_q_chunks] or NULL (all unlimited): -1 = unlimited,
+                              r >= 0 = the chunk sees itself and its r preceding chunks */
+} magi_seq_desc;
+
+/* Library version string (static storage). */
+const char* magi_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* magi_last_error(void);
+
+/*
+ * magi_slices_build -- mask description -> AttnSlices.           [host only]
+ *
+ * For every query chunk c of every video emits one FULL slice
+ *   q = [q_offset + j*C, q_offset + (j+1)*C)          (j = c - first query chunk)
+ *   k = [k_offset + lo*C, k_offset + (c+1)*C)         (lo = 0, or max(0, c - r) with KV range r)
+ * except that a video with chunk_len 1, no KV range limit and queries on all
+ * chunks becomes a single CAUSAL slice.  Videos must not overlap each other
+ * in either index space (MAGI_ERR_OVERLAP).
+ *
+ * seqs        [host] num_seqs descriptors (num_seqs >= 0)
+ * slices      [host] output array of slice_cap entries, or NULL with slice_cap 0
+ * num_slices  [host] out: number of slices needed (always written on OK and on
+ *             MAGI_ERR_BUFFER_TOO_SMALL)
+ * With slices == NULL and slice_cap == 0 this is a size query and returns MAGI_OK.
+ */
+int32_t magi_slices_build(const magi_seq_desc* seqs, int32_t num_seqs,
+                          magi_attn_slice* slices, int32_t slice_cap, int32_t* num_slices);
+
+/*
+ * magi_default_tile_q -- query tokens per work item that magi_ffa_fwd's
+ * kernel is built for at this shape (the kernel covers 256 query rows =
+ * tile_q tokens x (hq/hkv) heads).  Returns < 0 on unsupported shapes.
+ */
+int32_t magi_default_tile_q(int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype);
+
+/*
+ * magi_schedule -- AttnSlices -> atomic-free work list.          [host only]
+ *
+ * Validates the slices (ranges inside [0,nq) x [0,nk), known mask type, no
+ * (q, k) pair listed twice), cuts the query axis at every slice boundary,
+ * tiles each piece into tiles of at most tile_q tokens (tile_q = 0 picks
+ * magi_default_tile_q), and emits one work item per (tile, KV group),
+ * including tiles no slice covers (their rows get O = 0, LSE = -inf).
+ * Items are ordered heaviest first by visible-pair area (the area measure of
+ * MagiAttention's dispatch solver: interview, answer on load balancing;
+ * 量子位 article, "计算负载均衡"), with the KV groups interleaved so that
+ * consecutive workgroups, which the GPU deals round-robin to its 8 XCDs,
+ * keep one KV group per XCD.
+ *
+ * slices       [host] num_slices slices (num_slices >= 0)
+ * work         [host] output, work_cap entries (or NULL with work_cap 0)
+ * tile_slices  [host] output, ts_cap int32 slice indices (or NULL with ts_cap 0)
+ * num_work, num_tile_slices [host] out: counts needed
+ * With both output arrays NULL and both caps 0 this is a size query.
+ * The work list is a deterministic function of the arguments.
+ */
+int32_t magi_schedule(const magi_attn_slice* slices, int32_t num_slices,
+                      int64_t nq, int64_t nk, int32_t hq, int32_t hkv,
+                      int32_t head_dim, int32_t dtype, int32_t tile_q,
+                      magi_work_item* work, int32_t work_cap, int32_t* num_work,
+                      int32_t* tile_slices, int32_t ts_cap, int32_t* num_tile_slices);
+
+/*
+ * magi_qknorm_rope -- QK-Norm then 3D RoPE on Q and (optionally) K.  [device]
+ *
+ * For every token i and head h of X in {Q, K}:
+ *   y = x / sqrt(mean_d(x^2) + eps) * gain           (RMS over head_dim)
+ *   then for axis a in (t, h, w), channel pair (2j, 2j+1) of section a
+ *   (head_dim/3 channels per section), angle = pos[i][a] * base_a^(-2j/(head_dim/3)):
+ *   (y0, y1) -> (y0 cos - y1 sin, y0 sin + y1 cos).
+ * Arithmetic is fp32; the result is stored in the input dtype
+ * (round-to-nearest-even for bf16).  Output may alias input.
+ *
+ * q_in, q_out   [device] [nq rows] x [hq heads] x [head_dim], row stride q_tok_stride
+ *               elements (>= hq*head_dim), heads contiguous; 16-byte aligned
+ * k_in, k_out   [device] same for K with hkv heads (both NULL and nk = 0 to skip K)
+ * head_dim      24 or 48 (must be divisible by 6)
+ * gain_q/gain_k [device] fp32 [head_dim] (gain_head_stride 0) or [heads][head_dim]
+ *               (gain_head_stride = head_dim)
+ * pos_q, pos_k  [device] int32 [n][3] latent (t, h, w) coordinates
+ * rope_base     [device] fp32 [3] base frequency of the t, h, w axes
+ */
+int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, int32_t hq, int64_t q_tok_stride,
+                         const void* k_in, void* k_out, int64_t nk, int32_t hkv, int64_t k_tok_stride,
+                         int32_t head_dim, int32_t dtype,
+                         const float* gain_q, const float* gain_k, int32_t gain_head_stride,
+                         float eps, const int32_t* pos_q, const int32_t* pos_k,
+                         const float* rope_base, void* stream);
+
+/*
+ * magi_ffa_fwd -- Flex-Flash-Attention forward over a work list.   [device]
+ *
+ * For every query row i and head h (KV group g = h / (hq/hkv)):
+ *   O[i,h]   = sum_k softmax_k(scale * q[i,h].k[k,g]) v[k,g]   over the visible k
+ *   LSE[i,h] = log sum_k exp(scale * q[i,h].k[k,g])             (natural log)
+ * where the visible k are the union of the slices listed by the work item
+ * that owns row i.  Rows with no visible key get O = 0 and LSE = -inf.
+ * bf16: bf16 MFMA products with fp32 accumulation and fp32 online softmax;
+ * P is rounded to bf16 for the PV product; O is stored as bf16.
+ * fp32: fp32 arithmetic throughout.  The result is bitwise deterministic.
+ *
+ * q            [device] [nq][hq][head_dim], row stride q_tok_stride elements
+ * k, v         [device] [nk][hkv][head_dim], row stride kv_tok_stride elements
+ * out          [device] [nq][hq][head_dim], row stride o_tok_stride elements
+ * lse          [device] fp32 [nq][hq] (row stride hq), or NULL
+ *              All tensor pointers 16-byte aligned, strides multiples of 8.
+ * softmax_scale  <= 0 selects 1/sqrt(head_dim)
+ * slices, work, tile_slices  [device] copies of magi_schedule's outputs made for
+ *              the same nq, nk, hq, hkv, head_dim, dtype (items are clamped to
+ *              the tensor bounds on the device, so a mismatched list cannot
+ *              read or write out of bounds)
+ * Supported: head_dim 24 or 48; hq % hkv == 0; hq/hkv <= 256.
+ */
+int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int64_t nq, int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
+                     int64_t q_tok_stride, int64_t kv_tok_stride, int64_t o_tok_stride,
+                     float softmax_scale,
+                     const magi_attn_slice* slices, int32_t num_slices,
+                     const magi_work_item* work, int32_t num_work,
+                     const int32_t* tile_slices, int32_t num_tile_slices,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MAGI_BCA_H */

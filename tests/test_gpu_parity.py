@@ -1,0 +1,284 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances (bf16 storage): max-abs <= 2e-2 and relative L2 <= 5e-3 on O;
+fp32: max-abs <= 1e-5.  LSE is checked with max-abs 1e-2 (bf16) / 1e-5
+(fp32).  Full-size workloads run the kernel at full size, in the launch
+configuration the benchmark times, and compare a seeded sample of rows (all
+heads) that the oracle computes one by one; small cases compare every row.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from block_causal_attention_amd import _lib, ops
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {"bf16": dict(max_abs=2e-2, rel_l2=5e-3, lse=1e-2), "fp32": dict(max_abs=1e-5, rel_l2=1e-5, lse=1e-5)}
+
+
+def note(msg):
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def compare(got, want, kind, what="O"):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    tol = TOL[kind]
+    if what == "LSE":
+        fin = np.isfinite(want)
+        assert np.array_equal(fin, np.isfinite(got)), "LSE -inf pattern differs"
+        if fin.any():
+            err = np.abs(got[fin] - want[fin]).max()
+            assert err <= tol["lse"], f"LSE max-abs {err:.3e}"
+        return
+    diff = got - want
+    max_abs = float(np.abs(diff).max()) if diff.size else 0.0
+    den = float(np.linalg.norm(want))
+    rel = float(np.linalg.norm(diff)) / den if den > 0 else float(np.linalg.norm(diff))
+    note(f"{what}: max-abs {max_abs:.3e} rel-L2 {rel:.3e}")
+    assert max_abs <= tol["max_abs"], f"{what} max-abs {max_abs:.3e} > {tol['max_abs']}"
+    assert rel <= tol["rel_l2"], f"{what} rel-L2 {rel:.3e} > {tol['rel_l2']}"
+
+
+def dev_inputs(wl, inp):
+    g = lambda t: t.to(DEV)
+    return dict(q=g(inp.q), k=g(inp.k), v=g(inp.v), gq=g(inp.gain_q), gk=g(inp.gain_k), pq=g(inp.pos_q),
+                pk=g(inp.pos_k), base=torch.tensor(wl.rope_base, dtype=torch.float32, device=DEV))
+
+
+def gpu_forward(wl, d, fresh_only=False):
+    """prologue (Q and K) then FFA over the builder's slices, as the benchmark runs it."""
+    k_src = d["k"]
+    qh, kh = ops.qknorm_rope(d["q"], k_src, d["gq"], d["gk"], d["pq"], d["pk"], d["base"], wl.eps)
+    plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, d["q"].dtype)
+    O, L = ops.ffa_fwd(qh, kh, d["v"], plan)
+    torch.cuda.synchronize()
+    return qh, kh, O, L
+
+
+def np64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+# --------------------------------------------------------------------------- prologue
+
+@pytest.mark.parametrize("name", ["tiny", "magi4.5b", "magi24b"])
+def test_prologue_matches_oracle(name):
+    note(f"prologue {name}")
+    wl = W.make_workload(name)
+    inp = W.make_inputs(wl, 0)
+    d = dev_inputs(wl, inp)
+    qh, kh = ops.qknorm_rope(d["q"], d["k"], d["gq"], d["gk"], d["pq"], d["pk"], d["base"], wl.eps)
+    torch.cuda.synchronize()
+    inv = oracle.rope_inv_freq(wl.rope_base, wl.head_dim)
+    rows = np.arange(wl.nq) if wl.nq <= 6000 else W.sample_rows(wl, 2000)
+    want_q = oracle.rope_3d(oracle.qk_norm(np64(inp.q[rows]), np64(inp.gain_q), wl.eps), inp.pos_q[rows].numpy(), inv)
+    want_k = oracle.rope_3d(oracle.qk_norm(np64(inp.k), np64(inp.gain_k), wl.eps), inp.pos_k.numpy(), inv)
+    compare(np64(qh)[rows], want_q, wl.dtype, "q_hat")
+    compare(np64(kh), want_k, wl.dtype, "k_hat")
+
+
+def test_prologue_per_head_gain_in_place_and_strided():
+    note("prologue per-head gains, in place, strided view")
+    wl = W.custom_block_causal(2, 2, 3, 4, 16, 2, 48)
+    inp = W.make_inputs(wl, 7)
+    rng = np.random.Generator(np.random.PCG64(7))
+    gq = rng.uniform(0.5, 1.5, (16, 48)).astype(np.float32)
+    base = torch.tensor([1e4, 3e3, 5e2], dtype=torch.float32, device=DEV)
+    # Q lives inside a wider row (a fused projection layout): row stride 20 heads
+    buf = torch.zeros(wl.nq, 20, 48, dtype=torch.bfloat16, device=DEV)
+    buf[:, 2:18] = inp.q.to(DEV)
+    qv = buf[:, 2:18]
+    ops.qknorm_rope(qv, None, torch.from_numpy(gq).to(DEV), None, inp.pos_q.to(DEV), None, base, 1e-6, q_out=qv)
+    torch.cuda.synchronize()
+    want = oracle.rope_3d(oracle.qk_norm(np64(inp.q), gq, 1e-6), inp.pos_q.numpy(),
+                          oracle.rope_inv_freq((1e4, 3e3, 5e2), 48))
+    compare(np64(qv), want, "bf16", "q_hat")
+    assert torch.count_nonzero(buf[:, :2]) == 0 and torch.count_nonzero(buf[:, 18:]) == 0
+
+
+# --------------------------------------------------------------------------- attention alone
+
+def ffa_case(q, k, v, slices, kind, scale=None, check_lse=True):
+    nq, hq, dd = q.shape
+    nk, hkv = k.shape[0], k.shape[1]
+    tdt = torch.bfloat16 if kind == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(x).to(tdt).to(DEV) for x in (q, k, v))
+    plan = ops.make_plan(np.asarray(slices, np.int32).reshape(-1, 5), nq, nk, hq, hkv, dd, tdt)
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full((nq, hq), float("nan"), dtype=torch.float32, device=DEV)
+    O, L = ops.ffa_fwd(qd, kd, vd, plan, softmax_scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    mask = oracle.slices_mask([tuple(int(x) for x in s) for s in slices], nq, nk) if len(slices) else \
+        np.zeros((nq, nk), bool)
+    qr, kr, vr = (np64(t) for t in (qd, kd, vd))
+    Ow, Lw = oracle.attention(qr, kr, vr, mask, scale if scale else dd ** -0.5)
+    assert not torch.isnan(O).any(), "output rows left unwritten"
+    compare(np64(O), Ow, kind)
+    if check_lse:
+        compare(np64(L), Lw, kind, "LSE")
+    return O, L
+
+
+def rand(shape, seed, scale=1.0):
+    return np.random.Generator(np.random.PCG64(seed)).standard_normal(shape).astype(np.float32) * scale
+
+
+@pytest.mark.parametrize("d", [24, 48])
+@pytest.mark.parametrize("G", [16, 4, 1, 3])
+def test_ffa_block_causal_ragged(d, G):
+    # 3 chunks of 37 tokens: no tile or 64-key boundary lines up
+    note(f"ffa block-causal ragged d={d} G={G}")
+    hkv = 2
+    seqs = [W.SeqDesc(37, 3, 3, 0, 0, (-1, -1, -1), 1, 1, 37)]
+    sl = ops.build_slices(seqs)
+    q, k, v = rand((111, G * hkv, d), 1), rand((111, hkv, d), 2), rand((111, hkv, d), 3)
+    ffa_case(q, k, v, sl, "bf16")
+
+
+@pytest.mark.parametrize("d", [24, 48])
+def test_ffa_causal_and_irregular_slices(d):
+    note(f"ffa irregular slices d={d}")
+    nq, nk = 150, 210
+    slices = [
+        (0, 70, 0, 70, _lib.MASK_CAUSAL),          # square causal
+        (70, 100, 0, 40, _lib.MASK_FULL),          # two k ranges for one q band
+        (70, 100, 60, 130, _lib.MASK_CAUSAL),      # wide causal, bottom-right aligned
+        (100, 140, 130, 150, _lib.MASK_CAUSAL),    # tall causal: early rows see nothing
+        # rows 140..149 are covered by no slice: O = 0, LSE = -inf
+    ]
+    q, k, v = rand((nq, 16, d), 4), rand((nk, 1, d), 5), rand((nk, 1, d), 6)
+    O, L = ffa_case(q, k, v, np.array(slices), "bf16")
+    assert torch.all(O[140:] == 0) and torch.all(torch.isneginf(L[140:]))
+
+
+def test_ffa_fp32_tiny_full():
+    note("ffa fp32 tiny")
+    wl = W.make_workload("tiny")
+    inp = W.make_inputs(wl, 0)
+    ffa_case(inp.q.numpy(), inp.k.numpy(), inp.v.numpy(), ops.build_slices(wl.seqs), "fp32")
+
+
+def test_ffa_fp32_irregular():
+    note("ffa fp32 irregular")
+    slices = np.array([(0, 40, 0, 40, 1), (40, 70, 10, 30, 0), (40, 70, 35, 80, 1)])
+    ffa_case(rand((80, 8, 48), 8), rand((80, 2, 48), 9), rand((80, 2, 48), 10), slices, "fp32", scale=0.3)
+
+
+def test_ffa_no_keys_and_scale():
+    note("ffa nk=0 and explicit scale")
+    q = torch.randn(20, 16, 24, device=DEV).to(torch.bfloat16)
+    k = torch.zeros(0, 1, 24, device=DEV, dtype=torch.bfloat16)
+    plan = ops.make_plan(np.zeros((0, 5), np.int32), 20, 0, 16, 1, 24, torch.bfloat16)
+    O, L = ops.ffa_fwd(q, k, k, plan)
+    torch.cuda.synchronize()
+    assert torch.all(O == 0) and torch.all(torch.isneginf(L))
+    sl = np.array([(0, 30, 0, 50, 0)])
+    ffa_case(rand((30, 16, 24), 11, 3.0), rand((50, 1, 24), 12, 3.0), rand((50, 1, 24), 13), sl, "bf16", scale=0.05)
+
+
+# --------------------------------------------------------------------------- full workloads
+
+def sampled_forward_parity(name, nrows, seed=0):
+    wl = W.make_workload(name, seed)
+    note(f"end-to-end {name} seed={seed}: drawing inputs")
+    inp = W.make_inputs(wl, seed)
+    d = dev_inputs(wl, inp)
+    note(f"end-to-end {name}: GPU run")
+    qh, kh, O, L = gpu_forward(wl, d)
+    rows = W.sample_rows(wl, nrows, seed)
+    note(f"end-to-end {name}: oracle on {len(rows)} rows")
+    mask = oracle.video_mask(wl.seqs, wl.nq, wl.nk, rows)
+    Ow, Lw = oracle.forward(np64(inp.q[rows]), np64(inp.k), np64(inp.v), np64(inp.gain_q), np64(inp.gain_k),
+                            inp.pos_q[rows].numpy(), inp.pos_k.numpy(), wl.rope_base, wl.eps, mask,
+                            wl.softmax_scale)
+    compare(np64(O[rows]), Ow, wl.dtype)
+    compare(np64(L[rows]), Lw, wl.dtype, "LSE")
+    assert not torch.isnan(O).any()
+
+
+def test_end_to_end_tiny_all_rows():
+    wl = W.make_workload("tiny")
+    inp = W.make_inputs(wl, 0)
+    d = dev_inputs(wl, inp)
+    qh, kh, O, L = gpu_forward(wl, d)
+    mask = oracle.video_mask(wl.seqs, wl.nq, wl.nk)
+    Ow, Lw = oracle.forward(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.gain_q), np64(inp.gain_k),
+                            inp.pos_q.numpy(), inp.pos_k.numpy(), wl.rope_base, wl.eps, mask, wl.softmax_scale)
+    compare(np64(O), Ow, "fp32")
+    compare(np64(L), Lw, "fp32", "LSE")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_end_to_end_magi45b(seed):
+    sampled_forward_parity("magi4.5b", 384, seed)
+
+
+def test_end_to_end_magi24b():
+    sampled_forward_parity("magi24b", 160)
+
+
+def test_end_to_end_stream():
+    sampled_forward_parity("stream", 48)
+
+
+def test_end_to_end_varlen():
+    sampled_forward_parity("varlen", 64)
+
+
+# --------------------------------------------------------------------------- invariants
+
+def test_bitwise_determinism_and_causality():
+    note("bitwise determinism and causality on magi4.5b")
+    wl = W.make_workload("magi4.5b")
+    inp = W.make_inputs(wl, 3)
+    d = dev_inputs(wl, inp)
+    plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, torch.bfloat16)
+    O1, L1 = ops.ffa_fwd(d["q"], d["k"], d["v"], plan)
+    O2, L2 = ops.ffa_fwd(d["q"], d["k"], d["v"], plan)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+    # perturb the last two chunks' K and V: the first two chunks' rows are bitwise unchanged
+    k2, v2 = d["k"].clone(), d["v"].clone()
+    k2[2 * 1440:] = torch.randn_like(k2[2 * 1440:])
+    v2[2 * 1440:] = 7.0
+    O3, L3 = ops.ffa_fwd(d["q"], k2, v2, plan)
+    torch.cuda.synchronize()
+    assert torch.equal(O3[:2 * 1440], O1[:2 * 1440]) and torch.equal(L3[:2 * 1440], L1[:2 * 1440])
+    assert not torch.equal(O3[2 * 1440:], O1[2 * 1440:])
+
+
+def test_streaming_rows_equal_full_run():
+    note("streaming == rows of the full run")
+    full = W.custom_block_causal(6, 2, 10, 12, 16, 1, 48)
+    strm = W.custom_block_causal(6, 2, 10, 12, 16, 1, 48, num_q_chunks=2)
+    inp = W.make_inputs(full, 5)
+    q, k, v = (t.to(DEV) for t in (inp.q, inp.k, inp.v))
+    pf = ops.plan_for_videos(full.seqs, full.nq, full.nk, 16, 1, 48, torch.bfloat16)
+    ps = ops.plan_for_videos(strm.seqs, strm.nq, strm.nk, 16, 1, 48, torch.bfloat16)
+    Of, Lf = ops.ffa_fwd(q, k, v, pf)
+    Os, Ls = ops.ffa_fwd(q[4 * 240:].contiguous(), k, v, ps)
+    torch.cuda.synchronize()
+    assert torch.equal(Os, Of[4 * 240:]) and torch.equal(Ls, Lf[4 * 240:])
+
+
+def test_packing_equals_separate_videos_gpu():
+    note("packing == separate videos")
+    pk = W.custom_packed([(3, 1, 8, 10, None), (2, 1, 8, 10, [-1, 1]), (4, 1, 8, 10, [-1, -1, 1, 1])], 16, 2, 24)
+    inp = W.make_inputs(pk, 9)
+    q, k, v = (t.to(DEV) for t in (inp.q, inp.k, inp.v))
+    O, L = ops.ffa_fwd(q, k, v, ops.plan_for_videos(pk.seqs, pk.nq, pk.nk, 16, 2, 24, torch.bfloat16))
+    torch.cuda.synchronize()
+    for s in pk.seqs:
+        a, b = s.q_offset, s.q_offset + s.nq
+        one = W.SeqDesc(s.chunk_len, s.num_kv_chunks, s.num_q_chunks, 0, 0, s.kv_range, 1, 8, 10)
+        Os, Ls = ops.ffa_fwd(q[a:b].contiguous(), k[a:b].contiguous(), v[a:b].contiguous(),
+                             ops.plan_for_videos([one], s.nq, s.nk, 16, 2, 24, torch.bfloat16))
+        torch.cuda.synchronize()
+        assert torch.equal(Os, O[a:b]) and torch.equal(Ls, L[a:b])

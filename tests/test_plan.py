@@ -1,0 +1,292 @@
+"""Host-side checks of libmagi_bca: exported symbols, the mask -> AttnSlice
+builder and the atomic-free scheduler (no GPU needed), and the C ABI's
+argument validation, which runs before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from block_causal_attention_amd import _lib, ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "magi_bca.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|int32_t)\s+(magi_\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_header_symbol():
+    L = _lib.lib()
+    names = header_functions()
+    assert len(names) == 7, names
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert b"gfx950" in L.magi_version()
+
+
+# --------------------------------------------------------------------------- builder
+
+def expand(slices, nq, nk):
+    return oracle.slices_mask([tuple(int(x) for x in s) for s in slices], nq, nk)
+
+
+@pytest.mark.parametrize("name", ["tiny", "magi4.5b", "magi24b", "varlen"])
+def test_builder_round_trip_matches_oracle_mask(name):
+    wl = W.make_workload(name)
+    sl = ops.build_slices(wl.seqs)
+    nchunks = sum(s.num_q_chunks for s in wl.seqs)
+    assert len(sl) == nchunks
+    # compare on a row sample for the big ones (mask rows are exact booleans)
+    rows = np.arange(wl.nq) if wl.nq <= 6000 else W.sample_rows(wl, 300)
+    want = oracle.video_mask(wl.seqs, wl.nq, wl.nk, rows)
+    got = oracle.slices_mask([tuple(int(x) for x in s) for s in sl], wl.nq, wl.nk, rows)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_builder_streaming_slices():
+    wl = W.make_workload("stream")
+    sl = ops.build_slices(wl.seqs)
+    C_ = 3600
+    np.testing.assert_array_equal(sl, [[j * C_, (j + 1) * C_, 0, (21 + j) * C_, 0] for j in range(4)])
+
+
+@pytest.mark.parametrize("trial", range(20))
+def test_builder_fuzz(trial):
+    rng = np.random.Generator(np.random.PCG64(100 + trial))
+    spec, qo, ko = [], 0, 0
+    for _ in range(int(rng.integers(1, 5))):
+        Cl = int(rng.integers(1, 6))
+        nkv = int(rng.integers(1, 7))
+        nqc = int(rng.integers(1, nkv + 1))
+        kvr = [int(x) for x in rng.integers(-1, 4, nqc)] if rng.random() < 0.6 else [-1] * nqc
+        qo += int(rng.integers(0, 3))  # gaps are allowed (rows/keys of no video)
+        ko += int(rng.integers(0, 3))
+        spec.append(W.SeqDesc(Cl, nkv, nqc, qo, ko, tuple(kvr), 1, 1, Cl))
+        qo += nqc * Cl
+        ko += nkv * Cl
+    sl = ops.build_slices(spec)
+    np.testing.assert_array_equal(expand(sl, qo, ko), oracle.video_mask(spec, qo, ko))
+
+
+def test_builder_unit_chunks_become_one_causal_slice():
+    s = W.SeqDesc(1, 10, 10, 0, 0, tuple([-1] * 10), 1, 1, 1)
+    sl = ops.build_slices([s])
+    np.testing.assert_array_equal(sl, [[0, 10, 0, 10, _lib.MASK_CAUSAL]])
+    st = W.SeqDesc(1, 10, 4, 0, 0, tuple([-1] * 4), 1, 1, 1)
+    sl = ops.build_slices([st])
+    np.testing.assert_array_equal(sl, [[0, 4, 0, 10, _lib.MASK_CAUSAL]])
+    np.testing.assert_array_equal(expand(sl, 4, 10), oracle.video_mask([st], 4, 10))
+
+
+def test_builder_rejects_bad_descriptors():
+    good = W.SeqDesc(4, 3, 3, 0, 0, (-1, -1, -1), 1, 2, 2)
+    for bad, code in [
+        (W.SeqDesc(0, 3, 3, 0, 0, None, 1, 1, 1), _lib.MAGI_ERR_INVALID_ARG),
+        (W.SeqDesc(4, 3, 4, 0, 0, None, 1, 1, 1), _lib.MAGI_ERR_INVALID_ARG),
+        (W.SeqDesc(4, 0, 0, 0, 0, None, 1, 1, 1), _lib.MAGI_ERR_INVALID_ARG),
+        (W.SeqDesc(4, 3, 3, -1, 0, None, 1, 1, 1), _lib.MAGI_ERR_INVALID_ARG),
+        (W.SeqDesc(4, 3, 3, 0, 0, (-1, -2, -1), 1, 1, 1), _lib.MAGI_ERR_INVALID_ARG),
+        (W.SeqDesc(2 ** 30, 3, 3, 0, 0, None, 1, 1, 1), _lib.MAGI_ERR_INVALID_ARG),
+    ]:
+        with pytest.raises(_lib.MagiError) as e:
+            ops.build_slices([bad])
+        assert e.value.status == code
+    # two videos sharing query rows
+    with pytest.raises(_lib.MagiError) as e:
+        ops.build_slices([good, W.SeqDesc(4, 3, 3, 8, 12, None, 1, 2, 2)])
+    assert e.value.status == _lib.MAGI_ERR_OVERLAP
+    # NULL count pointer / NULL seqs
+    L = _lib.lib()
+    assert L.magi_slices_build(None, 1, None, 0, None) == _lib.MAGI_ERR_INVALID_ARG
+    n = C.c_int32()
+    assert L.magi_slices_build(None, 1, None, 0, C.byref(n)) == _lib.MAGI_ERR_INVALID_ARG
+    assert L.magi_slices_build(None, 0, None, 0, C.byref(n)) == 0 and n.value == 0
+    # two-call protocol: too small a buffer reports the size
+    descs = (_lib.SeqDesc * 1)(_lib.SeqDesc(4, 3, 3, 0, 0, None))
+    buf = (_lib.AttnSlice * 2)()
+    assert L.magi_slices_build(descs, 1, buf, 2, C.byref(n)) == _lib.MAGI_ERR_BUFFER_TOO_SMALL
+    assert n.value == 3
+    assert b"slice_cap" in L.magi_last_error()
+
+
+# --------------------------------------------------------------------------- scheduler
+
+def check_schedule(slices, nq, nk, hq, hkv, d, dtype=_lib.DTYPE_BF16, tile_q=0):
+    work, ts = ops.schedule(slices, nq, nk, hq, hkv, d, dtype, tile_q)
+    tq = tile_q or ops.default_tile_q(hq, hkv, d, dtype)
+    owner = np.full((nq, hkv), -1)
+    sl = [tuple(int(x) for x in s) for s in slices]
+    full = oracle.slices_mask(sl, nq, nk) if nq * nk <= 4e7 else None
+    for i, (q0, ql, sb, se, g, cost) in enumerate(work):
+        assert 1 <= ql <= tq and 0 <= g < hkv and 0 <= sb <= se <= len(ts)
+        assert (owner[q0:q0 + ql, g] == -1).all(), "row owned twice"
+        owner[q0:q0 + ql, g] = i
+        mine = [sl[j] for j in ts[sb:se]]
+        for (qs, qe, *_r) in mine:
+            assert qs <= q0 and q0 + ql <= qe, "tile straddles a slice boundary"
+        if full is not None:
+            sub = oracle.slices_mask(mine, nq, nk, np.arange(q0, q0 + ql)) if mine else np.zeros((ql, nk), bool)
+            np.testing.assert_array_equal(sub, full[q0:q0 + ql])
+            assert cost == min(int(sub.sum()), 2 ** 31 - 1)
+    assert (owner >= 0).all(), "a (row, group) has no owner"
+    costs = work[::hkv, 5]
+    assert (np.diff(costs) <= 0).all(), "not heaviest-first"
+    for r in range(len(work) // hkv):
+        np.testing.assert_array_equal(work[r * hkv:(r + 1) * hkv, 4], np.arange(hkv))
+    w2, ts2 = ops.schedule(slices, nq, nk, hq, hkv, d, dtype, tile_q)
+    np.testing.assert_array_equal(w2, work)
+    np.testing.assert_array_equal(ts2, ts)
+    return work, ts
+
+
+@pytest.mark.parametrize("name", ["tiny", "magi4.5b", "varlen"])
+def test_schedule_workloads(name):
+    wl = W.make_workload(name)
+    sl = ops.build_slices(wl.seqs)
+    work, ts = check_schedule(sl, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim,
+                              _lib.DTYPE_FP32 if wl.dtype == "fp32" else _lib.DTYPE_BF16)
+    area = int(oracle.video_mask(wl.seqs, wl.nq, wl.nk).sum()) if wl.nq < 10000 else None
+    if area is not None:
+        assert work[:, 5].astype(np.int64).sum() == area * wl.hkv
+
+
+def test_schedule_area_24b_closed_form():
+    wl = W.make_workload("magi24b")
+    work, _ = ops.schedule(ops.build_slices(wl.seqs), wl.nq, wl.nk, 128, 8, 48, _lib.DTYPE_BF16)
+    assert work[:, 5].astype(np.int64).sum() == 3600 * 3600 * 36 * 8
+    assert len(work) == (28800 // 16) * 8
+
+
+@pytest.mark.parametrize("trial", range(25))
+def test_schedule_fuzz_raw_slices(trial):
+    rng = np.random.Generator(np.random.PCG64(500 + trial))
+    nq, nk = int(rng.integers(1, 120)), int(rng.integers(1, 120))
+    hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 3, 4, 16]))
+    # non-overlapping random slices: carve the k axis per q band
+    slices = []
+    q = 0
+    while q < nq:
+        qe = min(nq, q + int(rng.integers(1, 30)))
+        if rng.random() < 0.8:
+            k = int(rng.integers(0, 5))
+            while k < nk:
+                ke = min(nk, k + int(rng.integers(1, 40)))
+                slices.append((q, qe, k, ke, int(rng.random() < 0.4)))
+                k = ke + int(rng.integers(0, 10))
+        q = qe + int(rng.integers(0, 4))
+    arr = np.array(slices, np.int32).reshape(-1, 5)
+    tq = int(rng.choice([0, 1, 5]))
+    check_schedule(arr, nq, nk, G * hkv, hkv, 24, _lib.DTYPE_BF16, tile_q=min(tq, 256 // G))
+
+
+def test_schedule_causal_overlap_detection():
+    # two causal slices that only meet on the last rows of their band
+    a = (0, 8, 0, 8, _lib.MASK_CAUSAL)
+    b = (0, 8, 6, 12, _lib.MASK_FULL)
+    with pytest.raises(_lib.MagiError) as e:
+        ops.schedule(np.array([a, b]), 8, 12, 16, 1, 24, 0)
+    assert e.value.status == _lib.MAGI_ERR_OVERLAP
+    # touching but disjoint: causal row r sees k <= r, full starts at 8
+    ok = ops.schedule(np.array([a, (0, 8, 8, 12, 0)]), 8, 12, 16, 1, 24, 0)
+    assert len(ok[0]) == 1
+    # a tall causal slice whose early rows see nothing is not an overlap
+    ops.schedule(np.array([(0, 8, 0, 2, 1), (0, 8, 2, 4, 0)]), 8, 4, 16, 1, 24, 0)
+
+
+def test_schedule_rejects_bad_arguments():
+    L = _lib.lib()
+    nw, nt = C.c_int32(), C.c_int32()
+    good = np.array([[0, 4, 0, 4, 0]], np.int32)
+
+    def call(sl, nq=4, nk=4, hq=16, hkv=1, d=24, dt=0, tq=0):
+        s = np.ascontiguousarray(np.asarray(sl, np.int32).reshape(-1, 5))
+        return L.magi_schedule(s.ctypes.data_as(C.POINTER(_lib.AttnSlice)), len(s), nq, nk, hq, hkv, d, dt, tq,
+                               None, 0, C.byref(nw), None, 0, C.byref(nt))
+    assert call(good) == 0 and nw.value == 1 and nt.value == 1
+    assert call([[0, 5, 0, 4, 0]]) == _lib.MAGI_ERR_INVALID_ARG      # q beyond nq
+    assert call([[2, 1, 0, 4, 0]]) == _lib.MAGI_ERR_INVALID_ARG      # q_start > q_end
+    assert call([[0, 4, -1, 4, 0]]) == _lib.MAGI_ERR_INVALID_ARG     # negative k
+    assert call([[0, 4, 0, 4, 7]]) == _lib.MAGI_ERR_INVALID_ARG      # bad mask type
+    assert call(good, hq=12, hkv=8) == _lib.MAGI_ERR_INVALID_ARG     # hq % hkv
+    assert call(good, d=64) == _lib.MAGI_ERR_UNSUPPORTED             # head_dim
+    assert call(good, hq=512, hkv=1) == _lib.MAGI_ERR_UNSUPPORTED    # group > 256
+    assert call(good, dt=5) == _lib.MAGI_ERR_INVALID_ARG             # dtype
+    assert call(good, tq=17) == _lib.MAGI_ERR_INVALID_ARG            # tile_q above kernel capacity
+    assert call(good, nq=-1) == _lib.MAGI_ERR_INVALID_ARG
+    assert call([[0, 4, 0, 3, 0], [0, 4, 2, 4, 0]]) == _lib.MAGI_ERR_OVERLAP
+    assert L.magi_schedule(None, 1, 4, 4, 16, 1, 24, 0, 0, None, 0, C.byref(nw), None, 0, C.byref(nt)) \
+        == _lib.MAGI_ERR_INVALID_ARG
+    w = (_lib.WorkItem * 1)()
+    t = (C.c_int32 * 1)()
+    s = np.ascontiguousarray(np.array([[0, 4, 0, 4, 0]] * 1, np.int32))
+    assert L.magi_schedule(s.ctypes.data_as(C.POINTER(_lib.AttnSlice)), 1, 40, 4, 16, 8, 24, 0, 0, w, 1,
+                           C.byref(nw), t, 1, C.byref(nt)) == _lib.MAGI_ERR_BUFFER_TOO_SMALL
+    assert nw.value > 1
+
+
+def test_schedule_uncovered_rows_get_owners():
+    work, ts = ops.schedule(np.array([[3, 5, 0, 2, 0]]), 9, 2, 4, 2, 24, 0)
+    cover = sorted((int(w[0]), int(w[1])) for w in work[::2])
+    assert cover == [(0, 3), (3, 2), (5, 4)]
+    assert all(w[2] == w[3] for w in work if w[0] != 3)
+
+
+def test_default_tile_q():
+    assert ops.default_tile_q(128, 8, 24, 0) == 16
+    assert ops.default_tile_q(8, 2, 24, 1) == 64
+    assert ops.default_tile_q(48, 16, 48, 0) == 85
+
+
+# --------------------------------------------------------------------------- device entry validation
+
+def test_device_entry_points_validate_before_any_hip_call():
+    L = _lib.lib()
+    p = C.c_void_p(4096)  # never dereferenced: every call below fails validation
+    f = C.c_void_p(4096)
+    # magi_qknorm_rope
+    assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 32, 0, f, None, 0, 1e-6, p, None, f,
+                              None) == _lib.MAGI_ERR_UNSUPPORTED
+    assert L.magi_qknorm_rope(p, p, 10, 8, 100, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, f,
+                              None) == _lib.MAGI_ERR_INVALID_ARG   # stride < heads*d
+    assert L.magi_qknorm_rope(C.c_void_p(4098), p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6,
+                              p, None, f, None) == _lib.MAGI_ERR_INVALID_ARG   # misaligned
+    assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, -1.0, p, None, f,
+                              None) == _lib.MAGI_ERR_INVALID_ARG   # eps < 0
+    assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 7, 1e-6, p, None, f,
+                              None) == _lib.MAGI_ERR_INVALID_ARG   # gain stride
+    assert L.magi_qknorm_rope(p, p, 10, 8, 192, p, p, 5, 2, 48, 24, 0, f, None, 0, 1e-6, p, p, f,
+                              None) == _lib.MAGI_ERR_INVALID_ARG   # gain_k NULL
+    assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, None,
+                              None) == _lib.MAGI_ERR_INVALID_ARG   # rope_base NULL
+    assert L.magi_qknorm_rope(None, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, f,
+                              None) == _lib.MAGI_ERR_INVALID_ARG   # q NULL
+    # magi_ffa_fwd
+    def ffa(**kw):
+        a = dict(q=p, k=p, v=p, out=p, lse=None, nq=16, nk=16, hq=16, hkv=1, d=24, dt=0, qs=384, kvs=24, os_=384,
+                 scale=0.0, sl=p, ns=1, w=p, nw=1, ts=p, nts=1)
+        a.update(kw)
+        return L.magi_ffa_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["nq"], a["nk"], a["hq"], a["hkv"],
+                              a["d"], a["dt"], a["qs"], a["kvs"], a["os_"], a["scale"], a["sl"], a["ns"], a["w"],
+                              a["nw"], a["ts"], a["nts"], None)
+    assert ffa(d=64) == _lib.MAGI_ERR_UNSUPPORTED
+    assert ffa(dt=3) == _lib.MAGI_ERR_INVALID_ARG
+    assert ffa(hq=12, hkv=8) == _lib.MAGI_ERR_INVALID_ARG
+    assert ffa(hq=512, hkv=1, qs=512 * 24, os_=512 * 24) == _lib.MAGI_ERR_UNSUPPORTED
+    assert ffa(q=None) == _lib.MAGI_ERR_INVALID_ARG
+    assert ffa(kvs=20) == _lib.MAGI_ERR_INVALID_ARG
+    assert ffa(kvs=28) == _lib.MAGI_ERR_INVALID_ARG      # not a 16-byte multiple
+    assert ffa(out=C.c_void_p(4100)) == _lib.MAGI_ERR_INVALID_ARG
+    assert ffa(lse=C.c_void_p(4098)) == _lib.MAGI_ERR_INVALID_ARG
+    assert ffa(scale=float("nan")) == _lib.MAGI_ERR_INVALID_ARG
+    assert ffa(w=None) == _lib.MAGI_ERR_INVALID_ARG
+    assert ffa(nw=-1) == _lib.MAGI_ERR_INVALID_ARG
+    assert ffa(nq=-2) == _lib.MAGI_ERR_INVALID_ARG
+    assert ffa(nq=0, q=None, out=None) == _lib.MAGI_ERR_INVALID_ARG  # work for no rows
+    assert b"work" in L.magi_last_error()
