@@ -67,11 +67,13 @@ def run_gpu(wl, steps, warmup, seed=0):
 
     def step(record):
         plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, tdt, dev)
-        ops.qknorm_rope(q, k, gq, gk, pq, pk, base, wl.eps, q_out=qh, k_out=kh)
+        # the softmax scale (times log2 e) is folded into K by the prologue
+        ops.qknorm_rope(q, k, gq, gk, pq, pk, base, wl.eps, q_out=qh, k_out=kh,
+                        k_scale=wl.softmax_scale * ops.LOG2E)
         if record:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-        ops.ffa_fwd(qh, kh, v, plan, out=out, lse=lse)
+        ops.ffa_fwd(qh, kh, v, plan, out=out, lse=lse, softmax_scale=ops.LN2)
         if record:
             b.record(stream)
             ev.append((a, b))

@@ -44,7 +44,8 @@ extern "C" int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, i
                                     const void* k_in, void* k_out, int64_t nk, int32_t hkv, int64_t k_tok_stride,
                                     int32_t head_dim, int32_t dtype, const float* gain_q, const float* gain_k,
                                     int32_t gain_head_stride, float eps, const int32_t* pos_q,
-                                    const int32_t* pos_k, const float* rope_base, void* stream) {
+                                    const int32_t* pos_k, const float* rope_base, float q_scale, float k_scale,
+                                    void* stream) {
   int32_t st;
   if ((st = check_common(head_dim, dtype)) != MAGI_OK) return st;
   if ((st = check_tensor("q_in", q_in, nq, hq, q_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
@@ -61,10 +62,12 @@ extern "C" int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, i
     return fail(MAGI_ERR_INVALID_ARG, "gain_head_stride must be 0 or head_dim");
   if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MAGI_ERR_INVALID_ARG, "eps must be finite and >= 0");
   if (rope_base == nullptr) return fail(MAGI_ERR_INVALID_ARG, "rope_base is NULL");
+  if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || q_scale == 0.f || k_scale == 0.f)
+    return fail(MAGI_ERR_INVALID_ARG, "q_scale and k_scale must be finite and non-zero");
 
   QkArgs a{};
-  a.side[0] = {q_in, q_out, nq, hq, q_tok_stride, gain_q, pos_q};
-  a.side[1] = {k_in, k_out, nk > 0 ? nk : 0, nk > 0 ? hkv : 1, k_tok_stride, gain_k, pos_k};
+  a.side[0] = {q_in, q_out, nq, hq, q_tok_stride, gain_q, pos_q, q_scale};
+  a.side[1] = {k_in, k_out, nk > 0 ? nk : 0, nk > 0 ? hkv : 1, k_tok_stride, gain_k, pos_k, k_scale};
   a.head_dim = head_dim;
   a.dtype = dtype;
   a.gain_head_stride = gain_head_stride;

@@ -50,6 +50,7 @@ constexpr int TK = 64;      // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1e30f;  // finite "minus infinity" for the running max
+constexpr float kShift = 8.0f;     // move the softmax reference when a score exceeds it by 2^8
 
 template <int D>
 struct Cfg {
@@ -73,16 +74,81 @@ __device__ inline int64_t causal_end(const magi_attn_slice& s, int64_t ke, int64
   return e < ke ? e : ke;
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void ffa_fwd_bf16(FfaArgs a) {
+// One slice as seen by one work item.  Every field is the same for the whole
+// workgroup and lives in scalar registers.
+struct SliceGeo {
+  int64_t ks;     // first key
+  int64_t khi;    // one past the last key that any row of the item sees
+  int64_t kfull;  // keys below this are visible to every row of the item
+  int64_t ke;     // slice key end, clamped to nk
+  int64_t koff;   // k_end - q_end: a causal row r sees keys below koff + r + 1
+  int32_t causal;
+  int32_t si;     // position in the tile-slice list
+};
+
+__device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// First slice at or after list position si that shows this item a key.
+// Returns false when the list is exhausted.
+__device__ __forceinline__ bool find_slice(const FfaArgs& a, const magi_work_item& wi, int si, int64_t first_tok,
+                                           int64_t last_tok, SliceGeo& g) {
+  const int end = wi.slice_end < a.num_tile_slices ? wi.slice_end : a.num_tile_slices;
+  for (si = si < 0 ? 0 : si; si < end; ++si) {
+    const int sidx = uni(a.tile_slices[si]);
+    if (sidx < 0 || sidx >= a.num_slices) continue;
+    const magi_attn_slice* sp = a.slices + sidx;
+    const int64_t qs = uni(sp->q_start), qe = uni(sp->q_end), k0 = uni(sp->k_start), k1 = uni(sp->k_end);
+    const int32_t causal = uni(sp->mask_type) == MAGI_MASK_CAUSAL;
+    const int64_t ks = k0 > 0 ? k0 : 0;
+    const int64_t ke = k1 < a.nk ? k1 : a.nk;
+    // a well-formed schedule only lists slices that cover every row of the item
+    if (ks >= ke || first_tok < qs || last_tok >= qe) continue;
+    const int64_t koff = k1 - qe;
+    const int64_t khi = causal ? (koff + last_tok + 1 < ke ? koff + last_tok + 1 : ke) : ke;
+    if (khi <= ks) continue;
+    g.ks = ks;
+    g.khi = khi;
+    g.kfull = causal ? (koff + first_tok + 1 < ke ? koff + first_tok + 1 : ke) : ke;
+    g.ke = ke;
+    g.koff = koff;
+    g.causal = causal;
+    g.si = si;
+    return true;
+  }
+  return false;
+}
+
+// Max of x over the lane pair (l, l ^ 32), and x from the partner lane.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_other(float x, int h) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(h ? r[0] : r[1]);
+}
+
+// PRESCALED: the caller folded softmax_scale * log2(e) into Q or K, so the
+// scores leave the MFMA already in log2 units and need no multiply.
+template <int D, bool PRESCALED>
+__global__ __launch_bounds__(kThreads, 2) void ffa_fwd_bf16(FfaArgs a) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[TK * C::KROW];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[TK * C::VROW];
+  constexpr int NCH = (TK * C::CH + kThreads - 1) / kThreads;  // 16-byte K (and V) chunks per thread per tile
+  // 32-key blocks whose scores are held at once: both for d=24, one at a
+  // time for d=48 where the larger accumulators leave fewer registers
+  constexpr int KG = D <= 32 ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][TK * C::KROW];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][TK * C::VROW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, ln = lane & 31;
-  const magi_work_item wi = a.work[blockIdx.x];
+  magi_work_item wi = a.work[blockIdx.x];
+  wi.q_start = uni(wi.q_start);
+  wi.q_len = uni(wi.q_len);
+  wi.slice_begin = uni(wi.slice_begin);
+  wi.slice_end = uni(wi.slice_end);
+  wi.kv_group = uni(wi.kv_group);
   const int G = a.hq / a.hkv;
   const int cap = kRows / G;
   if (wi.q_start < 0 || wi.q_len <= 0 || (int64_t)wi.q_start + wi.q_len > a.nq || wi.kv_group < 0 ||
@@ -94,17 +160,19 @@ __global__ __launch_bounds__(kThreads) void ffa_fwd_bf16(FfaArgs a) {
   const __bf16* __restrict__ kp = reinterpret_cast<const __bf16*>(a.k);
   const __bf16* __restrict__ vp = reinterpret_cast<const __bf16*>(a.v);
 
-  // constant padding columns of the LDS tiles: K columns D..DK-1 are 0, V
-  // column D is 1 (denominator), V columns D+1..DV-1 are 0
-  if constexpr (C::DK > D)
-    for (int i = tid; i < TK * (C::DK - D); i += kThreads)
-      Ks[(i / (C::DK - D)) * C::KROW + D + i % (C::DK - D)] = (__bf16)0.0f;
-  for (int i = tid; i < TK * (C::DV - D); i += kThreads) {
-    const int c = D + i % (C::DV - D);
-    Vs[(i / (C::DV - D)) * C::VROW + c] = (__bf16)(c == D ? 1.0f : 0.0f);
+  // constant padding columns of both LDS buffers: K columns D..DK-1 are 0,
+  // V column D is 1 (it accumulates the softmax denominator), D+1..DV-1 are 0
+  for (int b = 0; b < 2; ++b) {
+    if constexpr (C::DK > D)
+      for (int i = tid; i < TK * (C::DK - D); i += kThreads)
+        Ks[b][(i / (C::DK - D)) * C::KROW + D + i % (C::DK - D)] = (__bf16)0.0f;
+    for (int i = tid; i < TK * (C::DV - D); i += kThreads) {
+      const int col = D + i % (C::DV - D);
+      Vs[b][(i / (C::DV - D)) * C::VROW + col] = (__bf16)(col == D ? 1.0f : 0.0f);
+    }
   }
 
-  // this lane's two query rows (one per 32-row column block)
+  // this lane's two query rows (one per 32-row column block) as MFMA B operands
   int64_t qi[2];
   int hg[2];
   bool rvalid[2];
@@ -126,122 +194,196 @@ __global__ __launch_bounds__(kThreads) void ffa_fwd_bf16(FfaArgs a) {
     }
   }
 
+  // Softmax state per row: the reference m (log2 units) is subtracted inside
+  // the score MFMA by starting its accumulator at -m (cinit).  m moves only
+  // when a row sees its first key or when a score exceeds m by more than
+  // kShift, so the common tile needs no rescale (P <= 2^kShift stays finite).
   const float c = a.scale * kLog2e;
-  float m[2] = {kNegBig, kNegBig};
+  const float cinv = PRESCALED ? 1.0f : 1.0f / c;
+  float m[2] = {0.f, 0.f};
+  bool init[2] = {false, false};
+  f32x16 cinit[2];
   f32x16 o[2][C::MB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < 2; ++nb) {
+    cinit[nb] = (f32x16){};
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) o[nb][mb] = (f32x16){};
+  }
 
   const int64_t first_tok = wi.q_start, last_tok = (int64_t)wi.q_start + qlen - 1;
-  for (int si = wi.slice_begin; si < wi.slice_end; ++si) {
-    if (si < 0 || si >= a.num_tile_slices) break;
-    const int sidx = a.tile_slices[si];
-    if (sidx < 0 || sidx >= a.num_slices) continue;
-    const magi_attn_slice sl = a.slices[sidx];
-    const int64_t ks = sl.k_start > 0 ? sl.k_start : 0;
-    const int64_t ke = sl.k_end < a.nk ? sl.k_end : a.nk;
-    if (ks >= ke) continue;
-    const bool causal = sl.mask_type == MAGI_MASK_CAUSAL;
-    const bool inq_first = first_tok >= sl.q_start && first_tok < sl.q_end;
-    const bool inq_last = last_tok >= sl.q_start && last_tok < sl.q_end;
-    if (!inq_first || !inq_last) continue;  // a well-formed schedule never does this
-    const int64_t khi = causal ? causal_end(sl, ke, last_tok) : ke;
-    const int64_t kfull = causal ? causal_end(sl, ke, first_tok) : ke;
-    int64_t re[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) re[nb] = !rvalid[nb] ? ks : (causal ? causal_end(sl, ke, qi[nb]) : ke);
+  const int li = lane & 15;
+  const int dgrp = ((lane >> 4) & 1) * 16;
+  // key offset (within a 32-key block) of accumulator element i of this lane
+  auto key_of = [&](int i) { return 8 * (i / 4) + 4 * h + (i % 4); };
+  uint4 kr[NCH], vr[NCH];
 
-    for (int64_t kt = ks; kt < khi; kt += TK) {
-      __syncthreads();  // previous tile fully consumed (and padding columns written)
-      for (int ci = tid; ci < TK * C::CH; ci += kThreads) {
-        const int r = ci / C::CH, part = ci % C::CH;
-        const int64_t key = kt + r;
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+  auto load_tile = [&](int64_t kt, int64_t khi) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int ci = tid + j * kThreads;
+      kr[j] = make_uint4(0, 0, 0, 0);
+      vr[j] = make_uint4(0, 0, 0, 0);
+      if (ci < TK * C::CH) {
+        const int64_t key = kt + ci / C::CH;
         if (key < khi) {
-          const int64_t off = key * a.kv_stride + (int64_t)g * D + part * 8;
-          kv = *reinterpret_cast<const uint4*>(kp + off);
-          vv = *reinterpret_cast<const uint4*>(vp + off);
+          const int64_t off = key * a.kv_stride + (int64_t)g * D + (ci % C::CH) * 8;
+          kr[j] = *reinterpret_cast<const uint4*>(kp + off);
+          vr[j] = *reinterpret_cast<const uint4*>(vp + off);
         }
-        *reinterpret_cast<uint4*>(&Ks[r * C::KROW + part * 8]) = kv;
-        *reinterpret_cast<uint4*>(&Vs[r * C::VROW + part * 8]) = vv;
       }
-      __syncthreads();
-      const bool masked = (kt + TK > kfull);
-
-      // S^T = K . Q^T for 64 keys x 64 rows: s[kb][nb], lane holds 16 keys of one row
-      f32x16 s[2][2];
+    }
+  };
+  auto store_tile = [&](int b) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int j = 0; j < NCH; ++j) {
+      const int ci = tid + j * kThreads;
+      if (ci < TK * C::CH) {
+        const int r = ci / C::CH, part = ci % C::CH;
+        *reinterpret_cast<uint4*>(&Ks[b][r * C::KROW + part * 8]) = kr[j];
+        *reinterpret_cast<uint4*>(&Vs[b][r * C::VROW + part * 8]) = vr[j];
+      }
+    }
+  };
+
+  SliceGeo cg;
+  bool have = find_slice(a, wi, wi.slice_begin, first_tok, last_tok, cg);
+  int64_t kt = cg.ks;
+  if (have) {
+    load_tile(kt, cg.khi);
+    store_tile(0);
+  }
+  int buf = 0;
+  while (have) {
+    // the tile after this one: next in the slice, else the next slice's first
+    SliceGeo ng = cg;
+    int64_t nkt = kt + TK;
+    bool have_next = true;
+    if (nkt >= cg.khi) {
+      have_next = find_slice(a, wi, cg.si + 1, first_tok, last_tok, ng);
+      nkt = ng.ks;
+    }
+    __syncthreads();  // tile `buf` is in LDS; buffer buf^1 is no longer read
+    if (have_next) load_tile(nkt, ng.khi);  // in flight while this tile is computed
+
+    const bool masked = kt + TK > cg.kfull;
+    int lim[2];  // keys at tile offset >= lim[nb] are hidden from the row
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      int64_t re = cg.ke;
+      if (cg.causal) {
+        const int64_t ce = cg.koff + qi[nb] + 1;
+        re = ce < re ? ce : re;
+      }
+      if (!rvalid[nb]) re = kt;
+      const int64_t rel = re - kt;
+      lim[nb] = rel < 0 ? 0 : (rel > TK ? TK : (int)rel);
+    }
+    const __bf16* Kb = Ks[buf];
+    __attribute__((address_space(3))) __bf16* Vb = (__attribute__((address_space(3))) __bf16*)Vs[buf];
+
+#pragma unroll
+    for (int kb0 = 0; kb0 < 2; kb0 += KG) {
+      // S'^T = K . Q^T - m for KG*32 keys x 64 rows; a lane holds 16 keys of one row per block
+      f32x16 s[KG][2];
+#pragma unroll
+      for (int kg = 0; kg < KG; ++kg) {
+        const int kb = kb0 + kg;
         bf16x8 kop[C::KS];
 #pragma unroll
         for (int ks2 = 0; ks2 < C::KS; ++ks2)
-          kop[ks2] = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + ln) * C::KROW + 16 * ks2 + 8 * h]);
+          kop[ks2] = *reinterpret_cast<const bf16x8*>(&Kb[(kb * 32 + ln) * C::KROW + 16 * ks2 + 8 * h]);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-          f32x16 acc = {};
+          f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qreg[nb][0], cinit[nb], 0, 0, 0);
 #pragma unroll
-          for (int ks2 = 0; ks2 < C::KS; ++ks2)
+          for (int ks2 = 1; ks2 < C::KS; ++ks2)
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks2], qreg[nb][ks2], acc, 0, 0, 0);
-          s[kb][nb] = acc;
+          s[kg][nb] = acc;
         }
       }
-
-      // online softmax (log2 domain)
-      bf16x8 pb[2][2][2];  // [kb][16-key half][nb]
+      if (masked) {
+#pragma unroll
+        for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if ((kb0 + kg) * 32 + key_of(i) >= lim[nb]) s[kg][nb][i] = -INFINITY;
+      }
+      // row maxima of the shifted scores; move m only where needed
+      bool sh[2];
+      float delta[2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        float mx = -INFINITY;
+        float mx = s[0][nb][0];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float x = s[kb][nb][i] * c;
-            if (masked) {
-              const int64_t key = kt + kb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
-              if (key >= re[nb]) x = -INFINITY;
-            }
-            s[kb][nb][i] = x;
-            mx = fmaxf(mx, x);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m[nb], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m[nb] - mnew);
-        m[nb] = mnew;
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kg][nb][i]);
+        mx = pair_max(mx);
+        const float xm = PRESCALED ? mx : mx * c;
+        sh[nb] = (!init[nb] && xm > -INFINITY) || xm > kShift;
+        delta[nb] = sh[nb] ? xm : 0.f;
+        init[nb] = init[nb] || xm > -INFINITY;
+      }
+      if (__any(sh[0] || sh[1])) {
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) o[nb][mb] *= alpha;
+        for (int nb = 0; nb < 2; ++nb) {
+          const float alpha = __builtin_amdgcn_exp2f(-delta[nb]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int mb = 0; mb < C::MB; ++mb) o[nb][mb] *= alpha;
+          m[nb] += delta[nb];
+          const float dsub = delta[nb] * cinv;
+#pragma unroll
+          for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kg][nb][i] -= dsub;
+          const float ci0 = -m[nb] * cinv;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) cinit[nb][i] = ci0;
+        }
+      }
+#pragma unroll
+      for (int kg = 0; kg < KG; ++kg) {
+        const int kb = kb0 + kg;
+        // P = 2^(S'), rounded to bf16, already in the B-operand layout of P^T
+        bf16x8 pb[2][2];  // [16-key half][nb]
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
           for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              pb[kb][i2][nb][e] = (__bf16)__builtin_amdgcn_exp2f(s[kb][nb][8 * i2 + e] - mnew);
-      }
-
-      // O^T += V^T . P^T ; V^T operand through the LDS transpose read
-      const int li = lane & 15;
-      const int dgrp = ((lane >> 4) & 1) * 16;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+            for (int e = 0; e < 8; ++e) {
+              const float x = PRESCALED ? s[kg][nb][8 * i2 + e] : s[kg][nb][8 * i2 + e] * c;
+              pb[i2][nb][e] = (__bf16)__builtin_amdgcn_exp2f(x);
+            }
+        // O^T += V^T . P^T ; the V^T operand comes from the row-major V tile
+        // through the LDS transpose read
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2) {
           const int krow = kb * 32 + 16 * i2 + 4 * h + li / 4;
 #pragma unroll
           for (int mb = 0; mb < C::MB; ++mb) {
             const int dcol = mb * 32 + dgrp + 4 * (li % 4);
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)((__attribute__((address_space(3))) __bf16*)Vs + krow * C::VROW + dcol));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)((__attribute__((address_space(3))) __bf16*)Vs + (krow + 8) * C::VROW + dcol));
-            const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + krow * C::VROW + dcol));
+            const s16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + (krow + 8) * C::VROW + dcol));
+            const bf16x8 vop =
+                __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
-              o[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb][i2][nb], o[nb][mb], 0, 0, 0);
+              o[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[i2][nb], o[nb][mb], 0, 0, 0);
           }
         }
+      }
     }
+
+    if (have_next) store_tile(buf ^ 1);
+    cg = ng;
+    kt = nkt;
+    have = have_next;
+    buf ^= 1;
   }
 
   // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
@@ -249,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void ffa_fwd_bf16(FfaArgs a) {
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const float mine = o[nb][C::LMB][C::LIDX];
-    const float other = __shfl_xor(mine, 32);
+    const float other = pair_other(mine, h);  // all 64 lanes must take part in the swap
     const float l = h == 0 ? mine : other;
     if (!rvalid[nb]) continue;
     const float inv = l > 0.f ? 1.0f / l : 0.f;
@@ -271,7 +413,6 @@ __global__ __launch_bounds__(kThreads) void ffa_fwd_bf16(FfaArgs a) {
       a.lse[qi[nb] * a.hq + g * G + hg[nb]] = l > 0.f ? (m[nb] + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
-
 // fp32 path (small shapes): one thread per query row, keys streamed from
 // global memory, fp32 online softmax.  Same work list and masking rules.
 template <int D>
@@ -336,10 +477,19 @@ hipError_t launch_ffa_fwd(const FfaArgs& a, hipStream_t stream) {
   if (a.num_work == 0) return hipSuccess;
   const dim3 grid(a.num_work), block(kThreads);
   if (a.dtype == MAGI_DTYPE_BF16) {
-    if (a.head_dim == 24)
-      hipLaunchKernelGGL(ffa_fwd_bf16<24>, grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL(ffa_fwd_bf16<48>, grid, block, 0, stream, a);
+    // scores arrive in log2 units when the caller folded scale * log2(e) into Q or K
+    const bool pre = fabsf(a.scale * kLog2e - 1.0f) < 1e-6f;
+    if (a.head_dim == 24) {
+      if (pre)
+        hipLaunchKernelGGL((ffa_fwd_bf16<24, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((ffa_fwd_bf16<24, false>), grid, block, 0, stream, a);
+    } else {
+      if (pre)
+        hipLaunchKernelGGL((ffa_fwd_bf16<48, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((ffa_fwd_bf16<48, false>), grid, block, 0, stream, a);
+    }
   } else {
     if (a.head_dim == 24)
       hipLaunchKernelGGL(ffa_fwd_f32<24>, grid, block, 0, stream, a);

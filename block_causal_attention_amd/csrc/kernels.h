@@ -17,6 +17,7 @@ struct QkSide {
   int64_t tok_stride;  // elements between consecutive tokens
   const float* gain;
   const int32_t* pos;  // [n][3]
+  float out_scale;     // factor applied to the result before it is stored
 };
 
 struct QkArgs {

@@ -8,6 +8,9 @@
 // (study notes, same section, Block-Causal Attention bullet; 量子位 article,
 // "Block-Causal Attention").
 //
+// An optional output factor lets the caller fold the softmax scale (times
+// log2 e) into K once here instead of into every score of the attention.
+//
 // The kernel is HBM-bound: it reads and writes each element once.  One block
 // owns a run of whole tokens; the rotation table (cos, sin per token and
 // channel pair) is shared by all heads of a token, so it is built once per
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(QkArgs a, int blo
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < D; ++i) ss = fmaf(x[i], x[i], ss);
-    const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
+    const float r = 1.0f / sqrtf(ss / (float)D + a.eps) * s.out_scale;
     const float* g = s.gain + (int64_t)h * a.gain_head_stride;
 #pragma unroll
     for (int i = 0; i < D; ++i) x[i] = x[i] * r * g[i];

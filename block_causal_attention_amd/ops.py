@@ -16,6 +16,9 @@ import torch
 from . import _lib
 from ._lib import AttnSlice, SeqDesc, WorkItem, check, lib
 
+LN2 = 0.6931471805599453
+LOG2E = 1.4426950408889634
+
 __all__ = ["build_slices", "schedule", "Plan", "make_plan", "plan_for_videos", "qknorm_rope",
            "ffa_fwd", "default_tile_q", "dtype_code"]
 
@@ -133,8 +136,9 @@ def _check_3d(name, t, heads, d):
 def qknorm_rope(q: torch.Tensor, k: Optional[torch.Tensor], gain_q: torch.Tensor,
                 gain_k: Optional[torch.Tensor], pos_q: torch.Tensor, pos_k: Optional[torch.Tensor],
                 rope_base: torch.Tensor, eps: float = 1e-6, q_out: Optional[torch.Tensor] = None,
-                k_out: Optional[torch.Tensor] = None):
-    """magi_qknorm_rope: QK-Norm then 3D RoPE; returns (q_out, k_out)."""
+                k_out: Optional[torch.Tensor] = None, q_scale: float = 1.0, k_scale: float = 1.0):
+    """magi_qknorm_rope: QK-Norm then 3D RoPE (results times q_scale / k_scale);
+    returns (q_out, k_out)."""
     d = q.shape[-1]
     _check_3d("q", q, q.shape[1], d)
     q_out = torch.empty_like(q) if q_out is None else q_out
@@ -159,7 +163,7 @@ def qknorm_rope(q: torch.Tensor, k: Optional[torch.Tensor], gain_q: torch.Tensor
         _ptr(q), _ptr(q_out), q.shape[0], q.shape[1], q.stride(0),
         _ptr(k), _ptr(k_out), nk, hkv, ks, d, dtype_code(q.dtype),
         _ptr(gain_q), _ptr(gain_k), ghs, float(eps), _ptr(pos_q), _ptr(pos_k), _ptr(rope_base),
-        _stream(q)))
+        float(q_scale), float(k_scale), _stream(q)))
     return q_out, k_out
 
 

@@ -146,8 +146,11 @@ int32_t magi_schedule(const magi_attn_slice* slices, int32_t num_slices,
  *   then for axis a in (t, h, w), channel pair (2j, 2j+1) of section a
  *   (head_dim/3 channels per section), angle = pos[i][a] * base_a^(-2j/(head_dim/3)):
  *   (y0, y1) -> (y0 cos - y1 sin, y0 sin + y1 cos).
- * Arithmetic is fp32; the result is stored in the input dtype
- * (round-to-nearest-even for bf16).  Output may alias input.
+ * then y is multiplied by q_scale (Q) or k_scale (K).  Arithmetic is fp32;
+ * the result is stored in the input dtype (round-to-nearest-even for bf16).
+ * Output may alias input.  Passing k_scale = softmax_scale * log2(e) and then
+ * softmax_scale = ln(2) to magi_ffa_fwd folds the softmax scale into K once,
+ * which removes one multiply per attention score.
  *
  * q_in, q_out   [device] [nq rows] x [hq heads] x [head_dim], row stride q_tok_stride
  *               elements (>= hq*head_dim), heads contiguous; 16-byte aligned
@@ -156,14 +159,15 @@ int32_t magi_schedule(const magi_attn_slice* slices, int32_t num_slices,
  * gain_q/gain_k [device] fp32 [head_dim] (gain_head_stride 0) or [heads][head_dim]
  *               (gain_head_stride = head_dim)
  * pos_q, pos_k  [device] int32 [n][3] latent (t, h, w) coordinates
- * rope_base     [device] fp32 [3] base frequency of the t, h, w axes
+ * rope_base     [device] fp32 [3] base frequency of the t, h, w axes (> 0)
+ * q_scale, k_scale  output factors (finite, non-zero; 1 = plain QK-Norm + RoPE)
  */
 int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, int32_t hq, int64_t q_tok_stride,
                          const void* k_in, void* k_out, int64_t nk, int32_t hkv, int64_t k_tok_stride,
                          int32_t head_dim, int32_t dtype,
                          const float* gain_q, const float* gain_k, int32_t gain_head_stride,
                          float eps, const int32_t* pos_q, const int32_t* pos_k,
-                         const float* rope_base, void* stream);
+                         const float* rope_base, float q_scale, float k_scale, void* stream);
 
 /*
  * magi_ffa_fwd -- Flex-Flash-Attention forward over a work list.   [device]
@@ -182,7 +186,8 @@ int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, int32_t hq, 
  * out          [device] [nq][hq][head_dim], row stride o_tok_stride elements
  * lse          [device] fp32 [nq][hq] (row stride hq), or NULL
  *              All tensor pointers 16-byte aligned, strides multiples of 8.
- * softmax_scale  <= 0 selects 1/sqrt(head_dim)
+ * softmax_scale  <= 0 selects 1/sqrt(head_dim); ln(2) means the scores are
+ *              already in log2 units (softmax scale folded into Q or K)
  * slices, work, tile_slices  [device] copies of magi_schedule's outputs made for
  *              the same nq, nk, hq, hkv, head_dim, dtype (items are clamped to
  *              the tensor bounds on the device, so a mismatched list cannot

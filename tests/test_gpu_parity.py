@@ -52,12 +52,13 @@ def dev_inputs(wl, inp):
                 pk=g(inp.pos_k), base=torch.tensor(wl.rope_base, dtype=torch.float32, device=DEV))
 
 
-def gpu_forward(wl, d, fresh_only=False):
-    """prologue (Q and K) then FFA over the builder's slices, as the benchmark runs it."""
-    k_src = d["k"]
-    qh, kh = ops.qknorm_rope(d["q"], k_src, d["gq"], d["gk"], d["pq"], d["pk"], d["base"], wl.eps)
+def gpu_forward(wl, d):
+    """prologue (Q and K, softmax scale folded into K) then FFA over the
+    builder's slices, exactly as the benchmark runs it."""
+    qh, kh = ops.qknorm_rope(d["q"], d["k"], d["gq"], d["gk"], d["pq"], d["pk"], d["base"], wl.eps,
+                             k_scale=wl.softmax_scale * ops.LOG2E)
     plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, d["q"].dtype)
-    O, L = ops.ffa_fwd(qh, kh, d["v"], plan)
+    O, L = ops.ffa_fwd(qh, kh, d["v"], plan, softmax_scale=ops.LN2)
     torch.cuda.synchronize()
     return qh, kh, O, L
 
@@ -82,6 +83,21 @@ def test_prologue_matches_oracle(name):
     want_k = oracle.rope_3d(oracle.qk_norm(np64(inp.k), np64(inp.gain_k), wl.eps), inp.pos_k.numpy(), inv)
     compare(np64(qh)[rows], want_q, wl.dtype, "q_hat")
     compare(np64(kh), want_k, wl.dtype, "k_hat")
+
+
+def test_prologue_output_scale():
+    note("prologue with q/k output scales")
+    wl = W.custom_block_causal(2, 2, 4, 5, 16, 2, 24)
+    inp = W.make_inputs(wl, 4)
+    d = dev_inputs(wl, inp)
+    qh, kh = ops.qknorm_rope(d["q"], d["k"], d["gq"], d["gk"], d["pq"], d["pk"], d["base"], wl.eps,
+                             q_scale=0.5, k_scale=0.2946)
+    torch.cuda.synchronize()
+    inv = oracle.rope_inv_freq(wl.rope_base, 24)
+    wq = oracle.rope_3d(oracle.qk_norm(np64(inp.q), np64(inp.gain_q), wl.eps), inp.pos_q.numpy(), inv) * 0.5
+    wk = oracle.rope_3d(oracle.qk_norm(np64(inp.k), np64(inp.gain_k), wl.eps), inp.pos_k.numpy(), inv) * 0.2946
+    compare(np64(qh), wq, "bf16", "q_hat")
+    compare(np64(kh), wk, "bf16", "k_hat")
 
 
 def test_prologue_per_head_gain_in_place_and_strided():
@@ -156,6 +172,17 @@ def test_ffa_causal_and_irregular_slices(d):
     q, k, v = rand((nq, 16, d), 4), rand((nk, 1, d), 5), rand((nk, 1, d), 6)
     O, L = ffa_case(q, k, v, np.array(slices), "bf16")
     assert torch.all(O[140:] == 0) and torch.all(torch.isneginf(L[140:]))
+
+
+@pytest.mark.parametrize("d", [24, 48])
+def test_ffa_prescaled_keys(d):
+    # K stored pre-multiplied by scale*log2(e) and softmax_scale = ln 2: the
+    # kernel takes its no-multiply path; the oracle sees the same rounded K
+    note(f"ffa prescaled K d={d}")
+    c = d ** -0.5 * ops.LOG2E
+    k = torch.from_numpy(rand((300, 2, d), 21) * c).to(torch.bfloat16).float().numpy()
+    seqs = [W.SeqDesc(100, 3, 3, 0, 0, (-1, -1, 1), 1, 1, 100)]
+    ffa_case(rand((300, 32, d), 20), k, rand((300, 2, d), 22), ops.build_slices(seqs), "bf16", scale=ops.LN2)
 
 
 def test_ffa_fp32_tiny_full():
