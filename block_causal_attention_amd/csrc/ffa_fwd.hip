@@ -42,6 +42,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kThreads = 256;
@@ -50,7 +51,17 @@ constexpr int TK = 64;      // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1e30f;  // finite "minus infinity" for the running max
-constexpr float kShift = 8.0f;     // move the softmax reference when a score exceeds it by 2^8
+constexpr int kBufCfg = 0x00020000;  // raw buffer resource word 3 (gfx9 family: 32-bit data format)
+constexpr float kShift = 8.0f;
+#ifndef MAGI_VROW_MODE
+#define MAGI_VROW_MODE 0
+#endif
+#ifndef MAGI_NB24
+#define MAGI_NB24 1
+#endif
+#ifndef MAGI_NB48
+#define MAGI_NB48 1
+#endif     // move the softmax reference when a score exceeds it by 2^8
 
 template <int D>
 struct Cfg {
@@ -59,7 +70,10 @@ struct Cfg {
   static constexpr int DV = (D + 1 + 31) / 32 * 32;   // V columns incl. the ones column
   static constexpr int MB = DV / 32;                  // 32-row blocks of O^T
   static constexpr int KROW = DK + 8;                 // LDS pitch of a K row (elements)
-  static constexpr int VROW = DV + 8;                 // LDS pitch of a V row (elements)
+  // LDS pitch of a V row (elements): ds_read_b64_tr_b16 has each group of
+  // 16 lanes read 4 consecutive rows x 32 bytes, so the pitch is chosen to
+  // put 4 consecutive rows in disjoint bank ranges
+  static constexpr int VROW = MAGI_VROW_MODE == 0 ? (DV == 32 ? 32 : DV + 32) : DV + 8;
   static constexpr int CH = D / 8;                    // 16-byte chunks per K/V row
   // position of the denominator (the ones column, V column D) in the O^T
   // accumulator of lane half 0: block D/32, index 4*((D%32)/8) + D%4
@@ -87,6 +101,17 @@ struct SliceGeo {
 };
 
 __device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Largest bf16 value <= x (x finite).
+__device__ __forceinline__ __bf16 bf16_floor(float x) {
+  __bf16 r = (__bf16)x;
+  if ((float)r > x) {
+    unsigned short b = __builtin_bit_cast(unsigned short, r);
+    b = (b & 0x7fff) == 0 ? 0x8001 : (b & 0x8000 ? b + 1 : b - 1);
+    r = __builtin_bit_cast(__bf16, b);
+  }
+  return r;
+}
 
 // First slice at or after list position si that shows this item a key.
 // Returns false when the list is exhausted.
@@ -130,10 +155,14 @@ __device__ __forceinline__ float pair_other(float x, int h) {
 
 // PRESCALED: the caller folded softmax_scale * log2(e) into Q or K, so the
 // scores leave the MFMA already in log2 units and need no multiply.
-template <int D, bool PRESCALED>
-__global__ __launch_bounds__(kThreads, 2) void ffa_fwd_bf16(FfaArgs a) {
+// NB: 32-row column blocks per wave.  The 256 rows of a work item are
+// spread over 256 / (32 NB) waves, so NB = 1 doubles the waves per SIMD
+// (more latency hiding) at the price of more LDS reads per score.
+template <int D, bool PRESCALED, int NB>
+__global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
   using C = Cfg<D>;
-  constexpr int NCH = (TK * C::CH + kThreads - 1) / kThreads;  // 16-byte K (and V) chunks per thread per tile
+  constexpr int NT = 512 / NB;  // threads per workgroup
+  constexpr int NCH = (TK * C::CH + NT - 1) / NT;  // 16-byte K (and V) chunks per thread per tile
   // 32-key blocks whose scores are held at once: both for d=24, one at a
   // time for d=48 where the larger accumulators leave fewer registers
   constexpr int KG = D <= 32 ? 2 : 1;
@@ -160,26 +189,34 @@ __global__ __launch_bounds__(kThreads, 2) void ffa_fwd_bf16(FfaArgs a) {
   const __bf16* __restrict__ kp = reinterpret_cast<const __bf16*>(a.k);
   const __bf16* __restrict__ vp = reinterpret_cast<const __bf16*>(a.v);
 
-  // constant padding columns of both LDS buffers: K columns D..DK-1 are 0,
-  // V column D is 1 (it accumulates the softmax denominator), D+1..DV-1 are 0
+  // When head_dim leaves padding in the Q.K contraction (24 -> 32), the
+  // running max rides in it: K padding column D holds 1 and the matching Q
+  // slot holds -m, so the score MFMA itself returns q.k - m.  Otherwise
+  // (48) the MFMA accumulator starts at -m instead.
+  constexpr bool AUG = C::DK > D;
+  // constant padding columns of both LDS buffers: K column D is 1 (AUG),
+  // K columns D+1..DK-1 are 0, V column D is 1 (it accumulates the softmax
+  // denominator), V columns D+1..DV-1 are 0
   for (int b = 0; b < 2; ++b) {
-    if constexpr (C::DK > D)
-      for (int i = tid; i < TK * (C::DK - D); i += kThreads)
-        Ks[b][(i / (C::DK - D)) * C::KROW + D + i % (C::DK - D)] = (__bf16)0.0f;
-    for (int i = tid; i < TK * (C::DV - D); i += kThreads) {
+    if constexpr (AUG)
+      for (int i = tid; i < TK * (C::DK - D); i += NT) {
+        const int col = D + i % (C::DK - D);
+        Ks[b][(i / (C::DK - D)) * C::KROW + col] = (__bf16)(col == D ? 1.0f : 0.0f);
+      }
+    for (int i = tid; i < TK * (C::DV - D); i += NT) {
       const int col = D + i % (C::DV - D);
       Vs[b][(i / (C::DV - D)) * C::VROW + col] = (__bf16)(col == D ? 1.0f : 0.0f);
     }
   }
 
   // this lane's two query rows (one per 32-row column block) as MFMA B operands
-  int64_t qi[2];
-  int hg[2];
-  bool rvalid[2];
-  bf16x8 qreg[2][C::KS];
+  int64_t qi[NB];
+  int hg[NB];
+  bool rvalid[NB];
+  bf16x8 qreg[NB][C::KS];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int n = wave * 64 + nb * 32 + ln;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = wave * (32 * NB) + nb * 32 + ln;
     const int t = n / G;
     hg[nb] = n % G;
     rvalid[nb] = (t < qlen);
@@ -195,17 +232,20 @@ __global__ __launch_bounds__(kThreads, 2) void ffa_fwd_bf16(FfaArgs a) {
   }
 
   // Softmax state per row: the reference m (log2 units) is subtracted inside
-  // the score MFMA by starting its accumulator at -m (cinit).  m moves only
-  // when a row sees its first key or when a score exceeds m by more than
-  // kShift, so the common tile needs no rescale (P <= 2^kShift stays finite).
+  // the score MFMA (Q padding slot or accumulator start, see AUG).  m moves
+  // only when a row sees its first key or when a score exceeds m by more
+  // than kShift, so the common tile needs no rescale (P <= 2^kShift stays
+  // finite).  With AUG, m is kept exactly representable in bf16.
   const float c = a.scale * kLog2e;
   const float cinv = PRESCALED ? 1.0f : 1.0f / c;
-  float m[2] = {0.f, 0.f};
-  bool init[2] = {false, false};
-  f32x16 cinit[2];
-  f32x16 o[2][C::MB];
+  float m[NB];
+  bool init[NB];
+  f32x16 cinit[NB];
+  f32x16 o[NB][C::MB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
+    m[nb] = 0.f;
+    init[nb] = false;
     cinit[nb] = (f32x16){};
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) o[nb][mb] = (f32x16){};
@@ -216,32 +256,40 @@ __global__ __launch_bounds__(kThreads, 2) void ffa_fwd_bf16(FfaArgs a) {
   const int dgrp = ((lane >> 4) & 1) * 16;
   // key offset (within a 32-key block) of accumulator element i of this lane
   auto key_of = [&](int i) { return 8 * (i / 4) + 4 * h + (i % 4); };
-  uint4 kr[NCH], vr[NCH];
+  // K/V tiles are fetched with buffer loads whose range ends at the last
+  // visible key, so rows past it read as zeros with no per-lane test; each
+  // thread's byte offset inside a tile never changes.
+  u32x4 kr[NCH], vr[NCH];
+  int ch_off[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int ci = tid + j * NT;
+    ch_off[j] = (ci / C::CH) * (int)a.kv_stride * 2 + (ci % C::CH) * 16;
+  }
+  const int64_t kv_row_bytes = a.kv_stride * 2;
 
   auto load_tile = [&](int64_t kt, int64_t khi) {
+    const int64_t elem0 = kt * a.kv_stride + (int64_t)g * D;
+    const int64_t valid = (khi - kt - 1) * kv_row_bytes + D * 2;
+    const int nrec = valid <= 0 ? 0 : (valid > 0x7fffffff ? 0x7fffffff : (int)valid);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kp + elem0), (short)0, nrec, kBufCfg);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vp + elem0), (short)0, nrec, kBufCfg);
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int ci = tid + j * kThreads;
-      kr[j] = make_uint4(0, 0, 0, 0);
-      vr[j] = make_uint4(0, 0, 0, 0);
-      if (ci < TK * C::CH) {
-        const int64_t key = kt + ci / C::CH;
-        if (key < khi) {
-          const int64_t off = key * a.kv_stride + (int64_t)g * D + (ci % C::CH) * 8;
-          kr[j] = *reinterpret_cast<const uint4*>(kp + off);
-          vr[j] = *reinterpret_cast<const uint4*>(vp + off);
-        }
+      if (tid + j * NT < TK * C::CH) {
+        kr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ch_off[j], 0, 0));
+        vr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ch_off[j], 0, 0));
       }
     }
   };
   auto store_tile = [&](int b) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int ci = tid + j * kThreads;
+      const int ci = tid + j * NT;
       if (ci < TK * C::CH) {
         const int r = ci / C::CH, part = ci % C::CH;
-        *reinterpret_cast<uint4*>(&Ks[b][r * C::KROW + part * 8]) = kr[j];
-        *reinterpret_cast<uint4*>(&Vs[b][r * C::VROW + part * 8]) = vr[j];
+        *reinterpret_cast<u32x4*>(&Ks[b][r * C::KROW + part * 8]) = kr[j];
+        *reinterpret_cast<u32x4*>(&Vs[b][r * C::VROW + part * 8]) = vr[j];
       }
     }
   };
@@ -267,9 +315,9 @@ __global__ __launch_bounds__(kThreads, 2) void ffa_fwd_bf16(FfaArgs a) {
     if (have_next) load_tile(nkt, ng.khi);  // in flight while this tile is computed
 
     const bool masked = kt + TK > cg.kfull;
-    int lim[2];  // keys at tile offset >= lim[nb] are hidden from the row
+    int lim[NB];  // keys at tile offset >= lim[nb] are hidden from the row
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
       int64_t re = cg.ke;
       if (cg.causal) {
         const int64_t ce = cg.koff + qi[nb] + 1;
@@ -285,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffa_fwd_bf16(FfaArgs a) {
 #pragma unroll
     for (int kb0 = 0; kb0 < 2; kb0 += KG) {
       // S'^T = K . Q^T - m for KG*32 keys x 64 rows; a lane holds 16 keys of one row per block
-      f32x16 s[KG][2];
+      f32x16 s[KG][NB];
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
         const int kb = kb0 + kg;
@@ -294,8 +342,9 @@ __global__ __launch_bounds__(kThreads, 2) void ffa_fwd_bf16(FfaArgs a) {
         for (int ks2 = 0; ks2 < C::KS; ++ks2)
           kop[ks2] = *reinterpret_cast<const bf16x8*>(&Kb[(kb * 32 + ln) * C::KROW + 16 * ks2 + 8 * h]);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qreg[nb][0], cinit[nb], 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb) {
+          f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qreg[nb][0], AUG ? (f32x16){} : cinit[nb],
+                                                               0, 0, 0);
 #pragma unroll
           for (int ks2 = 1; ks2 < C::KS; ++ks2)
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks2], qreg[nb][ks2], acc, 0, 0, 0);
@@ -306,16 +355,16 @@ __global__ __launch_bounds__(kThreads, 2) void ffa_fwd_bf16(FfaArgs a) {
 #pragma unroll
         for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
+          for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
               if ((kb0 + kg) * 32 + key_of(i) >= lim[nb]) s[kg][nb][i] = -INFINITY;
       }
       // row maxima of the shifted scores; move m only where needed
-      bool sh[2];
-      float delta[2];
+      bool sh[NB];
+      float delta[NB];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         float mx = s[0][nb][0];
 #pragma unroll
         for (int kg = 0; kg < KG; ++kg)
@@ -327,30 +376,47 @@ __global__ __launch_bounds__(kThreads, 2) void ffa_fwd_bf16(FfaArgs a) {
         delta[nb] = sh[nb] ? xm : 0.f;
         init[nb] = init[nb] || xm > -INFINITY;
       }
-      if (__any(sh[0] || sh[1])) {
+      bool any_sh = false;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const float alpha = __builtin_amdgcn_exp2f(-delta[nb]);
+      for (int nb = 0; nb < NB; ++nb) any_sh |= sh[nb];
+      if (__any(any_sh)) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          float mnew = m[nb] + delta[nb];
+          __bf16 slot;
+          if constexpr (AUG) {
+            // the score MFMA subtracts a bf16 copy of m (unscaled units):
+            // round it toward larger m so no score can exceed it by more
+            // than the rounding step, and track exactly that value
+            slot = bf16_floor(-mnew * cinv);
+            mnew = PRESCALED ? -(float)slot : -(float)slot * c;
+          }
+          const float step = mnew - m[nb];
+          m[nb] = mnew;
+          const float alpha = __builtin_amdgcn_exp2f(-step);
 #pragma unroll
           for (int mb = 0; mb < C::MB; ++mb) o[nb][mb] *= alpha;
-          m[nb] += delta[nb];
-          const float dsub = delta[nb] * cinv;
+          const float dsub = step * cinv;
 #pragma unroll
           for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[kg][nb][i] -= dsub;
-          const float ci0 = -m[nb] * cinv;
+          if constexpr (AUG) {
+            qreg[nb][C::KS - 1][0] = h ? slot : qreg[nb][C::KS - 1][0];
+          } else {
+            const float ci0 = -mnew * cinv;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) cinit[nb][i] = ci0;
+            for (int i = 0; i < 16; ++i) cinit[nb][i] = ci0;
+          }
         }
       }
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
         const int kb = kb0 + kg;
         // P = 2^(S'), rounded to bf16, already in the B-operand layout of P^T
-        bf16x8 pb[2][2];  // [16-key half][nb]
+        bf16x8 pb[2][NB];  // [16-key half][nb]
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
@@ -372,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffa_fwd_bf16(FfaArgs a) {
             const bf16x8 vop =
                 __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
               o[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[i2][nb], o[nb][mb], 0, 0, 0);
           }
         }
@@ -389,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffa_fwd_bf16(FfaArgs a) {
   // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
   __bf16* __restrict__ op = reinterpret_cast<__bf16*>(a.out);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const float mine = o[nb][C::LMB][C::LIDX];
     const float other = pair_other(mine, h);  // all 64 lanes must take part in the swap
     const float l = h == 0 ? mine : other;
@@ -479,16 +545,17 @@ hipError_t launch_ffa_fwd(const FfaArgs& a, hipStream_t stream) {
   if (a.dtype == MAGI_DTYPE_BF16) {
     // scores arrive in log2 units when the caller folded scale * log2(e) into Q or K
     const bool pre = fabsf(a.scale * kLog2e - 1.0f) < 1e-6f;
+    constexpr int NB24 = MAGI_NB24, NB48 = MAGI_NB48;
     if (a.head_dim == 24) {
       if (pre)
-        hipLaunchKernelGGL((ffa_fwd_bf16<24, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((ffa_fwd_bf16<24, true, NB24>), grid, dim3(512 / NB24), 0, stream, a);
       else
-        hipLaunchKernelGGL((ffa_fwd_bf16<24, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((ffa_fwd_bf16<24, false, NB24>), grid, dim3(512 / NB24), 0, stream, a);
     } else {
       if (pre)
-        hipLaunchKernelGGL((ffa_fwd_bf16<48, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((ffa_fwd_bf16<48, true, NB48>), grid, dim3(512 / NB48), 0, stream, a);
       else
-        hipLaunchKernelGGL((ffa_fwd_bf16<48, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((ffa_fwd_bf16<48, false, NB48>), grid, dim3(512 / NB48), 0, stream, a);
     }
   } else {
     if (a.head_dim == 24)
