@@ -60,6 +60,7 @@ def run_gpu(wl, steps, warmup, seed=0):
     base = torch.tensor(wl.rope_base, dtype=torch.float32, device=dev)
     tdt = q.dtype
     qh, kh = torch.empty_like(q), torch.empty_like(k)
+    knm = torch.empty(wl.hkv, dtype=torch.float32, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -69,11 +70,11 @@ def run_gpu(wl, steps, warmup, seed=0):
         plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, tdt, dev)
         # the softmax scale (times log2 e) is folded into K by the prologue
         ops.qknorm_rope(q, k, gq, gk, pq, pk, base, wl.eps, q_out=qh, k_out=kh,
-                        k_scale=wl.softmax_scale * ops.LOG2E)
+                        k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm)
         if record:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-        ops.ffa_fwd(qh, kh, v, plan, out=out, lse=lse, softmax_scale=ops.LN2)
+        ops.ffa_fwd(qh, kh, v, plan, out=out, lse=lse, softmax_scale=ops.LN2, k_norm_max=knm)
         if record:
             b.record(stream)
             ev.append((a, b))

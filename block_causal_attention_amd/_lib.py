@@ -69,9 +69,9 @@ def lib() -> C.CDLL:
                                     C.POINTER(WorkItem), i32, C.POINTER(i32), C.POINTER(i32), i32,
                                     C.POINTER(i32)]
         L.magi_qknorm_rope.argtypes = [vp, vp, i64, i32, i64, vp, vp, i64, i32, i64, i32, i32,
-                                       vp, vp, i32, C.c_float, vp, vp, vp, C.c_float, C.c_float, vp]
+                                       vp, vp, i32, C.c_float, vp, vp, vp, C.c_float, C.c_float, vp, vp]
         L.magi_ffa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i64, i64, i64,
-                                   C.c_float, vp, i32, vp, i32, vp, i32, vp]
+                                   C.c_float, vp, vp, i32, vp, i32, vp, i32, vp]
         for name in ("magi_slices_build", "magi_default_tile_q", "magi_schedule", "magi_qknorm_rope",
                      "magi_ffa_fwd"):
             getattr(L, name).restype = i32

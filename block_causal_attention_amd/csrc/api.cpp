@@ -45,7 +45,7 @@ extern "C" int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, i
                                     int32_t head_dim, int32_t dtype, const float* gain_q, const float* gain_k,
                                     int32_t gain_head_stride, float eps, const int32_t* pos_q,
                                     const int32_t* pos_k, const float* rope_base, float q_scale, float k_scale,
-                                    void* stream) {
+                                    float* k_norm_max, void* stream) {
   int32_t st;
   if ((st = check_common(head_dim, dtype)) != MAGI_OK) return st;
   if ((st = check_tensor("q_in", q_in, nq, hq, q_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
@@ -73,6 +73,11 @@ extern "C" int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, i
   a.gain_head_stride = gain_head_stride;
   a.eps = eps;
   a.rope_base = rope_base;
+  if (k_norm_max != nullptr && nk == 0)
+    return fail(MAGI_ERR_INVALID_ARG, "k_norm_max needs K (nk > 0)");
+  if (k_norm_max != nullptr && (reinterpret_cast<uintptr_t>(k_norm_max) & 3u))
+    return fail(MAGI_ERR_INVALID_ARG, "k_norm_max is not 4-byte aligned");
+  a.k_norm_max = k_norm_max;
   const hipError_t e = launch_qknorm_rope(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MAGI_ERR_HIP, "qknorm_rope launch: %s", hipGetErrorString(e));
   return ok();
@@ -81,7 +86,8 @@ extern "C" int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, i
 extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t nq,
                                 int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
                                 int64_t q_tok_stride, int64_t kv_tok_stride, int64_t o_tok_stride,
-                                float softmax_scale, const magi_attn_slice* slices, int32_t num_slices,
+                                float softmax_scale, const float* k_norm_max, const magi_attn_slice* slices,
+                                int32_t num_slices,
                                 const magi_work_item* work, int32_t num_work, const int32_t* tile_slices,
                                 int32_t num_tile_slices, void* stream) {
   int32_t st;
@@ -97,6 +103,8 @@ extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, voi
     return fail(MAGI_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
     return fail(MAGI_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (k_norm_max != nullptr && (reinterpret_cast<uintptr_t>(k_norm_max) & 3u))
+    return fail(MAGI_ERR_INVALID_ARG, "k_norm_max is not 4-byte aligned");
   if (num_slices < 0 || num_work < 0 || num_tile_slices < 0)
     return fail(MAGI_ERR_INVALID_ARG, "negative list length");
   if ((num_slices > 0 && slices == nullptr) || (num_work > 0 && work == nullptr) ||
@@ -120,6 +128,7 @@ extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, voi
   a.kv_stride = kv_tok_stride;
   a.o_stride = o_tok_stride;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  a.k_norm_max = dtype == MAGI_DTYPE_BF16 ? k_norm_max : nullptr;
   a.slices = slices;
   a.num_slices = num_slices;
   a.work = work;

@@ -53,6 +53,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1e30f;  // finite "minus infinity" for the running max
 constexpr int kBufCfg = 0x00020000;  // raw buffer resource word 3 (gfx9 family: 32-bit data format)
 constexpr float kShift = 8.0f;
+constexpr float kBoundMargin = 1.0f + 1.0f / 128.0f;  // covers bf16 rounding of k and fp32 sums
+constexpr float kBoundMax = 60.0f;                    // log2 units, see the bounded reference
 #ifndef MAGI_VROW_MODE
 #define MAGI_VROW_MODE 0
 #endif
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
   }
 
   // this lane's two query rows (one per 32-row column block) as MFMA B operands
-  int64_t qi[NB];
+  int32_t qi[NB];  // query token of the row (< nq < 2^31)
   int hg[NB];
   bool rvalid[NB];
   bf16x8 qreg[NB][C::KS];
@@ -220,35 +222,75 @@ __global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
     const int t = n / G;
     hg[nb] = n % G;
     rvalid[nb] = (t < qlen);
-    qi[nb] = (int64_t)wi.q_start + (rvalid[nb] ? t : 0);
+    qi[nb] = wi.q_start + (rvalid[nb] ? t : 0);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       const int d0 = 16 * ks + 8 * h;
       bf16x8 x = {};
       if (rvalid[nb] && d0 < D)
-        x = *reinterpret_cast<const bf16x8*>(qp + qi[nb] * a.q_stride + (int64_t)(g * G + hg[nb]) * D + d0);
+        x = *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi[nb] * a.q_stride + (int64_t)(g * G + hg[nb]) * D + d0);
       qreg[nb][ks] = x;
     }
   }
 
-  // Softmax state per row: the reference m (log2 units) is subtracted inside
-  // the score MFMA (Q padding slot or accumulator start, see AUG).  m moves
-  // only when a row sees its first key or when a score exceeds m by more
-  // than kShift, so the common tile needs no rescale (P <= 2^kShift stays
-  // finite).  With AUG, m is kept exactly representable in bf16.
+  // Softmax state per row: the reference m (log2 units).  With AUG it is
+  // subtracted inside the score MFMA (Q padding slot) and kept exactly
+  // representable in bf16; otherwise it is subtracted in the exponent.  m
+  // moves only when a row sees its first key or when a score exceeds m by
+  // more than kShift, so the common tile needs no rescale (P <= 2^kShift
+  // stays finite).
   const float c = a.scale * kLog2e;
   const float cinv = PRESCALED ? 1.0f : 1.0f / c;
   float m[NB];
   bool init[NB];
-  f32x16 cinit[NB];
   f32x16 o[NB][C::MB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     m[nb] = 0.f;
     init[nb] = false;
-    cinit[nb] = (f32x16){};
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) o[nb][mb] = (f32x16){};
+  }
+  // Bounded reference.  When the caller supplies B >= |k| for every key of
+  // the group, q.k <= |q| B (Cauchy-Schwarz) bounds every score of a row, so
+  // |q| B can be the row's softmax reference from the start: no running
+  // max, no rescaling.  A wave uses it when every row's bound keeps the
+  // smallest possible score, -|q| B, within 2^-120 of it (bound <= 60 in
+  // log2 units: no underflow to zero or denormals); otherwise it keeps the
+  // online max.
+  bool bounded = false;
+  if (a.k_norm_max != nullptr) {
+    const float B = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(a.k_norm_max[g])));
+    bool ok = B > 0.f;  // also false for NaN
+    float mb_row[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = (float)qreg[nb][ks][e];
+          ss = fmaf(x, x, ss);
+        }
+      ss += pair_other(ss, h);
+      mb_row[nb] = sqrtf(ss) * B * (PRESCALED ? 1.0f : c) * kBoundMargin;
+      ok = ok && mb_row[nb] <= kBoundMax;
+    }
+    bounded = __all(ok);
+    if (bounded) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        init[nb] = true;
+        if constexpr (AUG) {
+          const __bf16 slot = bf16_floor(-mb_row[nb] * cinv);
+          m[nb] = PRESCALED ? -(float)slot : -(float)slot * c;
+          qreg[nb][C::KS - 1][0] = h ? slot : qreg[nb][C::KS - 1][0];
+        } else {
+          m[nb] = mb_row[nb];
+        }
+      }
+    }
   }
 
   const int64_t first_tok = wi.q_start, last_tok = (int64_t)wi.q_start + qlen - 1;
@@ -320,7 +362,7 @@ __global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
     for (int nb = 0; nb < NB; ++nb) {
       int64_t re = cg.ke;
       if (cg.causal) {
-        const int64_t ce = cg.koff + qi[nb] + 1;
+        const int64_t ce = (int64_t)cg.koff + qi[nb] + 1;
         re = ce < re ? ce : re;
       }
       if (!rvalid[nb]) re = kt;
@@ -332,7 +374,8 @@ __global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
 
 #pragma unroll
     for (int kb0 = 0; kb0 < 2; kb0 += KG) {
-      // S'^T = K . Q^T - m for KG*32 keys x 64 rows; a lane holds 16 keys of one row per block
+      // S^T = K . Q^T (minus m with AUG) for KG*32 keys x 32 NB rows; a lane
+      // holds 16 keys of one row per block
       f32x16 s[KG][NB];
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
@@ -343,8 +386,7 @@ __global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
           kop[ks2] = *reinterpret_cast<const bf16x8*>(&Kb[(kb * 32 + ln) * C::KROW + 16 * ks2 + 8 * h]);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qreg[nb][0], AUG ? (f32x16){} : cinit[nb],
-                                                               0, 0, 0);
+          f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qreg[nb][0], (f32x16){}, 0, 0, 0);
 #pragma unroll
           for (int ks2 = 1; ks2 < C::KS; ++ks2)
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks2], qreg[nb][ks2], acc, 0, 0, 0);
@@ -360,9 +402,11 @@ __global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
             for (int i = 0; i < 16; ++i)
               if ((kb0 + kg) * 32 + key_of(i) >= lim[nb]) s[kg][nb][i] = -INFINITY;
       }
-      // row maxima of the shifted scores; move m only where needed
+      // row maxima of the shifted scores; move m only where needed (the
+      // bounded reference never moves)
       bool sh[NB];
       float delta[NB];
+      if (!bounded) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         float mx = s[0][nb][0];
@@ -371,7 +415,7 @@ __global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kg][nb][i]);
         mx = pair_max(mx);
-        const float xm = PRESCALED ? mx : mx * c;
+        const float xm = (PRESCALED ? mx : mx * c) - (AUG ? 0.f : m[nb]);
         sh[nb] = (!init[nb] && xm > -INFINITY) || xm > kShift;
         delta[nb] = sh[nb] ? xm : 0.f;
         init[nb] = init[nb] || xm > -INFINITY;
@@ -396,19 +440,16 @@ __global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
           const float alpha = __builtin_amdgcn_exp2f(-step);
 #pragma unroll
           for (int mb = 0; mb < C::MB; ++mb) o[nb][mb] *= alpha;
-          const float dsub = step * cinv;
-#pragma unroll
-          for (int kg = 0; kg < KG; ++kg)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[kg][nb][i] -= dsub;
           if constexpr (AUG) {
-            qreg[nb][C::KS - 1][0] = h ? slot : qreg[nb][C::KS - 1][0];
-          } else {
-            const float ci0 = -mnew * cinv;
+            const float dsub = step * cinv;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) cinit[nb][i] = ci0;
+            for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) s[kg][nb][i] -= dsub;
+            qreg[nb][C::KS - 1][0] = h ? slot : qreg[nb][C::KS - 1][0];
           }
         }
+      }
       }
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
@@ -421,7 +462,12 @@ __global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
           for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const float x = PRESCALED ? s[kg][nb][8 * i2 + e] : s[kg][nb][8 * i2 + e] * c;
+              const float sv = s[kg][nb][8 * i2 + e];
+              float x;
+              if constexpr (AUG)
+                x = PRESCALED ? sv : sv * c;
+              else
+                x = PRESCALED ? sv - m[nb] : fmaf(sv, c, -m[nb]);
               pb[i2][nb][e] = (__bf16)__builtin_amdgcn_exp2f(x);
             }
         // O^T += V^T . P^T ; the V^T operand comes from the row-major V tile
@@ -461,7 +507,7 @@ __global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
     const float l = h == 0 ? mine : other;
     if (!rvalid[nb]) continue;
     const float inv = l > 0.f ? 1.0f / l : 0.f;
-    const int64_t obase = qi[nb] * a.o_stride + (int64_t)(g * G + hg[nb]) * D;
+    const int64_t obase = (int64_t)qi[nb] * a.o_stride + (int64_t)(g * G + hg[nb]) * D;
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
@@ -476,7 +522,7 @@ __global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
         }
       }
     if (a.lse != nullptr && h == 0)
-      a.lse[qi[nb] * a.hq + g * G + hg[nb]] = l > 0.f ? (m[nb] + __log2f(l)) * kLn2 : -INFINITY;
+      a.lse[(int64_t)qi[nb] * a.hq + g * G + hg[nb]] = l > 0.f ? (m[nb] + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
 // fp32 path (small shapes): one thread per query row, keys streamed from

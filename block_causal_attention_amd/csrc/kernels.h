@@ -22,6 +22,7 @@ struct QkSide {
 
 struct QkArgs {
   QkSide side[2];  // Q, then K (side[1].n == 0 to skip)
+  float* k_norm_max;  // device [hkv] out: bound on the norm of every output key of a group, or nullptr
   int32_t head_dim;
   int32_t dtype;
   int32_t gain_head_stride;
@@ -41,6 +42,7 @@ struct FfaArgs {
   int32_t hq, hkv, head_dim, dtype;
   int64_t q_stride, kv_stride, o_stride;
   float scale;
+  const float* k_norm_max;  // device [hkv] upper bounds on key norms, or nullptr
   const magi_attn_slice* slices;
   int32_t num_slices;
   const magi_work_item* work;

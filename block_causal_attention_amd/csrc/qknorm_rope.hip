@@ -55,6 +55,19 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(QkArgs a, int blo
   if (tok0 >= s.n) return;
   const int ntok = (int)min<int64_t>(tpb, s.n - tok0);
 
+  // first K block: bound on the norm of every output key of each head.
+  // |x / rms(x) * g| <= sqrt(D) max|g| (the RMS step leaves norm sqrt(D)
+  // at most, the rotation keeps norms), times |k_scale|, plus a margin for
+  // the bf16 rounding of the stored keys.
+  if (sidx == 1 && b == 0 && a.k_norm_max != nullptr) {
+    for (int hh = threadIdx.x; hh < s.heads; hh += kThreads) {
+      const float* gg = s.gain + (int64_t)hh * a.gain_head_stride;
+      float gmax = 0.f;
+      for (int i = 0; i < D; ++i) gmax = fmaxf(gmax, fabsf(gg[i]));
+      a.k_norm_max[hh] = sqrtf((float)D) * gmax * fabsf(s.out_scale) * (1.0f + 1.0f / 128.0f);
+    }
+  }
+
   extern __shared__ float2 table[];  // [tpb][P] (cos, sin)
 
   for (int i = threadIdx.x; i < ntok * P; i += kThreads) {

@@ -136,9 +136,11 @@ def _check_3d(name, t, heads, d):
 def qknorm_rope(q: torch.Tensor, k: Optional[torch.Tensor], gain_q: torch.Tensor,
                 gain_k: Optional[torch.Tensor], pos_q: torch.Tensor, pos_k: Optional[torch.Tensor],
                 rope_base: torch.Tensor, eps: float = 1e-6, q_out: Optional[torch.Tensor] = None,
-                k_out: Optional[torch.Tensor] = None, q_scale: float = 1.0, k_scale: float = 1.0):
+                k_out: Optional[torch.Tensor] = None, q_scale: float = 1.0, k_scale: float = 1.0,
+                k_norm_max: Optional[torch.Tensor] = None):
     """magi_qknorm_rope: QK-Norm then 3D RoPE (results times q_scale / k_scale);
-    returns (q_out, k_out)."""
+    returns (q_out, k_out).  ``k_norm_max`` (float32 [hkv], optional) receives
+    an upper bound on the norm of every output key of each head."""
     d = q.shape[-1]
     _check_3d("q", q, q.shape[1], d)
     q_out = torch.empty_like(q) if q_out is None else q_out
@@ -146,6 +148,8 @@ def qknorm_rope(q: torch.Tensor, k: Optional[torch.Tensor], gain_q: torch.Tensor
     if q_out.stride(0) != q.stride(0):
         raise ValueError("q and q_out must share the row stride")
     ghs = 0 if gain_q.dim() == 1 else d
+    if gain_k is not None and gain_k.dim() != gain_q.dim():
+        raise ValueError("gain_q and gain_k must both be shared [d] or both per head [heads, d]")
     nk, hkv, ks = 0, 1, q.shape[1] * d
     if k is not None:
         _check_3d("k", k, k.shape[1], d)
@@ -153,6 +157,8 @@ def qknorm_rope(q: torch.Tensor, k: Optional[torch.Tensor], gain_q: torch.Tensor
         if k_out.stride(0) != k.stride(0):
             raise ValueError("k and k_out must share the row stride")
         nk, hkv, ks = k.shape[0], k.shape[1], k.stride(0)
+    if k_norm_max is not None and (k_norm_max.dtype != torch.float32 or k_norm_max.numel() < hkv):
+        raise ValueError("k_norm_max must be float32 with one entry per K head")
     for t in (gain_q, gain_k, rope_base):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError("gains and rope_base must be contiguous float32")
@@ -163,14 +169,17 @@ def qknorm_rope(q: torch.Tensor, k: Optional[torch.Tensor], gain_q: torch.Tensor
         _ptr(q), _ptr(q_out), q.shape[0], q.shape[1], q.stride(0),
         _ptr(k), _ptr(k_out), nk, hkv, ks, d, dtype_code(q.dtype),
         _ptr(gain_q), _ptr(gain_k), ghs, float(eps), _ptr(pos_q), _ptr(pos_k), _ptr(rope_base),
-        float(q_scale), float(k_scale), _stream(q)))
+        float(q_scale), float(k_scale), _ptr(k_norm_max), _stream(q)))
     return q_out, k_out
 
 
 def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
             softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-            lse: Optional[torch.Tensor] = None, return_lse: bool = True):
-    """magi_ffa_fwd over ``plan``; returns (out [nq, hq, d], lse [nq, hq] fp32 or None)."""
+            lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+            k_norm_max: Optional[torch.Tensor] = None):
+    """magi_ffa_fwd over ``plan``; returns (out [nq, hq, d], lse [nq, hq] fp32 or None).
+    ``k_norm_max`` (float32 [hkv], optional) must bound the norm of every key
+    row of each group (qknorm_rope writes one)."""
     d = q.shape[-1]
     hq, hkv = q.shape[1], k.shape[1]
     _check_3d("q", q, hq, d)
@@ -188,7 +197,7 @@ def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
     check(lib().magi_ffa_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q.shape[0], k.shape[0], hq, hkv, d,
         dtype_code(q.dtype), q.stride(0), k.stride(0), out.stride(0),
-        0.0 if softmax_scale is None else float(softmax_scale),
+        0.0 if softmax_scale is None else float(softmax_scale), _ptr(k_norm_max),
         _ptr(plan.slices), int(plan.host["slices"].shape[0]), _ptr(plan.work), plan.num_work,
         _ptr(plan.tile_slices), int(plan.host["tile_slices"].shape[0]), _stream(q)))
     return out, lse

@@ -161,13 +161,19 @@ int32_t magi_schedule(const magi_attn_slice* slices, int32_t num_slices,
  * pos_q, pos_k  [device] int32 [n][3] latent (t, h, w) coordinates
  * rope_base     [device] fp32 [3] base frequency of the t, h, w axes (> 0)
  * q_scale, k_scale  output factors (finite, non-zero; 1 = plain QK-Norm + RoPE)
+ * k_norm_max    [device] fp32 [hkv] out, or NULL: an upper bound on the L2
+ *               norm of every stored K row of each head, sqrt(head_dim) *
+ *               max|gain_k| * |k_scale| * (1 + 2^-7) (the RMS step leaves
+ *               norm <= sqrt(head_dim), the rotation keeps norms; the margin
+ *               covers bf16 rounding).  Pass it to magi_ffa_fwd.
  */
 int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, int32_t hq, int64_t q_tok_stride,
                          const void* k_in, void* k_out, int64_t nk, int32_t hkv, int64_t k_tok_stride,
                          int32_t head_dim, int32_t dtype,
                          const float* gain_q, const float* gain_k, int32_t gain_head_stride,
                          float eps, const int32_t* pos_q, const int32_t* pos_k,
-                         const float* rope_base, float q_scale, float k_scale, void* stream);
+                         const float* rope_base, float q_scale, float k_scale,
+                         float* k_norm_max, void* stream);
 
 /*
  * magi_ffa_fwd -- Flex-Flash-Attention forward over a work list.   [device]
@@ -188,6 +194,13 @@ int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, int32_t hq, 
  *              All tensor pointers 16-byte aligned, strides multiples of 8.
  * softmax_scale  <= 0 selects 1/sqrt(head_dim); ln(2) means the scores are
  *              already in log2 units (softmax scale folded into Q or K)
+ * k_norm_max   [device] fp32 [hkv] or NULL: an upper bound on the L2 norm of
+ *              every K row of each group (as written by magi_qknorm_rope).
+ *              With it, each row's softmax reference is |q| * bound
+ *              (Cauchy-Schwarz) instead of a running max, which saves the max
+ *              and rescaling work; rows whose bound exceeds 60 in log2 units
+ *              keep the running max.  A value below the true norms gives wrong
+ *              results (possibly inf).  Ignored for fp32.
  * slices, work, tile_slices  [device] copies of magi_schedule's outputs made for
  *              the same nq, nk, hq, hkv, head_dim, dtype (items are clamped to
  *              the tensor bounds on the device, so a mismatched list cannot
@@ -197,7 +210,7 @@ int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, int32_t hq, 
 int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                      int64_t nq, int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
                      int64_t q_tok_stride, int64_t kv_tok_stride, int64_t o_tok_stride,
-                     float softmax_scale,
+                     float softmax_scale, const float* k_norm_max,
                      const magi_attn_slice* slices, int32_t num_slices,
                      const magi_work_item* work, int32_t num_work,
                      const int32_t* tile_slices, int32_t num_tile_slices,

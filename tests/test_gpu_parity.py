@@ -55,10 +55,11 @@ def dev_inputs(wl, inp):
 def gpu_forward(wl, d):
     """prologue (Q and K, softmax scale folded into K) then FFA over the
     builder's slices, exactly as the benchmark runs it."""
+    knm = torch.empty(wl.hkv, dtype=torch.float32, device=DEV)
     qh, kh = ops.qknorm_rope(d["q"], d["k"], d["gq"], d["gk"], d["pq"], d["pk"], d["base"], wl.eps,
-                             k_scale=wl.softmax_scale * ops.LOG2E)
+                             k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm)
     plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, d["q"].dtype)
-    O, L = ops.ffa_fwd(qh, kh, d["v"], plan, softmax_scale=ops.LN2)
+    O, L = ops.ffa_fwd(qh, kh, d["v"], plan, softmax_scale=ops.LN2, k_norm_max=knm)
     torch.cuda.synchronize()
     return qh, kh, O, L
 
@@ -100,6 +101,26 @@ def test_prologue_output_scale():
     compare(np64(kh), wk, "bf16", "k_hat")
 
 
+def test_prologue_key_norm_bound():
+    note("prologue key-norm bound")
+    wl = W.custom_block_causal(2, 2, 4, 5, 16, 4, 48)
+    inp = W.make_inputs(wl, 6)
+    d = dev_inputs(wl, inp)
+    rng = np.random.Generator(np.random.PCG64(6))
+    # per-head gains (the gain stride is shared by Q and K)
+    gq = torch.from_numpy(rng.uniform(0.5, 1.5, (16, 48)).astype(np.float32)).to(DEV)
+    gk = torch.from_numpy(rng.uniform(0.5, 1.5, (4, 48)).astype(np.float32)).to(DEV)
+    knm = torch.full((4,), float("nan"), dtype=torch.float32, device=DEV)
+    _, kh = ops.qknorm_rope(d["q"], d["k"], gq, gk, d["pq"], d["pk"], d["base"], wl.eps,
+                            k_scale=0.3, k_norm_max=knm)
+    torch.cuda.synchronize()
+    norms = kh.float().norm(dim=-1).amax(dim=0).cpu().numpy()
+    bound = knm.cpu().numpy()
+    want = 48 ** 0.5 * gk.abs().amax(dim=1).cpu().numpy() * 0.3 * (1 + 2 ** -7)
+    np.testing.assert_allclose(bound, want, rtol=1e-6)
+    assert (norms <= bound).all() and (norms > 0.5 * bound).all()
+
+
 def test_prologue_per_head_gain_in_place_and_strided():
     note("prologue per-head gains, in place, strided view")
     wl = W.custom_block_causal(2, 2, 3, 4, 16, 2, 48)
@@ -121,7 +142,7 @@ def test_prologue_per_head_gain_in_place_and_strided():
 
 # --------------------------------------------------------------------------- attention alone
 
-def ffa_case(q, k, v, slices, kind, scale=None, check_lse=True):
+def ffa_case(q, k, v, slices, kind, scale=None, check_lse=True, knm=None):
     nq, hq, dd = q.shape
     nk, hkv = k.shape[0], k.shape[1]
     tdt = torch.bfloat16 if kind == "bf16" else torch.float32
@@ -129,7 +150,8 @@ def ffa_case(q, k, v, slices, kind, scale=None, check_lse=True):
     plan = ops.make_plan(np.asarray(slices, np.int32).reshape(-1, 5), nq, nk, hq, hkv, dd, tdt)
     out = torch.full_like(qd, float("nan"))
     lse = torch.full((nq, hq), float("nan"), dtype=torch.float32, device=DEV)
-    O, L = ops.ffa_fwd(qd, kd, vd, plan, softmax_scale=scale, out=out, lse=lse)
+    kn = None if knm is None else torch.tensor(knm, dtype=torch.float32, device=DEV)
+    O, L = ops.ffa_fwd(qd, kd, vd, plan, softmax_scale=scale, out=out, lse=lse, k_norm_max=kn)
     torch.cuda.synchronize()
     mask = oracle.slices_mask([tuple(int(x) for x in s) for s in slices], nq, nk) if len(slices) else \
         np.zeros((nq, nk), bool)
@@ -183,6 +205,22 @@ def test_ffa_prescaled_keys(d):
     k = torch.from_numpy(rand((300, 2, d), 21) * c).to(torch.bfloat16).float().numpy()
     seqs = [W.SeqDesc(100, 3, 3, 0, 0, (-1, -1, 1), 1, 1, 100)]
     ffa_case(rand((300, 32, d), 20), k, rand((300, 2, d), 22), ops.build_slices(seqs), "bf16", scale=ops.LN2)
+
+
+@pytest.mark.parametrize("d", [24, 48])
+@pytest.mark.parametrize("loose", [False, True])
+def test_ffa_key_norm_bound(d, loose):
+    # the bounded reference (no running max) must give the online-max result;
+    # a bound too loose to use (> 60 in log2 units) falls back to the running max
+    note(f"ffa key-norm bound d={d} loose={loose}")
+    hkv = 2
+    q, k, v = rand((150, 32, d), 30 + d), rand((150, hkv, d), 31), rand((150, hkv, d), 32)
+    kb = torch.from_numpy(k).to(torch.bfloat16).float().norm(dim=-1).amax(dim=0).numpy() * 1.001
+    if loose:
+        kb = kb * 40.0
+    seqs = [W.SeqDesc(50, 3, 3, 0, 0, (-1, -1, 1), 1, 1, 50)]
+    ffa_case(q, k, v, ops.build_slices(seqs), "bf16", knm=kb)
+    ffa_case(q, k, v, np.array([(0, 150, 0, 150, 1)]), "bf16", knm=kb)
 
 
 def test_ffa_fp32_tiny_full():

@@ -252,33 +252,35 @@ def test_device_entry_points_validate_before_any_hip_call():
     f = C.c_void_p(4096)
     # magi_qknorm_rope
     assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 32, 0, f, None, 0, 1e-6, p, None, f,
-                              1.0, 1.0, None) == _lib.MAGI_ERR_UNSUPPORTED
+                              1.0, 1.0, None, None) == _lib.MAGI_ERR_UNSUPPORTED
     assert L.magi_qknorm_rope(p, p, 10, 8, 100, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, f,
-                              1.0, 1.0, None) == _lib.MAGI_ERR_INVALID_ARG   # stride < heads*d
+                              1.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # stride < heads*d
     assert L.magi_qknorm_rope(C.c_void_p(4098), p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6,
-                              p, None, f, 1.0, 1.0, None) == _lib.MAGI_ERR_INVALID_ARG   # misaligned
+                              p, None, f, 1.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # misaligned
     assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, -1.0, p, None, f,
-                              1.0, 1.0, None) == _lib.MAGI_ERR_INVALID_ARG   # eps < 0
+                              1.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # eps < 0
     assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 7, 1e-6, p, None, f,
-                              1.0, 1.0, None) == _lib.MAGI_ERR_INVALID_ARG   # gain stride
+                              1.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # gain stride
     assert L.magi_qknorm_rope(p, p, 10, 8, 192, p, p, 5, 2, 48, 24, 0, f, None, 0, 1e-6, p, p, f,
-                              1.0, 1.0, None) == _lib.MAGI_ERR_INVALID_ARG   # gain_k NULL
+                              1.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # gain_k NULL
     assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, None,
-                              1.0, 1.0, None) == _lib.MAGI_ERR_INVALID_ARG   # rope_base NULL
+                              1.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # rope_base NULL
     assert L.magi_qknorm_rope(None, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, f,
-                              1.0, 1.0, None) == _lib.MAGI_ERR_INVALID_ARG   # q NULL
+                              1.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # q NULL
     assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, f,
-                              0.0, 1.0, None) == _lib.MAGI_ERR_INVALID_ARG   # zero scale
+                              0.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # zero scale
     assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, f,
-                              1.0, float("inf"), None) == _lib.MAGI_ERR_INVALID_ARG   # inf scale
+                              1.0, 1.0, f, None) == _lib.MAGI_ERR_INVALID_ARG   # k_norm_max without K
+    assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, f,
+                              1.0, float("inf"), None, None) == _lib.MAGI_ERR_INVALID_ARG   # inf scale
     # magi_ffa_fwd
     def ffa(**kw):
         a = dict(q=p, k=p, v=p, out=p, lse=None, nq=16, nk=16, hq=16, hkv=1, d=24, dt=0, qs=384, kvs=24, os_=384,
-                 scale=0.0, sl=p, ns=1, w=p, nw=1, ts=p, nts=1)
+                 scale=0.0, knm=None, sl=p, ns=1, w=p, nw=1, ts=p, nts=1)
         a.update(kw)
         return L.magi_ffa_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["nq"], a["nk"], a["hq"], a["hkv"],
-                              a["d"], a["dt"], a["qs"], a["kvs"], a["os_"], a["scale"], a["sl"], a["ns"], a["w"],
-                              a["nw"], a["ts"], a["nts"], None)
+                              a["d"], a["dt"], a["qs"], a["kvs"], a["os_"], a["scale"], a["knm"], a["sl"], a["ns"],
+                              a["w"], a["nw"], a["ts"], a["nts"], None)
     assert ffa(d=64) == _lib.MAGI_ERR_UNSUPPORTED
     assert ffa(dt=3) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(hq=12, hkv=8) == _lib.MAGI_ERR_INVALID_ARG
@@ -289,6 +291,7 @@ def test_device_entry_points_validate_before_any_hip_call():
     assert ffa(out=C.c_void_p(4100)) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(lse=C.c_void_p(4098)) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(scale=float("nan")) == _lib.MAGI_ERR_INVALID_ARG
+    assert ffa(knm=C.c_void_p(4098)) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(w=None) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(nw=-1) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(nq=-2) == _lib.MAGI_ERR_INVALID_ARG
