@@ -131,6 +131,9 @@ def main():
     ap.add_argument("--workload", default="magi4.5b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (a known-size "
+                         "reference for calibrating the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the attention path has no "
@@ -140,6 +143,14 @@ def main():
     import torch
     import workloads as W
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 4, "launches": 5}), flush=True)
+        return
 
     wl = W.make_workload(args.workload)
     flops = masked_flops(wl)
