@@ -92,6 +92,21 @@ def run_gpu(wl, steps, warmup, seed=0):
     return (t1 - t0) * 1e3 / steps, float(np.mean(kernel_ms)), plan.num_work
 
 
+def committed_traffic(wl_name: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary (profiles/traffic_<workload>.json), or None when the kernel
+    source changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl_name}.json")
+    src = os.path.join(ROOT, "block_causal_attention_amd", "csrc", "ffa_fwd.hip")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("ffa_fwd_hip_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(wl, target_s=15.0, seed=0):
     """Time the float64 oracle on a seeded row sample (all heads) of the workload."""
     import oracle
@@ -174,7 +189,8 @@ def main():
                    "masked_flops_per_step": flops, "work_items": nwork, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": committed_traffic(wl.name),
                      "kernel": "ffa_fwd_bf16", "avg_launch_ms": round(ms_kernel, 5)},
     }
     if not args.no_secondary and wl.name == "magi4.5b":
