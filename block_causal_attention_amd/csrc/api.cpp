@@ -99,6 +99,9 @@ extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, voi
   if ((st = check_tensor("out", out, nq, hq, o_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
   if ((st = check_tensor("k", k, nk, hkv, kv_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
   if ((st = check_tensor("v", v, nk, hkv, kv_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
+  // the kernel addresses one K/V tile with 32-bit byte offsets
+  if (kv_tok_stride >= (int64_t)1 << 23)
+    return fail(MAGI_ERR_UNSUPPORTED, "kv row stride %lld >= 2^23 elements", (long long)kv_tok_stride);
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(MAGI_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   if (std::isnan(softmax_scale) || std::isinf(softmax_scale))

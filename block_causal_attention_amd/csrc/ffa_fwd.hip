@@ -9,9 +9,10 @@
 // CDNA4 and needs no atomics because every work item owns its output rows.
 //
 // bf16 kernel layout (one workgroup = one work item = up to 256 query rows):
-//  * GQA packing: the 16 query heads of a KV group share K and V, so a query
-//    "row" is a (token, head) pair and the item's rows are tile_q tokens x 16
-//    heads.  Each of the 4 waves owns 64 rows as two 32-row MFMA column blocks.
+//  * GQA packing: the query heads of a KV group share K and V, so a query
+//    "row" is a (token, head) pair and the item's rows are tile_q tokens x G
+//    heads.  Each wave owns NB 32-row MFMA column blocks (NB = 2 for head_dim
+//    24: 4 waves; NB = 1 for 48: 8 waves).
 //  * Scores are computed transposed, S^T = K . Q^T, with
 //    v_mfma_f32_32x32x16_bf16: keys run along the MFMA M axis and rows along
 //    N, so every lane holds 16 scores of one row.  The row max needs only
@@ -26,12 +27,15 @@
 //    48 -> 64).  The first padding column of V holds 1.0, so the same MFMA
 //    that accumulates P.V also accumulates the softmax denominator sum(P)
 //    (of the bf16-rounded P actually used), at no VALU cost.
-//  * K/V tiles of 64 keys are staged in LDS once and read by all 4 waves
-//    (64 query heads x tokens).  Tiles wholly outside the visible range are
-//    never visited; only tiles crossing a range end or a causal diagonal pay
-//    for element masking.
-//  * Online softmax in fp32 in the log2 domain (scale * log2(e) folded into
-//    one multiply), exp via v_exp_f32.
+//  * K/V tiles of 64 keys are staged in LDS once and read by every wave of
+//    the item.  Three LDS buffers rotate: one tile is computed while the next
+//    sits in LDS and the one after is in flight from HBM; the K operand of
+//    each 32-key block is read one block ahead.  Tiles wholly outside the
+//    visible range are never visited; only tiles crossing a range end or a
+//    causal diagonal pay for element masking.
+//  * Softmax in fp32 in the log2 domain against a fixed per-row reference
+//    (a bound from the key norms when the caller supplies one, else an
+//    online max that moves only by large steps), exp via v_exp_f32.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -45,25 +49,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kThreads = 256;
-constexpr int kRows = 256;  // query rows per work item
-constexpr int TK = 64;      // keys per LDS tile
+constexpr int kRows = 256;        // query rows per work item
+constexpr int kThreads = kRows;   // fp32 kernel: one thread per row
+constexpr int TK = 64;  // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1e30f;  // finite "minus infinity" for the running max
 constexpr int kBufCfg = 0x00020000;  // raw buffer resource word 3 (gfx9 family: 32-bit data format)
-constexpr float kShift = 8.0f;
+constexpr float kShift = 8.0f;  // move the softmax reference when a score exceeds it by 2^8
 constexpr float kBoundMargin = 1.0f + 1.0f / 128.0f;  // covers bf16 rounding of k and fp32 sums
 constexpr float kBoundMax = 60.0f;                    // log2 units, see the bounded reference
-#ifndef MAGI_VROW_MODE
-#define MAGI_VROW_MODE 0
-#endif
-#ifndef MAGI_NB24
-#define MAGI_NB24 1
-#endif
-#ifndef MAGI_NB48
-#define MAGI_NB48 1
-#endif     // move the softmax reference when a score exceeds it by 2^8
 
 template <int D>
 struct Cfg {
@@ -75,7 +70,7 @@ struct Cfg {
   // LDS pitch of a V row (elements): ds_read_b64_tr_b16 has each group of
   // 16 lanes read 4 consecutive rows x 32 bytes, so the pitch is chosen to
   // put 4 consecutive rows in disjoint bank ranges
-  static constexpr int VROW = MAGI_VROW_MODE == 0 ? (DV == 32 ? 32 : DV + 32) : DV + 8;
+  static constexpr int VROW = DV == 32 ? 32 : DV + 32;
   static constexpr int CH = D / 8;                    // 16-byte chunks per K/V row
   // position of the denominator (the ones column, V column D) in the O^T
   // accumulator of lane half 0: block D/32, index 4*((D%32)/8) + D%4
@@ -91,18 +86,27 @@ __device__ inline int64_t causal_end(const magi_attn_slice& s, int64_t ke, int64
 }
 
 // One slice as seen by one work item.  Every field is the same for the whole
-// workgroup and lives in scalar registers.
+// workgroup and lives in scalar registers.  Token and key indices fit in 32
+// bits (the entry point rejects nq or nk >= 2^31), so all of it is 32-bit
+// scalar arithmetic.
 struct SliceGeo {
-  int64_t ks;     // first key
-  int64_t khi;    // one past the last key that any row of the item sees
-  int64_t kfull;  // keys below this are visible to every row of the item
-  int64_t ke;     // slice key end, clamped to nk
-  int64_t koff;   // k_end - q_end: a causal row r sees keys below koff + r + 1
+  int32_t ks;     // first key
+  int32_t khi;    // one past the last key that any row of the item sees
+  int32_t kfull;  // keys below this are visible to every row of the item
+  int32_t ke;     // slice key end, clamped to nk
+  int32_t koff;   // k_end - q_end: a causal row r sees keys below koff + r + 1
   int32_t causal;
   int32_t si;     // position in the tile-slice list
 };
 
 __device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Scalar load of a word that stays constant while the kernel runs (the work
+// and slice lists): through the constant address space it becomes a scalar
+// memory load, independent of the vector-memory counter.
+__device__ __forceinline__ int32_t const_ld(const int32_t* p) {
+  return *(__attribute__((address_space(4))) const int32_t*)p;
+}
 
 // Largest bf16 value <= x (x finite).
 __device__ __forceinline__ __bf16 bf16_floor(float x) {
@@ -117,21 +121,25 @@ __device__ __forceinline__ __bf16 bf16_floor(float x) {
 
 // First slice at or after list position si that shows this item a key.
 // Returns false when the list is exhausted.
-__device__ __forceinline__ bool find_slice(const FfaArgs& a, const magi_work_item& wi, int si, int64_t first_tok,
-                                           int64_t last_tok, SliceGeo& g) {
+__device__ __forceinline__ bool find_slice(const FfaArgs& a, const magi_work_item& wi, int si, int32_t first_tok,
+                                           int32_t last_tok, SliceGeo& g) {
   const int end = wi.slice_end < a.num_tile_slices ? wi.slice_end : a.num_tile_slices;
+  const int32_t nk = (int32_t)a.nk;
   for (si = si < 0 ? 0 : si; si < end; ++si) {
-    const int sidx = uni(a.tile_slices[si]);
+    const int sidx = const_ld(a.tile_slices + si);
     if (sidx < 0 || sidx >= a.num_slices) continue;
     const magi_attn_slice* sp = a.slices + sidx;
-    const int64_t qs = uni(sp->q_start), qe = uni(sp->q_end), k0 = uni(sp->k_start), k1 = uni(sp->k_end);
-    const int32_t causal = uni(sp->mask_type) == MAGI_MASK_CAUSAL;
-    const int64_t ks = k0 > 0 ? k0 : 0;
-    const int64_t ke = k1 < a.nk ? k1 : a.nk;
-    // a well-formed schedule only lists slices that cover every row of the item
+    const int32_t qs = const_ld(&sp->q_start), qe = const_ld(&sp->q_end), k0 = const_ld(&sp->k_start),
+                  k1 = const_ld(&sp->k_end);
+    const int32_t causal = const_ld(&sp->mask_type) == MAGI_MASK_CAUSAL;
+    const int32_t ks = k0 > 0 ? k0 : 0;
+    const int32_t ke = k1 < nk ? k1 : nk;
+    // a well-formed schedule only lists slices that cover every row of the
+    // item (so qe > last_tok >= first_tok >= qs >= 0 and no sum below
+    // leaves 32 bits)
     if (ks >= ke || first_tok < qs || last_tok >= qe) continue;
-    const int64_t koff = k1 - qe;
-    const int64_t khi = causal ? (koff + last_tok + 1 < ke ? koff + last_tok + 1 : ke) : ke;
+    const int32_t koff = k1 - qe;
+    const int32_t khi = causal ? (koff + last_tok + 1 < ke ? koff + last_tok + 1 : ke) : ke;
     if (khi <= ks) continue;
     g.ks = ks;
     g.khi = khi;
@@ -161,25 +169,26 @@ __device__ __forceinline__ float pair_other(float x, int h) {
 // spread over 256 / (32 NB) waves, so NB = 1 doubles the waves per SIMD
 // (more latency hiding) at the price of more LDS reads per score.
 template <int D, bool PRESCALED, int NB>
-__global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
+__global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(FfaArgs a) {
   using C = Cfg<D>;
-  constexpr int NT = 512 / NB;  // threads per workgroup
+  constexpr int NT = 2 * kRows / NB;  // threads per workgroup: 32 NB rows per wave
   constexpr int NCH = (TK * C::CH + NT - 1) / NT;  // 16-byte K (and V) chunks per thread per tile
-  // 32-key blocks whose scores are held at once: both for d=24, one at a
-  // time for d=48 where the larger accumulators leave fewer registers
-  constexpr int KG = D <= 32 ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][TK * C::KROW];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][TK * C::VROW];
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[3][TK * C::KROW];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[3][TK * C::VROW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, ln = lane & 31;
-  magi_work_item wi = a.work[blockIdx.x];
-  wi.q_start = uni(wi.q_start);
-  wi.q_len = uni(wi.q_len);
-  wi.slice_begin = uni(wi.slice_begin);
-  wi.slice_end = uni(wi.slice_end);
-  wi.kv_group = uni(wi.kv_group);
+  magi_work_item wi;
+  {
+    const magi_work_item* wp = a.work + blockIdx.x;
+    wi.q_start = const_ld(&wp->q_start);
+    wi.q_len = const_ld(&wp->q_len);
+    wi.slice_begin = const_ld(&wp->slice_begin);
+    wi.slice_end = const_ld(&wp->slice_end);
+    wi.kv_group = const_ld(&wp->kv_group);
+    wi.cost = 0;
+  }
   const int G = a.hq / a.hkv;
   const int cap = kRows / G;
   if (wi.q_start < 0 || wi.q_len <= 0 || (int64_t)wi.q_start + wi.q_len > a.nq || wi.kv_group < 0 ||
@@ -199,7 +208,7 @@ __global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
   // constant padding columns of both LDS buffers: K column D is 1 (AUG),
   // K columns D+1..DK-1 are 0, V column D is 1 (it accumulates the softmax
   // denominator), V columns D+1..DV-1 are 0
-  for (int b = 0; b < 2; ++b) {
+  for (int b = 0; b < 3; ++b) {
     if constexpr (AUG)
       for (int i = tid; i < TK * (C::DK - D); i += NT) {
         const int col = D + i % (C::DK - D);
@@ -293,14 +302,15 @@ __global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
     }
   }
 
-  const int64_t first_tok = wi.q_start, last_tok = (int64_t)wi.q_start + qlen - 1;
+  const int32_t first_tok = wi.q_start, last_tok = wi.q_start + qlen - 1;
   const int li = lane & 15;
   const int dgrp = ((lane >> 4) & 1) * 16;
   // key offset (within a 32-key block) of accumulator element i of this lane
   auto key_of = [&](int i) { return 8 * (i / 4) + 4 * h + (i % 4); };
   // K/V tiles are fetched with buffer loads whose range ends at the last
   // visible key, so rows past it read as zeros with no per-lane test; each
-  // thread's byte offset inside a tile never changes.
+  // thread's byte offset inside a tile never changes.  A tile spans TK rows
+  // of kv_stride elements, which the entry point keeps under 2^31 bytes.
   u32x4 kr[NCH], vr[NCH];
   int ch_off[NCH];
 #pragma unroll
@@ -308,194 +318,223 @@ __global__ __launch_bounds__(512 / NB, 4 / NB) void ffa_fwd_bf16(FfaArgs a) {
     const int ci = tid + j * NT;
     ch_off[j] = (ci / C::CH) * (int)a.kv_stride * 2 + (ci % C::CH) * 16;
   }
-  const int64_t kv_row_bytes = a.kv_stride * 2;
+  const int32_t kv_row_bytes = (int32_t)a.kv_stride * 2;
 
-  auto load_tile = [&](int64_t kt, int64_t khi) {
-    const int64_t elem0 = kt * a.kv_stride + (int64_t)g * D;
-    const int64_t valid = (khi - kt - 1) * kv_row_bytes + D * 2;
-    const int nrec = valid <= 0 ? 0 : (valid > 0x7fffffff ? 0x7fffffff : (int)valid);
+  // The item's tiles in visiting order: TK-key steps through one slice's
+  // visible key range, then on to the next slice that shows the item a key.
+  struct TileRef {
+    SliceGeo geo;
+    int32_t kt;     // first key of the tile
+    int32_t valid;  // 0 once the slice list is exhausted
+  };
+  auto next_tile = [&](const TileRef& t, TileRef& n) {
+    n.geo = t.geo;
+    n.kt = t.kt + TK;
+    n.valid = t.valid;
+    if (t.valid && n.kt >= t.geo.khi) {
+      n.valid = find_slice(a, wi, t.geo.si + 1, first_tok, last_tok, n.geo);
+      n.kt = n.geo.ks;
+    }
+  };
+  auto load_tile = [&](const TileRef& t, u32x4 (&kd)[NCH], u32x4 (&vd)[NCH]) {
+    const int64_t elem0 = (int64_t)t.kt * a.kv_stride + (int64_t)g * D;
+    const int32_t rows = t.geo.khi - t.kt < TK ? t.geo.khi - t.kt : TK;  // >= 1
+    const int nrec = (rows - 1) * kv_row_bytes + D * 2;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kp + elem0), (short)0, nrec, kBufCfg);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vp + elem0), (short)0, nrec, kBufCfg);
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       if (tid + j * NT < TK * C::CH) {
-        kr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ch_off[j], 0, 0));
-        vr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ch_off[j], 0, 0));
+        kd[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ch_off[j], 0, 0));
+        vd[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ch_off[j], 0, 0));
       }
     }
   };
-  auto store_tile = [&](int b) {
+  auto store_tile = [&](int b, const u32x4 (&kd)[NCH], const u32x4 (&vd)[NCH]) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int ci = tid + j * NT;
       if (ci < TK * C::CH) {
         const int r = ci / C::CH, part = ci % C::CH;
-        *reinterpret_cast<u32x4*>(&Ks[b][r * C::KROW + part * 8]) = kr[j];
-        *reinterpret_cast<u32x4*>(&Vs[b][r * C::VROW + part * 8]) = vr[j];
+        *reinterpret_cast<u32x4*>(&Ks[b][r * C::KROW + part * 8]) = kd[j];
+        *reinterpret_cast<u32x4*>(&Vs[b][r * C::VROW + part * 8]) = vd[j];
       }
     }
   };
+  // LDS-only workgroup barrier: the tile stores before it are visible after
+  // it, while global loads issued earlier stay in flight across it
+  auto lds_barrier = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  // K operand (A of S^T = K . Q^T) of 32-key block kb of LDS buffer b
+  auto read_k = [&](int b, int kb, bf16x8 (&kop)[C::KS]) {
+#pragma unroll
+    for (int ks2 = 0; ks2 < C::KS; ++ks2)
+      kop[ks2] = *reinterpret_cast<const bf16x8*>(&Ks[b][(kb * 32 + ln) * C::KROW + 16 * ks2 + 8 * h]);
+  };
 
-  SliceGeo cg;
-  bool have = find_slice(a, wi, wi.slice_begin, first_tok, last_tok, cg);
-  int64_t kt = cg.ks;
-  if (have) {
-    load_tile(kt, cg.khi);
-    store_tile(0);
+  // Pipeline.  Three LDS buffers hold consecutive tiles.  While a tile is
+  // computed, the next one sits in LDS and the one after is in flight from
+  // global memory; the K operand of each 32-key block is read from LDS one
+  // block ahead, so neither the global nor the LDS latency is on the
+  // critical path.  With tile t in buffer t % 3 and one barrier per tile
+  // (before its last block):
+  //   block NBLK-2 of tile t ends by storing tile t+1 (loads issued one tile
+  //   earlier) into buffer (t+1) % 3, whose previous tile t-2 was last read
+  //   before the barrier of tile t-1;
+  //   after the barrier, the loads of tile t+2 are issued and the K operand
+  //   of tile t+1's first block is read.
+  constexpr int NBLK = TK / 32;
+  static_assert(NBLK >= 2, "the pipeline needs two blocks per tile");
+  TileRef T0, T1;
+  T0.valid = find_slice(a, wi, wi.slice_begin, first_tok, last_tok, T0.geo);
+  T0.kt = T0.geo.ks;
+  next_tile(T0, T1);
+  bf16x8 kcur[C::KS];
+  {
+    // the first two tiles are fetched together; the second one stays in the
+    // staging registers until the first tile's pass stores it
+    u32x4 k0r[NCH], v0r[NCH];
+    if (T0.valid) load_tile(T0, k0r, v0r);
+    if (T1.valid) load_tile(T1, kr, vr);
+    // Drain every outstanding memory operation before the loop (both tiles
+    // are in flight together, so this costs one latency).  Without it the
+    // wait-count bookkeeping merges the lane-masked paths above into the
+    // loop header and makes every tile wait for its own prefetch.
+    __builtin_amdgcn_s_waitcnt(0);
+    if (T0.valid) store_tile(0, k0r, v0r);
   }
-  int buf = 0;
-  while (have) {
-    // the tile after this one: next in the slice, else the next slice's first
-    SliceGeo ng = cg;
-    int64_t nkt = kt + TK;
-    bool have_next = true;
-    if (nkt >= cg.khi) {
-      have_next = find_slice(a, wi, cg.si + 1, first_tok, last_tok, ng);
-      nkt = ng.ks;
-    }
-    __syncthreads();  // tile `buf` is in LDS; buffer buf^1 is no longer read
-    if (have_next) load_tile(nkt, ng.khi);  // in flight while this tile is computed
-
-    const bool masked = kt + TK > cg.kfull;
-    int lim[NB];  // keys at tile offset >= lim[nb] are hidden from the row
+  lds_barrier();
+  read_k(0, 0, kcur);  // unused if the item sees no key
+  int b0 = 0;  // buffer of T0
+  while (T0.valid) {
+    const int b1 = b0 == 2 ? 0 : b0 + 1;
+    const bool masked = T0.kt + TK > T0.geo.kfull;
+    const __bf16* Kb = Ks[b0];
+    __attribute__((address_space(3))) __bf16* Vb = (__attribute__((address_space(3))) __bf16*)Vs[b0];
+    TileRef T2;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      int64_t re = cg.ke;
-      if (cg.causal) {
-        const int64_t ce = (int64_t)cg.koff + qi[nb] + 1;
-        re = ce < re ? ce : re;
+    for (int kb = 0; kb < NBLK; ++kb) {
+      bf16x8 knext[C::KS];
+      if (kb == NBLK - 1) {
+        lds_barrier();  // tile T1 is in buffer b1
+        next_tile(T1, T2);
+        if (T2.valid) load_tile(T2, kr, vr);  // stored at the end of the next tile's block NBLK-2
+        read_k(b1, 0, knext);  // unused after the last tile
+      } else {
+        read_k(b0, kb + 1, knext);
       }
-      if (!rvalid[nb]) re = kt;
-      const int64_t rel = re - kt;
-      lim[nb] = rel < 0 ? 0 : (rel > TK ? TK : (int)rel);
-    }
-    const __bf16* Kb = Ks[buf];
-    __attribute__((address_space(3))) __bf16* Vb = (__attribute__((address_space(3))) __bf16*)Vs[buf];
-
+      // S^T = K . Q^T (minus m with AUG) for 32 keys x 32 NB rows; a lane
+      // holds 16 keys of one row
+      f32x16 sc[NB];
 #pragma unroll
-    for (int kb0 = 0; kb0 < 2; kb0 += KG) {
-      // S^T = K . Q^T (minus m with AUG) for KG*32 keys x 32 NB rows; a lane
-      // holds 16 keys of one row per block
-      f32x16 s[KG][NB];
+      for (int nb = 0; nb < NB; ++nb) {
+        f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[0], qreg[nb][0], (f32x16){}, 0, 0, 0);
 #pragma unroll
-      for (int kg = 0; kg < KG; ++kg) {
-        const int kb = kb0 + kg;
-        bf16x8 kop[C::KS];
-#pragma unroll
-        for (int ks2 = 0; ks2 < C::KS; ++ks2)
-          kop[ks2] = *reinterpret_cast<const bf16x8*>(&Kb[(kb * 32 + ln) * C::KROW + 16 * ks2 + 8 * h]);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qreg[nb][0], (f32x16){}, 0, 0, 0);
-#pragma unroll
-          for (int ks2 = 1; ks2 < C::KS; ++ks2)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks2], qreg[nb][ks2], acc, 0, 0, 0);
-          s[kg][nb] = acc;
-        }
+        for (int ks2 = 1; ks2 < C::KS; ++ks2)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[ks2], qreg[nb][ks2], acc, 0, 0, 0);
+        sc[nb] = acc;
       }
+#pragma unroll
+      for (int ks2 = 0; ks2 < C::KS; ++ks2) kcur[ks2] = knext[ks2];
       if (masked) {
 #pragma unroll
-        for (int kg = 0; kg < KG; ++kg)
+        for (int nb = 0; nb < NB; ++nb) {
+          // keys at block offset >= lim are hidden from the row
+          int32_t re = T0.geo.ke;
+          if (T0.geo.causal) {
+            const int32_t ce = T0.geo.koff + qi[nb] + 1;
+            re = ce < re ? ce : re;
+          }
+          const int32_t lim = re - T0.kt - kb * 32;
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if ((kb0 + kg) * 32 + key_of(i) >= lim[nb]) s[kg][nb][i] = -INFINITY;
+          for (int i = 0; i < 16; ++i)
+            if (key_of(i) >= lim) sc[nb][i] = -INFINITY;
+        }
       }
       // row maxima of the shifted scores; move m only where needed (the
       // bounded reference never moves)
-      bool sh[NB];
-      float delta[NB];
       if (!bounded) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float mx = s[0][nb][0];
-#pragma unroll
-        for (int kg = 0; kg < KG; ++kg)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kg][nb][i]);
-        mx = pair_max(mx);
-        const float xm = (PRESCALED ? mx : mx * c) - (AUG ? 0.f : m[nb]);
-        sh[nb] = (!init[nb] && xm > -INFINITY) || xm > kShift;
-        delta[nb] = sh[nb] ? xm : 0.f;
-        init[nb] = init[nb] || xm > -INFINITY;
-      }
-      bool any_sh = false;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) any_sh |= sh[nb];
-      if (__any(any_sh)) {
+        bool sh[NB];
+        float delta[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          float mnew = m[nb] + delta[nb];
-          __bf16 slot;
-          if constexpr (AUG) {
-            // the score MFMA subtracts a bf16 copy of m (unscaled units):
-            // round it toward larger m so no score can exceed it by more
-            // than the rounding step, and track exactly that value
-            slot = bf16_floor(-mnew * cinv);
-            mnew = PRESCALED ? -(float)slot : -(float)slot * c;
-          }
-          const float step = mnew - m[nb];
-          m[nb] = mnew;
-          const float alpha = __builtin_amdgcn_exp2f(-step);
+          float mx = sc[nb][0];
 #pragma unroll
-          for (int mb = 0; mb < C::MB; ++mb) o[nb][mb] *= alpha;
-          if constexpr (AUG) {
-            const float dsub = step * cinv;
+          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[nb][i]);
+          mx = pair_max(mx);
+          const float xm = (PRESCALED ? mx : mx * c) - (AUG ? 0.f : m[nb]);
+          sh[nb] = (!init[nb] && xm > -INFINITY) || xm > kShift;
+          delta[nb] = sh[nb] ? xm : 0.f;
+          init[nb] = init[nb] || xm > -INFINITY;
+        }
+        bool any_sh = false;
 #pragma unroll
-            for (int kg = 0; kg < KG; ++kg)
+        for (int nb = 0; nb < NB; ++nb) any_sh |= sh[nb];
+        if (__any(any_sh)) {
 #pragma unroll
-              for (int i = 0; i < 16; ++i) s[kg][nb][i] -= dsub;
-            qreg[nb][C::KS - 1][0] = h ? slot : qreg[nb][C::KS - 1][0];
+          for (int nb = 0; nb < NB; ++nb) {
+            float mnew = m[nb] + delta[nb];
+            __bf16 slot;
+            if constexpr (AUG) {
+              // the score MFMA subtracts a bf16 copy of m (unscaled units):
+              // round it toward larger m so no score can exceed it by more
+              // than the rounding step, and track exactly that value
+              slot = bf16_floor(-mnew * cinv);
+              mnew = PRESCALED ? -(float)slot : -(float)slot * c;
+            }
+            const float step = mnew - m[nb];
+            m[nb] = mnew;
+            const float alpha = __builtin_amdgcn_exp2f(-step);
+#pragma unroll
+            for (int mb = 0; mb < C::MB; ++mb) o[nb][mb] *= alpha;
+            if constexpr (AUG) {
+              const float dsub = step * cinv;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) sc[nb][i] -= dsub;
+              qreg[nb][C::KS - 1][0] = h ? slot : qreg[nb][C::KS - 1][0];
+            }
           }
         }
       }
-      }
+      // P = 2^(S'), rounded to bf16, already in the B-operand layout of P^T;
+      // O^T += V^T . P^T with the V^T operand read from the row-major V tile
+      // through the LDS transpose read
 #pragma unroll
-      for (int kg = 0; kg < KG; ++kg) {
-        const int kb = kb0 + kg;
-        // P = 2^(S'), rounded to bf16, already in the B-operand layout of P^T
-        bf16x8 pb[2][NB];  // [16-key half][nb]
+      for (int i2 = 0; i2 < 2; ++i2) {
+        bf16x8 pb[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float sv = s[kg][nb][8 * i2 + e];
-              float x;
-              if constexpr (AUG)
-                x = PRESCALED ? sv : sv * c;
-              else
-                x = PRESCALED ? sv - m[nb] : fmaf(sv, c, -m[nb]);
-              pb[i2][nb][e] = (__bf16)__builtin_amdgcn_exp2f(x);
-            }
-        // O^T += V^T . P^T ; the V^T operand comes from the row-major V tile
-        // through the LDS transpose read
-#pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) {
-          const int krow = kb * 32 + 16 * i2 + 4 * h + li / 4;
-#pragma unroll
-          for (int mb = 0; mb < C::MB; ++mb) {
-            const int dcol = mb * 32 + dgrp + 4 * (li % 4);
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + krow * C::VROW + dcol));
-            const s16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + (krow + 8) * C::VROW + dcol));
-            const bf16x8 vop =
-                __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              o[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[i2][nb], o[nb][mb], 0, 0, 0);
+          for (int e = 0; e < 8; ++e) {
+            const float sv = sc[nb][8 * i2 + e];
+            float x;
+            if constexpr (AUG)
+              x = PRESCALED ? sv : sv * c;
+            else
+              x = PRESCALED ? sv - m[nb] : fmaf(sv, c, -m[nb]);
+            pb[nb][e] = (__bf16)__builtin_amdgcn_exp2f(x);
           }
+        const int krow = kb * 32 + 16 * i2 + 4 * h + li / 4;
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) {
+          const int dcol = mb * 32 + dgrp + 4 * (li % 4);
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + krow * C::VROW + dcol));
+          const s16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + (krow + 8) * C::VROW + dcol));
+          const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            o[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[nb], o[nb][mb], 0, 0, 0);
         }
       }
+      if (kb == NBLK - 2 && T1.valid) store_tile(b1, kr, vr);
     }
-
-    if (have_next) store_tile(buf ^ 1);
-    cg = ng;
-    kt = nkt;
-    have = have_next;
-    buf ^= 1;
+    T0 = T1;
+    T1 = T2;
+    b0 = b1;
   }
 
   // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
@@ -591,17 +630,19 @@ hipError_t launch_ffa_fwd(const FfaArgs& a, hipStream_t stream) {
   if (a.dtype == MAGI_DTYPE_BF16) {
     // scores arrive in log2 units when the caller folded scale * log2(e) into Q or K
     const bool pre = fabsf(a.scale * kLog2e - 1.0f) < 1e-6f;
-    constexpr int NB24 = MAGI_NB24, NB48 = MAGI_NB48;
+    // head_dim 24: 64 rows per wave halve the LDS operand reads per score
+    // (3 waves per SIMD); head_dim 48: 32 rows per wave (4 waves per SIMD)
+    constexpr int NB24 = 2, NB48 = 1;
     if (a.head_dim == 24) {
       if (pre)
-        hipLaunchKernelGGL((ffa_fwd_bf16<24, true, NB24>), grid, dim3(512 / NB24), 0, stream, a);
+        hipLaunchKernelGGL((ffa_fwd_bf16<24, true, NB24>), grid, dim3(2 * kRows / NB24), 0, stream, a);
       else
-        hipLaunchKernelGGL((ffa_fwd_bf16<24, false, NB24>), grid, dim3(512 / NB24), 0, stream, a);
+        hipLaunchKernelGGL((ffa_fwd_bf16<24, false, NB24>), grid, dim3(2 * kRows / NB24), 0, stream, a);
     } else {
       if (pre)
-        hipLaunchKernelGGL((ffa_fwd_bf16<48, true, NB48>), grid, dim3(512 / NB48), 0, stream, a);
+        hipLaunchKernelGGL((ffa_fwd_bf16<48, true, NB48>), grid, dim3(2 * kRows / NB48), 0, stream, a);
       else
-        hipLaunchKernelGGL((ffa_fwd_bf16<48, false, NB48>), grid, dim3(512 / NB48), 0, stream, a);
+        hipLaunchKernelGGL((ffa_fwd_bf16<48, false, NB48>), grid, dim3(2 * kRows / NB48), 0, stream, a);
     }
   } else {
     if (a.head_dim == 24)

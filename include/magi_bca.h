@@ -205,7 +205,8 @@ int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, int32_t hq, 
  *              the same nq, nk, hq, hkv, head_dim, dtype (items are clamped to
  *              the tensor bounds on the device, so a mismatched list cannot
  *              read or write out of bounds)
- * Supported: head_dim 24 or 48; hq % hkv == 0; hq/hkv <= 256.
+ * Supported: head_dim 24 or 48; hq % hkv == 0; hq/hkv <= 256;
+ *              kv_tok_stride < 2^23 elements (MAGI_ERR_UNSUPPORTED otherwise).
  */
 int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                      int64_t nq, int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,

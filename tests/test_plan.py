@@ -288,6 +288,7 @@ def test_device_entry_points_validate_before_any_hip_call():
     assert ffa(q=None) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(kvs=20) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(kvs=28) == _lib.MAGI_ERR_INVALID_ARG      # not a 16-byte multiple
+    assert ffa(kvs=1 << 23) == _lib.MAGI_ERR_UNSUPPORTED  # a K/V tile would pass 2^31 bytes
     assert ffa(out=C.c_void_p(4100)) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(lse=C.c_void_p(4098)) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(scale=float("nan")) == _lib.MAGI_ERR_INVALID_ARG
