@@ -38,6 +38,8 @@
 //    online max that moves only by large steps), exp via v_exp_f32.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace magi {
@@ -260,13 +262,14 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) o[nb][mb] = (f32x16){};
   }
-  // Bounded reference.  When the caller supplies B >= |k| for every key of
-  // the group, q.k <= |q| B (Cauchy-Schwarz) bounds every score of a row, so
-  // |q| B can be the row's softmax reference from the start: no running
-  // max, no rescaling.  A wave uses it when every row's bound keeps the
-  // smallest possible score, -|q| B, within 2^-120 of it (bound <= 60 in
-  // log2 units: no underflow to zero or denormals); otherwise it keeps the
-  // online max.
+  // Bounded scores.  When the caller supplies B >= |k| for every key of the
+  // group, every score of a row lies within +-|q| B (Cauchy-Schwarz).  If
+  // that is at most 60 log2 units for every row of the wave, P = 2^s itself
+  // stays within [2^-60, 2^60] (normal in fp32 and bf16, sums far from
+  // overflow), and a softmax reference would only cancel in
+  // O = sum(P v) / sum(P): the wave then uses m = 0 and skips the running
+  // max, the rescaling and the subtraction.  Otherwise it keeps the online
+  // max.
   bool bounded = false;
   if (a.k_norm_max != nullptr) {
     const float B = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(a.k_norm_max[g])));
@@ -287,26 +290,15 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
       ok = ok && mb_row[nb] <= kBoundMax;
     }
     bounded = __all(ok);
-    if (bounded) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        init[nb] = true;
-        if constexpr (AUG) {
-          const __bf16 slot = bf16_floor(-mb_row[nb] * cinv);
-          m[nb] = PRESCALED ? -(float)slot : -(float)slot * c;
-          qreg[nb][C::KS - 1][0] = h ? slot : qreg[nb][C::KS - 1][0];
-        } else {
-          m[nb] = mb_row[nb];
-        }
-      }
-    }
   }
 
   const int32_t first_tok = wi.q_start, last_tok = wi.q_start + qlen - 1;
   const int li = lane & 15;
   const int dgrp = ((lane >> 4) & 1) * 16;
-  // key offset (within a 32-key block) of accumulator element i of this lane
-  auto key_of = [&](int i) { return 8 * (i / 4) + 4 * h + (i % 4); };
+  // Accumulator element i of lane half h holds key 8 (i / 4) + 4 h + i % 4
+  // of its 32-key block; the lane-independent part is a compile-time
+  // constant, so masking compares against constants.
+  constexpr auto key_of0 = [](int i) { return 8 * (i / 4) + (i % 4); };
   // K/V tiles are fetched with buffer loads whose range ends at the last
   // visible key, so rows past it read as zeros with no per-lane test; each
   // thread's byte offset inside a tile never changes.  A tile spans TK rows
@@ -409,133 +401,142 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
   lds_barrier();
   read_k(0, 0, kcur);  // unused if the item sees no key
   int b0 = 0;  // buffer of T0
-  while (T0.valid) {
-    const int b1 = b0 == 2 ? 0 : b0 + 1;
-    const bool masked = T0.kt + TK > T0.geo.kfull;
-    const __bf16* Kb = Ks[b0];
-    __attribute__((address_space(3))) __bf16* Vb = (__attribute__((address_space(3))) __bf16*)Vs[b0];
-    TileRef T2;
+  // the tile loop, compiled once for bounded waves and once for waves with
+  // an online max
+  auto tile_loop = [&](auto bounded_tag) {
+    constexpr bool BOUNDED = decltype(bounded_tag)::value;
+    while (T0.valid) {
+      const int b1 = b0 == 2 ? 0 : b0 + 1;
+      const bool masked = T0.kt + TK > T0.geo.kfull;
+      const __bf16* Kb = Ks[b0];
+      __attribute__((address_space(3))) __bf16* Vb = (__attribute__((address_space(3))) __bf16*)Vs[b0];
+      TileRef T2;
 #pragma unroll
-    for (int kb = 0; kb < NBLK; ++kb) {
-      bf16x8 knext[C::KS];
-      if (kb == NBLK - 1) {
-        lds_barrier();  // tile T1 is in buffer b1
-        next_tile(T1, T2);
-        if (T2.valid) load_tile(T2, kr, vr);  // stored at the end of the next tile's block NBLK-2
-        read_k(b1, 0, knext);  // unused after the last tile
-      } else {
-        read_k(b0, kb + 1, knext);
-      }
-      // S^T = K . Q^T (minus m with AUG) for 32 keys x 32 NB rows; a lane
-      // holds 16 keys of one row
-      f32x16 sc[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[0], qreg[nb][0], (f32x16){}, 0, 0, 0);
-#pragma unroll
-        for (int ks2 = 1; ks2 < C::KS; ++ks2)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[ks2], qreg[nb][ks2], acc, 0, 0, 0);
-        sc[nb] = acc;
-      }
-#pragma unroll
-      for (int ks2 = 0; ks2 < C::KS; ++ks2) kcur[ks2] = knext[ks2];
-      if (masked) {
+      for (int kb = 0; kb < NBLK; ++kb) {
+        bf16x8 knext[C::KS];
+        if (kb == NBLK - 1) {
+          lds_barrier();  // tile T1 is in buffer b1
+          next_tile(T1, T2);
+          if (T2.valid) load_tile(T2, kr, vr);  // stored at the end of the next tile's block NBLK-2
+          read_k(b1, 0, knext);  // unused after the last tile
+        } else {
+          read_k(b0, kb + 1, knext);
+        }
+        // S^T = K . Q^T (minus m with AUG) for 32 keys x 32 NB rows; a lane
+        // holds 16 keys of one row
+        f32x16 sc[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          // keys at block offset >= lim are hidden from the row
-          int32_t re = T0.geo.ke;
-          if (T0.geo.causal) {
-            const int32_t ce = T0.geo.koff + qi[nb] + 1;
-            re = ce < re ? ce : re;
-          }
-          const int32_t lim = re - T0.kt - kb * 32;
+          f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[0], qreg[nb][0], (f32x16){}, 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (key_of(i) >= lim) sc[nb][i] = -INFINITY;
+          for (int ks2 = 1; ks2 < C::KS; ++ks2)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[ks2], qreg[nb][ks2], acc, 0, 0, 0);
+          sc[nb] = acc;
         }
-      }
-      // row maxima of the shifted scores; move m only where needed (the
-      // bounded reference never moves)
-      if (!bounded) {
-        bool sh[NB];
-        float delta[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          float mx = sc[nb][0];
-#pragma unroll
-          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[nb][i]);
-          mx = pair_max(mx);
-          const float xm = (PRESCALED ? mx : mx * c) - (AUG ? 0.f : m[nb]);
-          sh[nb] = (!init[nb] && xm > -INFINITY) || xm > kShift;
-          delta[nb] = sh[nb] ? xm : 0.f;
-          init[nb] = init[nb] || xm > -INFINITY;
-        }
-        bool any_sh = false;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) any_sh |= sh[nb];
-        if (__any(any_sh)) {
+        for (int ks2 = 0; ks2 < C::KS; ++ks2) kcur[ks2] = knext[ks2];
+        if (masked) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
-            float mnew = m[nb] + delta[nb];
-            __bf16 slot;
-            if constexpr (AUG) {
-              // the score MFMA subtracts a bf16 copy of m (unscaled units):
-              // round it toward larger m so no score can exceed it by more
-              // than the rounding step, and track exactly that value
-              slot = bf16_floor(-mnew * cinv);
-              mnew = PRESCALED ? -(float)slot : -(float)slot * c;
+            // keys at block offset >= lim are hidden from the row
+            int32_t re = T0.geo.ke;
+            if (T0.geo.causal) {
+              const int32_t ce = T0.geo.koff + qi[nb] + 1;
+              re = ce < re ? ce : re;
             }
-            const float step = mnew - m[nb];
-            m[nb] = mnew;
-            const float alpha = __builtin_amdgcn_exp2f(-step);
+            const int32_t lim = re - T0.kt - kb * 32 - 4 * h;
 #pragma unroll
-            for (int mb = 0; mb < C::MB; ++mb) o[nb][mb] *= alpha;
-            if constexpr (AUG) {
-              const float dsub = step * cinv;
+            for (int i = 0; i < 16; ++i)
+              if (key_of0(i) >= lim) sc[nb][i] = -INFINITY;
+          }
+        }
+        // row maxima of the shifted scores; move m only where needed (the
+        // bounded reference never moves)
+        if constexpr (!BOUNDED) {
+          bool sh[NB];
+          float delta[NB];
 #pragma unroll
-              for (int i = 0; i < 16; ++i) sc[nb][i] -= dsub;
-              qreg[nb][C::KS - 1][0] = h ? slot : qreg[nb][C::KS - 1][0];
+          for (int nb = 0; nb < NB; ++nb) {
+            float mx = sc[nb][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[nb][i]);
+            mx = pair_max(mx);
+            const float xm = (PRESCALED ? mx : mx * c) - (AUG ? 0.f : m[nb]);
+            sh[nb] = (!init[nb] && xm > -INFINITY) || xm > kShift;
+            delta[nb] = sh[nb] ? xm : 0.f;
+            init[nb] = init[nb] || xm > -INFINITY;
+          }
+          bool any_sh = false;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) any_sh |= sh[nb];
+          if (__any(any_sh)) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              float mnew = m[nb] + delta[nb];
+              __bf16 slot;
+              if constexpr (AUG) {
+                // the score MFMA subtracts a bf16 copy of m (unscaled units):
+                // round it toward larger m so no score can exceed it by more
+                // than the rounding step, and track exactly that value
+                slot = bf16_floor(-mnew * cinv);
+                mnew = PRESCALED ? -(float)slot : -(float)slot * c;
+              }
+              const float step = mnew - m[nb];
+              m[nb] = mnew;
+              const float alpha = __builtin_amdgcn_exp2f(-step);
+#pragma unroll
+              for (int mb = 0; mb < C::MB; ++mb) o[nb][mb] *= alpha;
+              if constexpr (AUG) {
+                const float dsub = step * cinv;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sc[nb][i] -= dsub;
+                qreg[nb][C::KS - 1][0] = h ? slot : qreg[nb][C::KS - 1][0];
+              }
             }
           }
         }
-      }
-      // P = 2^(S'), rounded to bf16, already in the B-operand layout of P^T;
-      // O^T += V^T . P^T with the V^T operand read from the row-major V tile
-      // through the LDS transpose read
+        // P = 2^(S'), rounded to bf16, already in the B-operand layout of P^T;
+        // O^T += V^T . P^T with the V^T operand read from the row-major V tile
+        // through the LDS transpose read
 #pragma unroll
-      for (int i2 = 0; i2 < 2; ++i2) {
-        bf16x8 pb[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float sv = sc[nb][8 * i2 + e];
-            float x;
-            if constexpr (AUG)
-              x = PRESCALED ? sv : sv * c;
-            else
-              x = PRESCALED ? sv - m[nb] : fmaf(sv, c, -m[nb]);
-            pb[nb][e] = (__bf16)__builtin_amdgcn_exp2f(x);
-          }
-        const int krow = kb * 32 + 16 * i2 + 4 * h + li / 4;
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) {
-          const int dcol = mb * 32 + dgrp + 4 * (li % 4);
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + krow * C::VROW + dcol));
-          const s16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + (krow + 8) * C::VROW + dcol));
-          const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int i2 = 0; i2 < 2; ++i2) {
+          bf16x8 pb[NB];
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
-            o[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[nb], o[nb][mb], 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float sv = sc[nb][8 * i2 + e];
+              float x;
+              if constexpr (AUG || BOUNDED)
+                x = PRESCALED ? sv : sv * c;
+              else
+                x = PRESCALED ? sv - m[nb] : fmaf(sv, c, -m[nb]);
+              pb[nb][e] = (__bf16)__builtin_amdgcn_exp2f(x);
+            }
+          const int krow = kb * 32 + 16 * i2 + 4 * h + li / 4;
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb) {
+            const int dcol = mb * 32 + dgrp + 4 * (li % 4);
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + krow * C::VROW + dcol));
+            const s16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + (krow + 8) * C::VROW + dcol));
+            const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              o[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[nb], o[nb][mb], 0, 0, 0);
+          }
         }
+        if (kb == NBLK - 2 && T1.valid) store_tile(b1, kr, vr);
       }
-      if (kb == NBLK - 2 && T1.valid) store_tile(b1, kr, vr);
+      T0 = T1;
+      T1 = T2;
+      b0 = b1;
     }
-    T0 = T1;
-    T1 = T2;
-    b0 = b1;
-  }
+  };
+  if (bounded)
+    tile_loop(std::true_type{});
+  else
+    tile_loop(std::false_type{});
 
   // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
   __bf16* __restrict__ op = reinterpret_cast<__bf16*>(a.out);

@@ -55,11 +55,16 @@ def build_slices(seqs: Sequence) -> np.ndarray:
             keep.append(arr)
         descs[i] = SeqDesc(s.chunk_len, s.num_kv_chunks, s.num_q_chunks, s.q_offset, s.k_offset,
                            C.cast(arr, C.POINTER(C.c_int32)) if arr is not None else None)
+    # one call with a generous capacity; the size query only on overflow
     cnt = C.c_int32(0)
-    check(lib().magi_slices_build(descs, n, None, 0, C.byref(cnt)))
-    out = (AttnSlice * max(cnt.value, 1))()
-    check(lib().magi_slices_build(descs, n, out, cnt.value, C.byref(cnt)))
-    return np.ctypeslib.as_array(C.cast(out, C.POINTER(C.c_int32)), shape=(max(cnt.value, 1), 5))[:cnt.value].copy()
+    cap = 2 * sum(int(s.num_q_chunks) for s in seqs) + 4
+    while True:
+        out = np.empty((cap, 5), np.int32)
+        st = lib().magi_slices_build(descs, n, out.ctypes.data_as(C.POINTER(AttnSlice)), cap, C.byref(cnt))
+        if st != _lib.MAGI_ERR_BUFFER_TOO_SMALL:
+            check(st)
+            return out[:cnt.value]
+        cap = cnt.value
 
 
 def default_tile_q(hq: int, hkv: int, head_dim: int, dtype: int) -> int:
@@ -73,19 +78,27 @@ def schedule(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim: 
     sp = s.ctypes.data_as(C.POINTER(AttnSlice)) if len(s) else None
     nw, nt = C.c_int32(0), C.c_int32(0)
     L = lib()
-    check(L.magi_schedule(sp, len(s), nq, nk, hq, hkv, head_dim, dtype, tile_q, None, 0, C.byref(nw),
-                          None, 0, C.byref(nt)))
-    work = np.zeros((max(nw.value, 1), 6), np.int32)
-    ts = np.zeros(max(nt.value, 1), np.int32)
-    check(L.magi_schedule(sp, len(s), nq, nk, hq, hkv, head_dim, dtype, tile_q,
-                          work.ctypes.data_as(C.POINTER(WorkItem)), work.shape[0], C.byref(nw),
-                          ts.ctypes.data_as(C.POINTER(C.c_int32)), ts.shape[0], C.byref(nt)))
-    return work[:nw.value], ts[:nt.value]
+    # one call with capacities that fit the usual schedule; the exact sizes
+    # come back with MAGI_ERR_BUFFER_TOO_SMALL otherwise
+    tq = tile_q if tile_q > 0 else max(default_tile_q(hq, hkv, head_dim, dtype), 1)
+    tiles = -(-nq // tq) + 2 * len(s) + 1
+    wcap, tcap = max(tiles * hkv, 1), max(tiles * min(max(len(s), 1), 8), 1)
+    while True:
+        work = np.empty((wcap, 6), np.int32)
+        ts = np.empty(tcap, np.int32)
+        st = L.magi_schedule(sp, len(s), nq, nk, hq, hkv, head_dim, dtype, tile_q,
+                             work.ctypes.data_as(C.POINTER(WorkItem)), wcap, C.byref(nw),
+                             ts.ctypes.data_as(C.POINTER(C.c_int32)), tcap, C.byref(nt))
+        if st != _lib.MAGI_ERR_BUFFER_TOO_SMALL:
+            check(st)
+            return work[:nw.value], ts[:nt.value]
+        wcap, tcap = max(nw.value, 1), max(nt.value, 1)
 
 
 @dataclass
 class Plan:
-    """Device copies of a schedule, ready for ffa_fwd."""
+    """Device copies of a schedule, ready for ffa_fwd (flat int32 views of one
+    device buffer; ``host`` keeps the shaped host arrays)."""
     nq: int
     nk: int
     hq: int
@@ -99,23 +112,28 @@ class Plan:
 
     @property
     def num_work(self) -> int:
-        return self.work.shape[0]
-
-
-def _to_device(a: np.ndarray, device) -> torch.Tensor:
-    t = torch.from_numpy(np.ascontiguousarray(a, np.int32))
-    if t.numel() == 0:
-        return torch.zeros(1, dtype=torch.int32, device=device)
-    return t.pin_memory().to(device, non_blocking=True)
+        return int(self.host["work"].shape[0])
 
 
 def make_plan(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim: int, dtype,
               device="cuda", tile_q: int = 0) -> Plan:
+    """schedule + one upload: the three int32 lists travel in a single pinned
+    host-to-device copy and the plan holds views of it."""
     code = dtype if isinstance(dtype, int) else dtype_code(dtype)
     slices = np.asarray(slices, np.int32).reshape(-1, 5)
     work, ts = schedule(slices, nq, nk, hq, hkv, head_dim, code, tile_q)
-    return Plan(nq, nk, hq, hkv, head_dim, code, _to_device(slices, device), _to_device(work, device),
-                _to_device(ts, device), {"slices": slices, "work": work, "tile_slices": ts})
+    parts = [slices.reshape(-1), work.reshape(-1), ts.reshape(-1)]
+    sizes = [max(p.size, 1) for p in parts]     # an empty list still gets one valid word
+    host = torch.zeros(sum(sizes), dtype=torch.int32, pin_memory=True)
+    hv = host.numpy()
+    off = 0
+    for p, n in zip(parts, sizes):
+        hv[off:off + p.size] = p
+        off += n
+    dev = host.to(device, non_blocking=True)
+    o1, o2 = sizes[0], sizes[0] + sizes[1]
+    return Plan(nq, nk, hq, hkv, head_dim, code, dev[:o1], dev[o1:o2], dev[o2:],
+                {"slices": slices, "work": work, "tile_slices": ts})
 
 
 def plan_for_videos(seqs: Sequence, nq: int, nk: int, hq: int, hkv: int, head_dim: int, dtype,
