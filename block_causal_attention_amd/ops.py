@@ -109,6 +109,7 @@ class Plan:
     work: torch.Tensor
     tile_slices: torch.Tensor
     host: dict = field(default_factory=dict)
+    ready: Optional[torch.cuda.Event] = None  # recorded after the upload; ffa_fwd waits on it
 
     @property
     def num_work(self) -> int:
@@ -130,10 +131,32 @@ def make_plan(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim:
     for p, n in zip(parts, sizes):
         hv[off:off + p.size] = p
         off += n
-    dev = host.to(device, non_blocking=True)
+    # The copy runs on a side stream so it does not queue behind the work
+    # already on the caller's stream (the previous attention launch); only
+    # ffa_fwd waits for it, through ``ready``.
+    main = torch.cuda.current_stream(device)
+    side = _upload_stream(main.device)
+    with torch.cuda.stream(side):
+        dev = host.to(device, non_blocking=True)
+        ready = torch.cuda.Event()
+        ready.record(side)
+    dev.record_stream(main)
     o1, o2 = sizes[0], sizes[0] + sizes[1]
     return Plan(nq, nk, hq, hkv, head_dim, code, dev[:o1], dev[o1:o2], dev[o2:],
-                {"slices": slices, "work": work, "tile_slices": ts})
+                {"slices": slices, "work": work, "tile_slices": ts}, ready)
+
+
+_UPLOAD_STREAMS = {}
+
+
+def _upload_stream(device) -> torch.cuda.Stream:
+    """One default-priority side stream per device for plan uploads."""
+    idx = torch.device(device).index
+    idx = torch.cuda.current_device() if idx is None else idx
+    s = _UPLOAD_STREAMS.get(idx)
+    if s is None:
+        s = _UPLOAD_STREAMS[idx] = torch.cuda.Stream(device=idx)
+    return s
 
 
 def plan_for_videos(seqs: Sequence, nq: int, nk: int, hq: int, hkv: int, head_dim: int, dtype,
@@ -212,6 +235,8 @@ def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
     _check_3d("out", out, hq, d)
     if lse is None and return_lse:
         lse = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
+    if plan.ready is not None:
+        torch.cuda.current_stream(q.device).wait_event(plan.ready)
     check(lib().magi_ffa_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q.shape[0], k.shape[0], hq, hkv, d,
         dtype_code(q.dtype), q.stride(0), k.stride(0), out.stride(0),
