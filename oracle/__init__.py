@@ -15,6 +15,7 @@ Functions (each cites the passage it follows in its docstring):
   video_mask       dense block-causal / KV-range / packed-video mask rows
   slices_mask      dense mask rows denoted by a list of AttnSlices
   attention        masked softmax attention with grouped K/V heads
+  attention_backward  its gradients with respect to q, k and v
   forward          qk_norm -> rope_3d -> attention, end to end
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against library
@@ -25,6 +26,6 @@ do not state them, so those readings are "parity unpinned" with respect to the
 model, while the oracle-vs-kernel parity is fully pinned.
 """
 from .reference import (  # noqa: F401
-    qk_norm, rope_inv_freq, rope_3d, video_mask, slices_mask, attention, forward,
+    qk_norm, rope_inv_freq, rope_3d, video_mask, slices_mask, attention, attention_backward, forward,
     MASK_FULL, MASK_CAUSAL,
 )

@@ -178,6 +178,53 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
     return O, LSE
 
 
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                       mask: np.ndarray, scale: float):
+    """Gradients of ``attention`` with respect to q, k and v, float64.
+
+    The attention is trained with the same kernel family ([notes] "训练 Infra":
+    Flex-Flash-Attention serves training; [interview] Q&A on MagiAttention),
+    so its backward is part of the method; the pages give no formula, and
+    this is the chain rule of the definition above written out per head h
+    with group g = h // (hq // hkv):
+        P  = softmax over visible keys of scale * q k^T     (rows x keys)
+        dV_g += P^T dO_h
+        dP = dO_h V_g^T
+        dS = P * (dP - rowsum(dO_h * O_h))                  (zero off the mask)
+        dQ_h  = scale * dS K_g
+        dK_g += scale * dS^T Q_h
+    A row that sees no key contributes nothing.  q, dout: [r, hq, d];
+    k, v: [nk, hkv, d]; mask: bool [r, nk].  Returns (dQ, dK, dV).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    dout = np.asarray(dout, np.float64)
+    r, hq, d = q.shape
+    hkv = k.shape[1]
+    G = hq // hkv
+    dQ = np.zeros_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+    live = mask.any(axis=1)
+    for h in range(hq):
+        g = h // G
+        s = (q[:, h, :] @ k[:, g, :].T) * scale
+        s = np.where(mask, s, -np.inf)
+        mx = np.where(live, np.max(s, axis=1), 0.0)
+        p = np.exp(s - mx[:, None])
+        l = np.where(live, p.sum(axis=1), 1.0)
+        p = p / l[:, None]                                   # rows with no key stay 0
+        o = p @ v[:, g, :]
+        dV[:, g, :] += p.T @ dout[:, h, :]
+        dp = dout[:, h, :] @ v[:, g, :].T
+        delta = np.sum(dout[:, h, :] * o, axis=1)
+        ds = p * (dp - delta[:, None])
+        dQ[:, h, :] = scale * (ds @ k[:, g, :])
+        dK[:, g, :] += scale * (ds.T @ q[:, h, :])
+    return dQ, dK, dV
+
+
 def forward(q, k, v, gain_q, gain_k, pos_q, pos_k, bases, eps, mask, scale,
             q_rows=None):
     """QK-Norm, then 3D RoPE on Q and K, then masked GQA attention.

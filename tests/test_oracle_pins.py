@@ -360,3 +360,85 @@ def test_forward_matches_torch_composition():
 
     ref = _sdpa(t_norm_rope(q, gq), t_norm_rope(k, gk), v, mask=mask)
     np.testing.assert_allclose(O, ref, rtol=1e-11, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- attention backward
+
+def _random_mask(r, nk, empty_rows=()):
+    m = RNG.random((r, nk)) < 0.6
+    m[np.arange(r), RNG.integers(0, nk, r)] = True
+    for i in empty_rows:
+        m[i] = False
+    return m
+
+
+def test_attention_backward_matches_finite_differences():
+    # brute force: central differences of sum(O * dO) through the forward;
+    # catches a wrong sign in dS, a missing delta term, a transposed dS or a
+    # dropped scale in dQ / dK, and GQA accumulation errors in dK / dV
+    r, nk, hq, hkv, d = 5, 6, 4, 2, 3
+    q = RNG.standard_normal((r, hq, d))
+    k = RNG.standard_normal((nk, hkv, d))
+    v = RNG.standard_normal((nk, hkv, d))
+    dO = RNG.standard_normal((r, hq, d))
+    mask = _random_mask(r, nk, empty_rows=(2,))
+    scale = 0.7
+    dQ, dK, dV = oracle.attention_backward(q, k, v, dO, mask, scale)
+
+    def f(qq, kk, vv):
+        return float(np.sum(attention(qq, kk, vv, mask, scale)[0] * dO))
+
+    eps = 1e-6
+    for name, x, g in (("q", q, dQ), ("k", k, dK), ("v", v, dV)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = {"q": q, "k": k, "v": v, name: xp}
+            args_m = {"q": q, "k": k, "v": v, name: xm}
+            num[idx] = (f(args_p["q"], args_p["k"], args_p["v"]) - f(args_m["q"], args_m["k"], args_m["v"])) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8, err_msg=name)
+    assert not dQ[2].any()   # the row that sees no key gets no gradient
+
+
+def test_attention_backward_matches_torch_autograd_sdpa():
+    # library routine: autograd through torch's SDPA (float64, GQA by
+    # repeating K/V) on a block-causal mask
+    n, hq, hkv, d = 12, 8, 2, 24
+    G = hq // hkv
+    q = RNG.standard_normal((n, hq, d))
+    k = RNG.standard_normal((n, hkv, d))
+    v = RNG.standard_normal((n, hkv, d))
+    dO = RNG.standard_normal((n, hq, d))
+    mask = video_mask([_seq(4, 3)], n, n)
+    scale = d ** -0.5
+    dQ, dK, dV = oracle.attention_backward(q, k, v, dO, mask, scale)
+    qt = torch.from_numpy(q).requires_grad_()
+    kt = torch.from_numpy(k).requires_grad_()
+    vt = torch.from_numpy(v).requires_grad_()
+    o = F.scaled_dot_product_attention(qt.permute(1, 0, 2), kt.repeat_interleave(G, dim=1).permute(1, 0, 2),
+                                       vt.repeat_interleave(G, dim=1).permute(1, 0, 2),
+                                       attn_mask=torch.from_numpy(mask), scale=scale)
+    o.permute(1, 0, 2).backward(torch.from_numpy(dO))
+    np.testing.assert_allclose(dQ, qt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dK, kt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dV, vt.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_attention_backward_sum_invariants():
+    # each live row's probabilities sum to 1 and its dS sums to 0, so per
+    # group sum_k dV[k] = sum of the live rows' dO over the group's heads and
+    # sum_k dK[k] = 0; catches a dropped delta term or an unnormalised P
+    r, nk, hq, hkv, d = 9, 11, 6, 3, 5
+    q = RNG.standard_normal((r, hq, d))
+    k = RNG.standard_normal((nk, hkv, d))
+    v = RNG.standard_normal((nk, hkv, d))
+    dO = RNG.standard_normal((r, hq, d))
+    mask = _random_mask(r, nk, empty_rows=(4,))
+    _, dK, dV = oracle.attention_backward(q, k, v, dO, mask, 0.4)
+    live = mask.any(axis=1)
+    G = hq // hkv
+    for g in range(hkv):
+        np.testing.assert_allclose(dV[:, g].sum(0), dO[live][:, g * G:(g + 1) * G].sum((0, 1)), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dK[:, g].sum(0), 0.0, atol=1e-12)
