@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmagi_bca.so")
-SOURCES = ["plan.cpp", "api.cpp", "qknorm_rope.hip", "ffa_fwd.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "qknorm_rope.hip", "ffa_fwd.hip", "ffa_bwd.hip"]
 ARCH = "gfx950"
 
 

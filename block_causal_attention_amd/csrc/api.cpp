@@ -142,3 +142,75 @@ extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, voi
   if (e != hipSuccess) return fail(MAGI_ERR_HIP, "ffa_fwd launch: %s", hipGetErrorString(e));
   return ok();
 }
+
+extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t nq,
+                                int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
+                                int64_t q_tok_stride, int64_t kv_tok_stride, int64_t o_tok_stride,
+                                float softmax_scale, const magi_attn_slice* slices, int32_t num_slices,
+                                const magi_work_item* qwork, int32_t num_qwork, const int32_t* q_tile_slices,
+                                int32_t num_q_tile_slices, const magi_work_item* kwork, int32_t num_kwork,
+                                const int32_t* k_tile_slices, int32_t num_k_tile_slices, void* stream) {
+  int32_t st;
+  if ((st = check_common(head_dim, dtype)) != MAGI_OK) return st;
+  if (hq < 1 || hkv < 1) return fail(MAGI_ERR_INVALID_ARG, "hq and hkv must be >= 1");
+  if (hq % hkv) return fail(MAGI_ERR_INVALID_ARG, "hq %% hkv != 0 (hq=%d hkv=%d)", hq, hkv);
+  if (hq / hkv > 64) return fail(MAGI_ERR_UNSUPPORTED, "group size %d > 64", hq / hkv);
+  const struct { const char* name; const void* p; int64_t n; int32_t heads; int64_t stride; } tensors[] = {
+      {"q", q, nq, hq, q_tok_stride},        {"dq", dq, nq, hq, q_tok_stride},
+      {"out", out, nq, hq, o_tok_stride},    {"dout", dout, nq, hq, o_tok_stride},
+      {"k", k, nk, hkv, kv_tok_stride},      {"v", v, nk, hkv, kv_tok_stride},
+      {"dk", dk, nk, hkv, kv_tok_stride},    {"dv", dv, nk, hkv, kv_tok_stride}};
+  for (const auto& t : tensors)
+    if ((st = check_tensor(t.name, t.p, t.n, t.heads, t.stride, head_dim, dtype)) != MAGI_OK) return st;
+  if (kv_tok_stride >= (int64_t)1 << 23)
+    return fail(MAGI_ERR_UNSUPPORTED, "kv row stride %lld >= 2^23 elements", (long long)kv_tok_stride);
+  if (nq > 0 && (lse == nullptr || delta == nullptr)) return fail(MAGI_ERR_INVALID_ARG, "lse and delta are required");
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(delta) & 3u))
+    return fail(MAGI_ERR_INVALID_ARG, "lse / delta not 4-byte aligned");
+  if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
+    return fail(MAGI_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (num_slices < 0 || num_qwork < 0 || num_q_tile_slices < 0 || num_kwork < 0 || num_k_tile_slices < 0)
+    return fail(MAGI_ERR_INVALID_ARG, "negative list length");
+  if ((num_slices > 0 && slices == nullptr) || (num_qwork > 0 && qwork == nullptr) ||
+      (num_q_tile_slices > 0 && q_tile_slices == nullptr) || (num_kwork > 0 && kwork == nullptr) ||
+      (num_k_tile_slices > 0 && k_tile_slices == nullptr))
+    return fail(MAGI_ERR_INVALID_ARG, "a non-empty list pointer is NULL");
+  if (num_qwork > 0 && nq == 0) return fail(MAGI_ERR_INVALID_ARG, "query work items for an empty query tensor");
+  if (num_kwork > 0 && nk == 0) return fail(MAGI_ERR_INVALID_ARG, "key work items for an empty key tensor");
+
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = delta;
+  a.nq = nq;
+  a.nk = nk;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.head_dim = head_dim;
+  a.dtype = dtype;
+  a.q_stride = q_tok_stride;
+  a.kv_stride = kv_tok_stride;
+  a.o_stride = o_tok_stride;
+  a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  a.slices = slices;
+  a.num_slices = num_slices;
+  a.qwork = qwork;
+  a.num_qwork = num_qwork;
+  a.q_tile_slices = q_tile_slices;
+  a.num_q_tile_slices = num_q_tile_slices;
+  a.kwork = kwork;
+  a.num_kwork = num_kwork;
+  a.k_tile_slices = k_tile_slices;
+  a.num_k_tile_slices = num_k_tile_slices;
+  const hipError_t e = launch_ffa_bwd(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MAGI_ERR_HIP, "ffa_bwd launch: %s", hipGetErrorString(e));
+  return ok();
+}

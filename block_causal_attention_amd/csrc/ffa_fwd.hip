@@ -40,24 +40,18 @@
 
 #include <type_traits>
 
+#include "ffa_common.h"
 #include "kernels.h"
 
 namespace magi {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+using namespace dev;
 
 constexpr int kRows = 256;        // query rows per work item
 constexpr int kThreads = kRows;   // fp32 kernel: one thread per row
 constexpr int TK = 64;  // keys per LDS tile
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1e30f;  // finite "minus infinity" for the running max
-constexpr int kBufCfg = 0x00020000;  // raw buffer resource word 3 (gfx9 family: 32-bit data format)
 constexpr float kShift = 8.0f;  // move the softmax reference when a score exceeds it by 2^8
 constexpr float kBoundMargin = 1.0f + 1.0f / 128.0f;  // covers bf16 rounding of k and fp32 sums
 constexpr float kBoundMax = 60.0f;                    // log2 units, see the bounded reference
@@ -81,35 +75,6 @@ struct Cfg {
   static_assert(((D % 32) / 4) % 2 == 0, "ones column must fall in lane half 0");
 };
 
-__device__ inline int64_t causal_end(const magi_attn_slice& s, int64_t ke, int64_t row) {
-  // bottom-right aligned causal: row r sees k with k - k_end <= r - q_end
-  const int64_t e = (int64_t)s.k_end - (int64_t)s.q_end + row + 1;
-  return e < ke ? e : ke;
-}
-
-// One slice as seen by one work item.  Every field is the same for the whole
-// workgroup and lives in scalar registers.  Token and key indices fit in 32
-// bits (the entry point rejects nq or nk >= 2^31), so all of it is 32-bit
-// scalar arithmetic.
-struct SliceGeo {
-  int32_t ks;     // first key
-  int32_t khi;    // one past the last key that any row of the item sees
-  int32_t kfull;  // keys below this are visible to every row of the item
-  int32_t ke;     // slice key end, clamped to nk
-  int32_t koff;   // k_end - q_end: a causal row r sees keys below koff + r + 1
-  int32_t causal;
-  int32_t si;     // position in the tile-slice list
-};
-
-__device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// Scalar load of a word that stays constant while the kernel runs (the work
-// and slice lists): through the constant address space it becomes a scalar
-// memory load, independent of the vector-memory counter.
-__device__ __forceinline__ int32_t const_ld(const int32_t* p) {
-  return *(__attribute__((address_space(4))) const int32_t*)p;
-}
-
 // Largest bf16 value <= x (x finite).
 __device__ __forceinline__ __bf16 bf16_floor(float x) {
   __bf16 r = (__bf16)x;
@@ -119,50 +84,6 @@ __device__ __forceinline__ __bf16 bf16_floor(float x) {
     r = __builtin_bit_cast(__bf16, b);
   }
   return r;
-}
-
-// First slice at or after list position si that shows this item a key.
-// Returns false when the list is exhausted.
-__device__ __forceinline__ bool find_slice(const FfaArgs& a, const magi_work_item& wi, int si, int32_t first_tok,
-                                           int32_t last_tok, SliceGeo& g) {
-  const int end = wi.slice_end < a.num_tile_slices ? wi.slice_end : a.num_tile_slices;
-  const int32_t nk = (int32_t)a.nk;
-  for (si = si < 0 ? 0 : si; si < end; ++si) {
-    const int sidx = const_ld(a.tile_slices + si);
-    if (sidx < 0 || sidx >= a.num_slices) continue;
-    const magi_attn_slice* sp = a.slices + sidx;
-    const int32_t qs = const_ld(&sp->q_start), qe = const_ld(&sp->q_end), k0 = const_ld(&sp->k_start),
-                  k1 = const_ld(&sp->k_end);
-    const int32_t causal = const_ld(&sp->mask_type) == MAGI_MASK_CAUSAL;
-    const int32_t ks = k0 > 0 ? k0 : 0;
-    const int32_t ke = k1 < nk ? k1 : nk;
-    // a well-formed schedule only lists slices that cover every row of the
-    // item (so qe > last_tok >= first_tok >= qs >= 0 and no sum below
-    // leaves 32 bits)
-    if (ks >= ke || first_tok < qs || last_tok >= qe) continue;
-    const int32_t koff = k1 - qe;
-    const int32_t khi = causal ? (koff + last_tok + 1 < ke ? koff + last_tok + 1 : ke) : ke;
-    if (khi <= ks) continue;
-    g.ks = ks;
-    g.khi = khi;
-    g.kfull = causal ? (koff + first_tok + 1 < ke ? koff + first_tok + 1 : ke) : ke;
-    g.ke = ke;
-    g.koff = koff;
-    g.causal = causal;
-    g.si = si;
-    return true;
-  }
-  return false;
-}
-
-// Max of x over the lane pair (l, l ^ 32), and x from the partner lane.
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_other(float x, int h) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(h ? r[0] : r[1]);
 }
 
 // PRESCALED: the caller folded softmax_scale * log2(e) into Q or K, so the
@@ -181,16 +102,7 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, ln = lane & 31;
-  magi_work_item wi;
-  {
-    const magi_work_item* wp = a.work + blockIdx.x;
-    wi.q_start = const_ld(&wp->q_start);
-    wi.q_len = const_ld(&wp->q_len);
-    wi.slice_begin = const_ld(&wp->slice_begin);
-    wi.slice_end = const_ld(&wp->slice_end);
-    wi.kv_group = const_ld(&wp->kv_group);
-    wi.cost = 0;
-  }
+  const magi_work_item wi = load_item(a.work, blockIdx.x);
   const int G = a.hq / a.hkv;
   const int cap = kRows / G;
   if (wi.q_start < 0 || wi.q_len <= 0 || (int64_t)wi.q_start + wi.q_len > a.nq || wi.kv_group < 0 ||
@@ -293,6 +205,7 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
   }
 
   const int32_t first_tok = wi.q_start, last_tok = wi.q_start + qlen - 1;
+  const SliceLists lists{a.slices, a.num_slices, a.tile_slices, a.num_tile_slices};
   const int li = lane & 15;
   const int dgrp = ((lane >> 4) & 1) * 16;
   // Accumulator element i of lane half h holds key 8 (i / 4) + 4 h + i % 4
@@ -324,7 +237,7 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
     n.kt = t.kt + TK;
     n.valid = t.valid;
     if (t.valid && n.kt >= t.geo.khi) {
-      n.valid = find_slice(a, wi, t.geo.si + 1, first_tok, last_tok, n.geo);
+      n.valid = find_slice(lists, wi.slice_end, (int32_t)a.nk, t.geo.si + 1, first_tok, last_tok, n.geo);
       n.kt = n.geo.ks;
     }
   };
@@ -353,13 +266,7 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
       }
     }
   };
-  // LDS-only workgroup barrier: the tile stores before it are visible after
-  // it, while global loads issued earlier stay in flight across it
-  auto lds_barrier = [&]() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  };
+
   // K operand (A of S^T = K . Q^T) of 32-key block kb of LDS buffer b
   auto read_k = [&](int b, int kb, bf16x8 (&kop)[C::KS]) {
 #pragma unroll
@@ -381,7 +288,7 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
   constexpr int NBLK = TK / 32;
   static_assert(NBLK >= 2, "the pipeline needs two blocks per tile");
   TileRef T0, T1;
-  T0.valid = find_slice(a, wi, wi.slice_begin, first_tok, last_tok, T0.geo);
+  T0.valid = find_slice(lists, wi.slice_end, (int32_t)a.nk, wi.slice_begin, first_tok, last_tok, T0.geo);
   T0.kt = T0.geo.ks;
   next_tile(T0, T1);
   bf16x8 kcur[C::KS];

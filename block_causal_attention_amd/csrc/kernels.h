@@ -53,4 +53,33 @@ struct FfaArgs {
 
 hipError_t launch_ffa_fwd(const FfaArgs& a, hipStream_t stream);
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // [nq][hq] rowsum(dout * out), written first
+  int64_t nq, nk;
+  int32_t hq, hkv, head_dim, dtype;
+  int64_t q_stride, kv_stride, o_stride;
+  float scale;
+  const magi_attn_slice* slices;
+  int32_t num_slices;
+  const magi_work_item* qwork;   // query-major items (magi_schedule)
+  int32_t num_qwork;
+  const int32_t* q_tile_slices;
+  int32_t num_q_tile_slices;
+  const magi_work_item* kwork;   // key-major items (magi_schedule_kv)
+  int32_t num_kwork;
+  const int32_t* k_tile_slices;
+  int32_t num_k_tile_slices;
+};
+
+hipError_t launch_ffa_bwd(const BwdArgs& a, hipStream_t stream);
+
 }  // namespace magi

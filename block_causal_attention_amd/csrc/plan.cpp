@@ -239,3 +239,101 @@ extern "C" int32_t magi_schedule(const magi_attn_slice* slices, int32_t num_slic
   }
   return ok();
 }
+
+namespace magi {
+namespace {
+constexpr int kKeysPerTile = 256;  // keys of one KV group per backward work item
+
+// Rows of slice s that see key k: [first, s.q_end).
+inline int64_t col_first(const magi_attn_slice& s, int64_t k) {
+  if (s.mask_type == MAGI_MASK_FULL) return s.q_start;
+  // causal, bottom-right aligned: row r sees k iff k < k_end - q_end + r + 1
+  return std::max<int64_t>(s.q_start, k - ((int64_t)s.k_end - (int64_t)s.q_end));
+}
+}  // namespace
+}  // namespace magi
+
+extern "C" int32_t magi_default_tile_k(int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype) {
+  const int32_t st = magi_default_tile_q(hq, hkv, head_dim, dtype);
+  return st < 0 ? st : kKeysPerTile;
+}
+
+extern "C" int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_slices, int64_t nq, int64_t nk,
+                                    int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype, int32_t tile_k,
+                                    magi_work_item* work, int32_t work_cap, int32_t* num_work,
+                                    int32_t* tile_slices, int32_t ts_cap, int32_t* num_tile_slices) {
+  if (num_work == nullptr || num_tile_slices == nullptr)
+    return fail(MAGI_ERR_INVALID_ARG, "num_work / num_tile_slices is NULL");
+  if (work_cap < 0 || ts_cap < 0) return fail(MAGI_ERR_INVALID_ARG, "negative capacity");
+  if ((work == nullptr) != (work_cap == 0) || (tile_slices == nullptr) != (ts_cap == 0))
+    return fail(MAGI_ERR_INVALID_ARG, "output array and capacity disagree (NULL needs cap 0)");
+  // the query-major size query validates the slices (ranges, types, overlap)
+  int32_t nw_q = 0, nts_q = 0;
+  const int32_t st = magi_schedule(slices, num_slices, nq, nk, hq, hkv, head_dim, dtype, 0, nullptr, 0, &nw_q,
+                                   nullptr, 0, &nts_q);
+  if (st < 0) return st;
+  const int32_t dflt = magi_default_tile_k(hq, hkv, head_dim, dtype);
+  if (dflt < 0) return dflt;
+  if (tile_k < 0 || tile_k > dflt)
+    return fail(MAGI_ERR_INVALID_ARG, "tile_k %d not in [0, %d] for this shape", tile_k, dflt);
+  if (tile_k == 0) tile_k = dflt;
+
+  // cut the key axis at every slice boundary
+  std::vector<int64_t> cuts = {0, nk};
+  for (int i = 0; i < num_slices; ++i)
+    if (slices[i].q_start < slices[i].q_end && slices[i].k_start < slices[i].k_end) {
+      cuts.push_back(slices[i].k_start);
+      cuts.push_back(slices[i].k_end);
+    }
+  std::sort(cuts.begin(), cuts.end());
+  cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+  const size_t nseg = cuts.size() - 1;
+  // slices that show some row a key of the segment, in query order
+  std::vector<std::vector<int32_t>> cover(nseg);
+  for (int i = 0; i < num_slices; ++i) {
+    const magi_attn_slice& s = slices[i];
+    if (s.q_start >= s.q_end || s.k_start >= s.k_end) continue;
+    size_t a = std::lower_bound(cuts.begin(), cuts.end(), (int64_t)s.k_start) - cuts.begin();
+    for (size_t g = a; g < nseg && cuts[g] < s.k_end; ++g)
+      if (col_first(s, cuts[g]) < s.q_end) cover[g].push_back(i);
+  }
+  for (auto& c : cover)
+    std::sort(c.begin(), c.end(), [&](int32_t x, int32_t y) {
+      return slices[x].q_start != slices[y].q_start ? slices[x].q_start < slices[y].q_start : x < y;
+    });
+
+  struct Tile { int64_t k0, len, cost; size_t seg; };
+  std::vector<Tile> tiles;
+  int64_t ts_total = 0;
+  for (size_t g = 0; g < nseg; ++g) {
+    for (int64_t t0 = cuts[g]; t0 < cuts[g + 1]; t0 += tile_k) {
+      const int64_t len = std::min<int64_t>(tile_k, cuts[g + 1] - t0);
+      int64_t cost = 0;
+      for (int32_t i : cover[g])
+        for (int64_t k = t0; k < t0 + len; ++k) cost += std::max<int64_t>(0, slices[i].q_end - col_first(slices[i], k));
+      tiles.push_back({t0, len, cost, g});
+      ts_total += (int64_t)cover[g].size();
+    }
+  }
+  const int64_t nwork = (int64_t)tiles.size() * hkv;
+  if (nwork > INT32_MAX || ts_total > INT32_MAX) return fail(MAGI_ERR_INVALID_ARG, "work list exceeds int32");
+  *num_work = (int32_t)nwork;
+  *num_tile_slices = (int32_t)ts_total;
+  if (work == nullptr && tile_slices == nullptr) return ok();
+  if (work_cap < nwork || ts_cap < ts_total)
+    return fail(MAGI_ERR_BUFFER_TOO_SMALL, "need work_cap >= %lld and ts_cap >= %lld", (long long)nwork,
+                (long long)ts_total);
+
+  std::vector<size_t> ord(tiles.size());
+  std::iota(ord.begin(), ord.end(), 0);
+  std::stable_sort(ord.begin(), ord.end(), [&](size_t x, size_t y) { return tiles[x].cost > tiles[y].cost; });
+  int32_t ts = 0, w = 0;
+  for (size_t rank = 0; rank < ord.size(); ++rank) {
+    const Tile& t = tiles[ord[rank]];
+    const int32_t sb = ts;
+    for (int32_t i : cover[t.seg]) tile_slices[ts++] = i;
+    for (int32_t g = 0; g < hkv; ++g)
+      work[w++] = {(int32_t)t.k0, (int32_t)t.len, sb, ts, g, (int32_t)std::min<int64_t>(t.cost, INT32_MAX)};
+  }
+  return ok();
+}

@@ -71,28 +71,40 @@ def default_tile_q(hq: int, hkv: int, head_dim: int, dtype: int) -> int:
     return check(lib().magi_default_tile_q(hq, hkv, head_dim, dtype))
 
 
-def schedule(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim: int, dtype: int,
-             tile_q: int = 0):
-    """magi_schedule: slices -> (work int32 [m, 6], tile_slices int32 [t])."""
+def _schedule(fn, dflt_fn, slices, nq, nk, hq, hkv, head_dim, dtype, tile):
     s = np.ascontiguousarray(np.asarray(slices, np.int32).reshape(-1, 5))
     sp = s.ctypes.data_as(C.POINTER(AttnSlice)) if len(s) else None
     nw, nt = C.c_int32(0), C.c_int32(0)
-    L = lib()
     # one call with capacities that fit the usual schedule; the exact sizes
     # come back with MAGI_ERR_BUFFER_TOO_SMALL otherwise
-    tq = tile_q if tile_q > 0 else max(default_tile_q(hq, hkv, head_dim, dtype), 1)
-    tiles = -(-nq // tq) + 2 * len(s) + 1
+    t = tile if tile > 0 else max(check(dflt_fn(hq, hkv, head_dim, dtype)), 1)
+    tiles = -(-max(nq, nk) // t) + 2 * len(s) + 1
     wcap, tcap = max(tiles * hkv, 1), max(tiles * min(max(len(s), 1), 8), 1)
     while True:
         work = np.empty((wcap, 6), np.int32)
         ts = np.empty(tcap, np.int32)
-        st = L.magi_schedule(sp, len(s), nq, nk, hq, hkv, head_dim, dtype, tile_q,
-                             work.ctypes.data_as(C.POINTER(WorkItem)), wcap, C.byref(nw),
-                             ts.ctypes.data_as(C.POINTER(C.c_int32)), tcap, C.byref(nt))
+        st = fn(sp, len(s), nq, nk, hq, hkv, head_dim, dtype, tile,
+                work.ctypes.data_as(C.POINTER(WorkItem)), wcap, C.byref(nw),
+                ts.ctypes.data_as(C.POINTER(C.c_int32)), tcap, C.byref(nt))
         if st != _lib.MAGI_ERR_BUFFER_TOO_SMALL:
             check(st)
             return work[:nw.value], ts[:nt.value]
         wcap, tcap = max(nw.value, 1), max(nt.value, 1)
+
+
+def schedule(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim: int, dtype: int,
+             tile_q: int = 0):
+    """magi_schedule: slices -> query-major (work int32 [m, 6], tile_slices int32 [t])."""
+    L = lib()
+    return _schedule(L.magi_schedule, L.magi_default_tile_q, slices, nq, nk, hq, hkv, head_dim, dtype, tile_q)
+
+
+def schedule_kv(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim: int, dtype: int,
+                tile_k: int = 0):
+    """magi_schedule_kv: slices -> key-major (work int32 [m, 6], tile_slices int32 [t])
+    for the backward's dK/dV pass (q_start/q_len of an item are its keys)."""
+    L = lib()
+    return _schedule(L.magi_schedule_kv, L.magi_default_tile_k, slices, nq, nk, hq, hkv, head_dim, dtype, tile_k)
 
 
 @dataclass
@@ -110,6 +122,8 @@ class Plan:
     tile_slices: torch.Tensor
     host: dict = field(default_factory=dict)
     ready: Optional[torch.cuda.Event] = None  # recorded after the upload; ffa_fwd waits on it
+    kwork: Optional[torch.Tensor] = None        # key-major lists (backward plans only)
+    k_tile_slices: Optional[torch.Tensor] = None
 
     @property
     def num_work(self) -> int:
@@ -117,13 +131,17 @@ class Plan:
 
 
 def make_plan(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim: int, dtype,
-              device="cuda", tile_q: int = 0) -> Plan:
-    """schedule + one upload: the three int32 lists travel in a single pinned
-    host-to-device copy and the plan holds views of it."""
+              device="cuda", tile_q: int = 0, backward: bool = False) -> Plan:
+    """schedule (+ schedule_kv when ``backward``) + one upload: the int32
+    lists travel in a single pinned host-to-device copy and the plan holds
+    views of it."""
     code = dtype if isinstance(dtype, int) else dtype_code(dtype)
     slices = np.asarray(slices, np.int32).reshape(-1, 5)
     work, ts = schedule(slices, nq, nk, hq, hkv, head_dim, code, tile_q)
     parts = [slices.reshape(-1), work.reshape(-1), ts.reshape(-1)]
+    if backward:
+        kwork, kts = schedule_kv(slices, nq, nk, hq, hkv, head_dim, code)
+        parts += [kwork.reshape(-1), kts.reshape(-1)]
     sizes = [max(p.size, 1) for p in parts]     # an empty list still gets one valid word
     host = torch.zeros(sum(sizes), dtype=torch.int32, pin_memory=True)
     hv = host.numpy()
@@ -141,9 +159,14 @@ def make_plan(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim:
         ready = torch.cuda.Event()
         ready.record(side)
     dev.record_stream(main)
-    o1, o2 = sizes[0], sizes[0] + sizes[1]
-    return Plan(nq, nk, hq, hkv, head_dim, code, dev[:o1], dev[o1:o2], dev[o2:],
-                {"slices": slices, "work": work, "tile_slices": ts}, ready)
+    offs = np.cumsum([0] + sizes)
+    views = [dev[offs[i]:offs[i + 1]] for i in range(len(parts))]
+    host_arrays = {"slices": slices, "work": work, "tile_slices": ts}
+    plan = Plan(nq, nk, hq, hkv, head_dim, code, views[0], views[1], views[2], host_arrays, ready)
+    if backward:
+        plan.kwork, plan.k_tile_slices = views[3], views[4]
+        host_arrays.update(kwork=kwork, k_tile_slices=kts)
+    return plan
 
 
 _UPLOAD_STREAMS = {}
@@ -160,9 +183,9 @@ def _upload_stream(device) -> torch.cuda.Stream:
 
 
 def plan_for_videos(seqs: Sequence, nq: int, nk: int, hq: int, hkv: int, head_dim: int, dtype,
-                    device="cuda", tile_q: int = 0) -> Plan:
-    """build_slices + schedule + upload."""
-    return make_plan(build_slices(seqs), nq, nk, hq, hkv, head_dim, dtype, device, tile_q)
+                    device="cuda", tile_q: int = 0, backward: bool = False) -> Plan:
+    """build_slices + schedule (+ schedule_kv) + upload."""
+    return make_plan(build_slices(seqs), nq, nk, hq, hkv, head_dim, dtype, device, tile_q, backward)
 
 
 def _check_3d(name, t, heads, d):
@@ -244,3 +267,44 @@ def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
         _ptr(plan.slices), int(plan.host["slices"].shape[0]), _ptr(plan.work), plan.num_work,
         _ptr(plan.tile_slices), int(plan.host["tile_slices"].shape[0]), _stream(q)))
     return out, lse
+
+
+def ffa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+            lse: torch.Tensor, plan: Plan, softmax_scale: Optional[float] = None,
+            dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+            dv: Optional[torch.Tensor] = None):
+    """magi_ffa_bwd over a backward ``plan`` (make_plan(..., backward=True));
+    returns (dq, dk, dv).  q, k, v, out, lse and softmax_scale are the
+    forward's; dout has the layout of out."""
+    d = q.shape[-1]
+    hq, hkv = q.shape[1], k.shape[1]
+    for name, t, heads in (("q", q, hq), ("k", k, hkv), ("v", v, hkv), ("out", out, hq), ("dout", dout, hq)):
+        _check_3d(name, t, heads, d)
+    if k.stride(0) != v.stride(0) or out.stride(0) != dout.stride(0):
+        raise ValueError("k/v and out/dout must share their row strides")
+    if plan.kwork is None:
+        raise ValueError("plan has no key-major lists: make it with backward=True")
+    if (plan.nq, plan.nk, plan.hq, plan.hkv, plan.head_dim, plan.dtype) != \
+            (q.shape[0], k.shape[0], hq, hkv, d, dtype_code(q.dtype)):
+        raise ValueError("plan was made for a different shape or dtype")
+    if lse.dtype != torch.float32 or lse.shape != (q.shape[0], hq) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [nq, hq]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype:
+            raise ValueError(f"{name} must match {name[1:]} in shape, strides and dtype")
+    delta = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
+    if plan.ready is not None:
+        torch.cuda.current_stream(q.device).wait_event(plan.ready)
+    H = plan.host
+    check(lib().magi_ffa_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
+        q.shape[0], k.shape[0], hq, hkv, d, dtype_code(q.dtype), q.stride(0), k.stride(0), out.stride(0),
+        0.0 if softmax_scale is None else float(softmax_scale),
+        _ptr(plan.slices), int(H["slices"].shape[0]), _ptr(plan.work), plan.num_work,
+        _ptr(plan.tile_slices), int(H["tile_slices"].shape[0]),
+        _ptr(plan.kwork), int(H["kwork"].shape[0]), _ptr(plan.k_tile_slices), int(H["k_tile_slices"].shape[0]),
+        _stream(q)))
+    return dq, dk, dv

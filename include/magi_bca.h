@@ -217,6 +217,73 @@ int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, void* out, flo
                      const int32_t* tile_slices, int32_t num_tile_slices,
                      void* stream);
 
+/*
+ * magi_default_tile_k -- keys per key-major work item that magi_ffa_bwd's
+ * dK/dV kernel is built for (256).  Returns < 0 on unsupported shapes.
+ */
+int32_t magi_default_tile_k(int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype);
+
+/*
+ * magi_schedule_kv -- AttnSlices -> key-major work list for the backward's
+ * dK/dV pass.                                                    [host only]
+ *
+ * The transpose of magi_schedule: validates the slices the same way, cuts
+ * the KEY axis at every slice boundary, tiles each piece into tiles of at
+ * most tile_k keys (0 = magi_default_tile_k) and emits one item per (tile,
+ * KV group), including tiles no row sees (their dK, dV are written as 0).
+ * In these items q_start / q_len hold the first key and the key count;
+ * [slice_begin, slice_end) indexes tile_slices, which lists the slices that
+ * show some row a key of the tile, in query order.  cost = visible pairs of
+ * the tile per head; order heaviest first with the KV groups interleaved.
+ * Arguments, size query and errors as magi_schedule.
+ */
+int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_slices,
+                         int64_t nq, int64_t nk, int32_t hq, int32_t hkv,
+                         int32_t head_dim, int32_t dtype, int32_t tile_k,
+                         magi_work_item* work, int32_t work_cap, int32_t* num_work,
+                         int32_t* tile_slices, int32_t ts_cap, int32_t* num_tile_slices);
+
+/*
+ * magi_ffa_bwd -- gradients of magi_ffa_fwd.              [device, async]
+ *
+ * The pages run the FFA kernels for training (study notes, "训练 Infra";
+ * interview, answer on MagiAttention) but state no backward; this is the
+ * chain rule of the forward's softmax attention over the same slices:
+ *   P = exp(scale q.k - LSE),  delta = rowsum(dout * out),
+ *   dS = P * (dout v^T - delta),
+ *   dq = scale dS k,  dk = scale dS^T q,  dv = P^T dout,
+ * with dk and dv summed over the query heads of each KV group.  No atomics
+ * and bitwise deterministic: a query-major pass (the forward's work list)
+ * writes dq, a key-major pass (magi_schedule_kv's list) writes dk and dv.
+ * bf16: bf16 MFMA products with fp32 accumulation; P and dS are rounded to
+ * bf16 for their products; the gradients are stored as bf16.  fp32: fp32
+ * arithmetic throughout.
+ *
+ * q, k, v, out, lse, softmax_scale: exactly the forward's inputs and
+ *              outputs (a forward run with softmax_scale = ln 2 on prescaled
+ *              keys has gradients with respect to those prescaled keys)
+ * dout         [device] [nq][hq][head_dim], row stride o_tok_stride
+ * dq           [device] out, layout of q (row stride q_tok_stride)
+ * dk, dv       [device] out, layout of k / v (row stride kv_tok_stride);
+ *              rows no query sees are written as 0
+ * delta        [device] fp32 [nq][hq] scratch the call fills first (caller
+ *              owned, no other contents needed)
+ * slices, qwork/q_tile_slices  the forward's schedule (magi_schedule)
+ * kwork/k_tile_slices          magi_schedule_kv's output for the same slices
+ * Supported: head_dim 24 or 48; hq % hkv == 0; hq/hkv <= 64;
+ * kv_tok_stride < 2^23.  Errors as magi_ffa_fwd.
+ */
+int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, float* delta,
+                     int64_t nq, int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
+                     int64_t q_tok_stride, int64_t kv_tok_stride, int64_t o_tok_stride,
+                     float softmax_scale, const magi_attn_slice* slices, int32_t num_slices,
+                     const magi_work_item* qwork, int32_t num_qwork,
+                     const int32_t* q_tile_slices, int32_t num_q_tile_slices,
+                     const magi_work_item* kwork, int32_t num_kwork,
+                     const int32_t* k_tile_slices, int32_t num_k_tile_slices,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

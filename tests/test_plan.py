@@ -23,7 +23,7 @@ def header_functions():
 def test_library_exports_every_header_symbol():
     L = _lib.lib()
     names = header_functions()
-    assert len(names) == 7, names
+    assert len(names) == 10, names
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -184,6 +184,77 @@ def test_schedule_fuzz_raw_slices(trial):
     arr = np.array(slices, np.int32).reshape(-1, 5)
     tq = int(rng.choice([0, 1, 5]))
     check_schedule(arr, nq, nk, G * hkv, hkv, 24, _lib.DTYPE_BF16, tile_q=min(tq, 256 // G))
+
+
+def check_schedule_kv(slices, nq, nk, hq, hkv, d, dtype=_lib.DTYPE_BF16, tile_k=0):
+    """Key-major schedule: every (key, group) owned once, each item's slice
+    list reproduces the mask's columns over its keys, costs are the visible
+    pairs, heaviest first with the groups interleaved, deterministic."""
+    work, ts = ops.schedule_kv(slices, nq, nk, hq, hkv, d, dtype, tile_k)
+    tk = tile_k or 256
+    owner = np.full((nk, hkv), -1)
+    sl = [tuple(int(x) for x in s) for s in slices]
+    full = oracle.slices_mask(sl, nq, nk) if nq * nk <= 4e7 else None
+    for i, (k0, kl, sb, se, g, cost) in enumerate(work):
+        assert 1 <= kl <= tk and 0 <= g < hkv and 0 <= sb <= se <= len(ts)
+        assert (owner[k0:k0 + kl, g] == -1).all(), "key owned twice"
+        owner[k0:k0 + kl, g] = i
+        mine = [sl[j] for j in ts[sb:se]]
+        assert [m[0] for m in mine] == sorted(m[0] for m in mine), "slices not in query order"
+        if full is not None:
+            sub = oracle.slices_mask(mine, nq, nk) if mine else np.zeros((nq, nk), bool)
+            np.testing.assert_array_equal(sub[:, k0:k0 + kl], full[:, k0:k0 + kl])
+            assert cost == min(int(sub[:, k0:k0 + kl].sum()), 2 ** 31 - 1)
+            for m in mine:   # every listed slice shows some row a key of the tile
+                assert oracle.slices_mask([m], nq, nk)[:, k0:k0 + kl].any()
+    assert (owner >= 0).all(), "a (key, group) has no owner"
+    assert (np.diff(work[::hkv, 5]) <= 0).all(), "not heaviest-first"
+    for r in range(len(work) // hkv):
+        np.testing.assert_array_equal(work[r * hkv:(r + 1) * hkv, 4], np.arange(hkv))
+    w2, ts2 = ops.schedule_kv(slices, nq, nk, hq, hkv, d, dtype, tile_k)
+    np.testing.assert_array_equal(w2, work)
+    np.testing.assert_array_equal(ts2, ts)
+    return work, ts
+
+
+@pytest.mark.parametrize("name", ["tiny", "magi4.5b", "varlen", "stream"])
+def test_schedule_kv_workloads(name):
+    wl = W.make_workload(name)
+    sl = ops.build_slices(wl.seqs)
+    work, _ = check_schedule_kv(sl, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim,
+                                _lib.DTYPE_FP32 if wl.dtype == "fp32" else _lib.DTYPE_BF16)
+    if wl.nq < 10000:
+        assert work[:, 5].astype(np.int64).sum() == int(oracle.video_mask(wl.seqs, wl.nq, wl.nk).sum()) * wl.hkv
+
+
+@pytest.mark.parametrize("trial", range(25))
+def test_schedule_kv_fuzz_raw_slices(trial):
+    rng = np.random.Generator(np.random.PCG64(900 + trial))
+    nq, nk = int(rng.integers(1, 120)), int(rng.integers(1, 120))
+    hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 3, 4, 16]))
+    slices = []
+    q = 0
+    while q < nq:
+        qe = min(nq, q + int(rng.integers(1, 30)))
+        if rng.random() < 0.8:
+            k = int(rng.integers(0, 5))
+            while k < nk:
+                ke = min(nk, k + int(rng.integers(1, 40)))
+                slices.append((q, qe, k, ke, int(rng.random() < 0.4)))
+                k = ke + int(rng.integers(0, 10))
+        q = qe + int(rng.integers(0, 4))
+    arr = np.array(slices, np.int32).reshape(-1, 5)
+    check_schedule_kv(arr, nq, nk, G * hkv, hkv, 24, _lib.DTYPE_BF16, tile_k=int(rng.choice([0, 1, 7, 64])))
+
+
+def test_schedule_kv_errors():
+    with pytest.raises(_lib.MagiError) as e:   # validated like magi_schedule
+        ops.schedule_kv(np.array([(0, 8, 0, 8, 1), (0, 8, 6, 12, 0)]), 8, 12, 16, 1, 24, 0)
+    assert e.value.status == _lib.MAGI_ERR_OVERLAP
+    with pytest.raises(_lib.MagiError) as e:
+        ops.schedule_kv(np.array([(0, 4, 0, 4, 0)]), 4, 4, 16, 1, 24, 0, tile_k=300)
+    assert e.value.status == _lib.MAGI_ERR_INVALID_ARG
 
 
 def test_schedule_causal_overlap_detection():
