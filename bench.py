@@ -92,6 +92,42 @@ def run_gpu(wl, steps, warmup, seed=0):
     return (t1 - t0) * 1e3 / steps, float(np.mean(kernel_ms)), plan.num_work
 
 
+def run_backward(wl, steps, warmup, seed=0):
+    """Backward of the attention (magi_ffa_bwd) after one forward on the
+    prologue's outputs; returns the average launch time in ms from HIP events
+    on the launching stream."""
+    import torch
+    import workloads as W
+    from block_causal_attention_amd import ops
+
+    dev = "cuda"
+    inp = W.make_inputs(wl, seed)
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    gq, gk, pq, pk = (t.to(dev) for t in (inp.gain_q, inp.gain_k, inp.pos_q, inp.pos_k))
+    base = torch.tensor(wl.rope_base, dtype=torch.float32, device=dev)
+    knm = torch.empty(wl.hkv, dtype=torch.float32, device=dev)
+    qh, kh = ops.qknorm_rope(q, k, gq, gk, pq, pk, base, wl.eps, k_scale=wl.softmax_scale * ops.LOG2E,
+                             k_norm_max=knm)
+    plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, q.dtype, dev, backward=True)
+    out, lse = ops.ffa_fwd(qh, kh, v, plan, softmax_scale=ops.LN2, k_norm_max=knm)
+    g = torch.Generator(device="cpu").manual_seed(seed + 1)
+    dout = torch.randn(out.shape, generator=g).to(out.dtype).to(dev)
+    dq, dk, dv = torch.empty_like(qh), torch.empty_like(kh), torch.empty_like(v)
+    stream = torch.cuda.current_stream()
+    ev = []
+    for i in range(warmup + steps):
+        rec = i >= warmup
+        if rec:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+        ops.ffa_bwd(qh, kh, v, out, dout, lse, plan, softmax_scale=ops.LN2, dq=dq, dk=dk, dv=dv)
+        if rec:
+            b.record(stream)
+            ev.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
 def committed_traffic(wl_name: str):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary (profiles/traffic_<workload>.json), or None when the kernel
@@ -200,6 +236,17 @@ def main():
         rec["secondary"] = {"workload": wl2.name, "ms_per_step": round(s2, 4),
                             "value": round(f2 / (s2 * 1e-3) / 1e12, 2), "kernel_tflops": round(f2 / (k2 * 1e-3) / 1e12, 2),
                             "pct_of_bf16_peak": round(100.0 * f2 / (k2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    if not args.no_secondary:
+        # backward: 5 products of 2 d flops per visible pair and head
+        # (S recomputed, dP, dV, dK, dQ) = 2.5 x the forward's masked FLOPs
+        bwd = {}
+        for name in ("magi4.5b", "magi24b"):
+            w = W.make_workload(name)
+            kb = run_backward(w, 5 if name == "magi24b" else 10, 2)
+            fb = 2.5 * masked_flops(w)
+            bwd[name] = {"avg_launch_ms": round(kb, 4), "tflops": round(fb / (kb * 1e-3) / 1e12, 2),
+                         "pct_of_bf16_peak": round(100.0 * fb / (kb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        rec["backward"] = bwd
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(rec), flush=True)
