@@ -13,7 +13,7 @@
 // item owning its outputs (the page's FFA uses atomics on Hopper).
 //   * dQ pass: the forward's query-major work items (q tile x KV group) walk
 //     their K/V tiles and accumulate dQ^T in registers.
-//   * dK/dV pass: key-major items (256 keys x KV group, magi_schedule_kv)
+//   * dK/dV pass: key-major items (128 keys x KV group, magi_schedule_kv)
 //     walk the query rows that see their keys, 64 rows (tokens x heads of
 //     the group) at a time, and accumulate dK^T and dV^T in registers; the
 //     GQA sum over the group's heads falls out because the heads are rows.
@@ -41,8 +41,9 @@ namespace {
 using namespace dev;
 
 constexpr int kRows = 256;      // query rows per dQ work item (the forward's items)
-constexpr int kKeys = 256;      // keys per dK/dV work item (8 waves x 32)
-constexpr int NT = 512;         // threads per workgroup of both bf16 passes
+constexpr int kKeys = 128;      // keys per dK/dV work item (4 waves x 32)
+constexpr int NT = 512;         // threads per workgroup of the bf16 dQ pass
+constexpr int NTK = 2 * kKeys;  // threads per workgroup of the bf16 dK/dV pass
 constexpr int TK = 64;          // keys per K/V tile (dQ pass)
 constexpr int TQ = 64;          // query rows per Q/dO tile (dK/dV pass)
 constexpr int kThreads32 = 256;  // fp32 kernels
@@ -338,9 +339,9 @@ __device__ __forceinline__ bool find_qrun(const SliceLists& L, int32_t slice_end
 }
 
 template <int D, bool PRESCALED>
-__global__ __launch_bounds__(NT, 2) void bwd_dkdv_bf16(BwdArgs a) {
+__global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
   using C = BCfg<D>;
-  constexpr int NCH = (TQ * C::CH + NT - 1) / NT;  // 16-byte chunks per thread per tile (Q and dO each)
+  constexpr int NCH = (TQ * C::CH + NTK - 1) / NTK;  // 16-byte chunks per thread per tile (Q and dO each)
   __shared__ __attribute__((aligned(16))) __bf16 Qs[2][TQ * C::PITCH];
   __shared__ __attribute__((aligned(16))) __bf16 Os[2][TQ * C::PITCH];
 
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dkdv_bf16(BwdArgs a) {
   // zero padding columns D+2.. of both buffers once; columns D, D+1 are
   // rewritten with each tile's augmented values
   for (int b = 0; b < 2; ++b)
-    for (int i = tid; i < TQ * (C::DA - D - 2); i += NT) {
+    for (int i = tid; i < TQ * (C::DA - D - 2); i += NTK) {
       const int col = D + 2 + i % (C::DA - D - 2), row = i / (C::DA - D - 2);
       Qs[b][row * C::PITCH + col] = (__bf16)0.0f;
       Os[b][row * C::PITCH + col] = (__bf16)0.0f;
@@ -403,7 +404,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dkdv_bf16(BwdArgs a) {
     const int32_t ntok = r.t_end - r.t0 < TQT ? r.t_end - r.t0 : TQT;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int ci = tid + j * NT;
+      const int ci = tid + j * NTK;
       u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
       if (ci < TQ * C::CH) {
         const int row = ci / C::CH, part = ci % C::CH;
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dkdv_bf16(BwdArgs a) {
   auto store_tile = [&](int b) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int ci = tid + j * NT;
+      const int ci = tid + j * NTK;
       if (ci < TQ * C::CH) {
         const int row = ci / C::CH, part = ci % C::CH;
         *reinterpret_cast<u32x4*>(&Qs[b][row * C::PITCH + part * 8]) = qr[j];
@@ -707,9 +708,9 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
     if (!bf)
       hipLaunchKernelGGL((bwd_dkdv_f32<D>), grid, dim3(kThreads32), 0, stream, a);
     else if (pre)
-      hipLaunchKernelGGL((bwd_dkdv_bf16<D, true>), grid, dim3(NT), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_bf16<D, true>), grid, dim3(NTK), 0, stream, a);
     else
-      hipLaunchKernelGGL((bwd_dkdv_bf16<D, false>), grid, dim3(NT), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_bf16<D, false>), grid, dim3(NTK), 0, stream, a);
   }
   return hipGetLastError();
 }

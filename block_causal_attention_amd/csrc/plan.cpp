@@ -242,7 +242,7 @@ extern "C" int32_t magi_schedule(const magi_attn_slice* slices, int32_t num_slic
 
 namespace magi {
 namespace {
-constexpr int kKeysPerTile = 256;  // keys of one KV group per backward work item
+constexpr int kKeysPerTile = 128;  // keys of one KV group per backward work item
 
 // Rows of slice s that see key k: [first, s.q_end).
 inline int64_t col_first(const magi_attn_slice& s, int64_t k) {

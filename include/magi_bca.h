@@ -219,7 +219,7 @@ int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, void* out, flo
 
 /*
  * magi_default_tile_k -- keys per key-major work item that magi_ffa_bwd's
- * dK/dV kernel is built for (256).  Returns < 0 on unsupported shapes.
+ * dK/dV kernel is built for (128).  Returns < 0 on unsupported shapes.
  */
 int32_t magi_default_tile_k(int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype);
 

@@ -191,7 +191,7 @@ def check_schedule_kv(slices, nq, nk, hq, hkv, d, dtype=_lib.DTYPE_BF16, tile_k=
     list reproduces the mask's columns over its keys, costs are the visible
     pairs, heaviest first with the groups interleaved, deterministic."""
     work, ts = ops.schedule_kv(slices, nq, nk, hq, hkv, d, dtype, tile_k)
-    tk = tile_k or 256
+    tk = tile_k or 128
     owner = np.full((nk, hkv), -1)
     sl = [tuple(int(x) for x in s) for s in slices]
     full = oracle.slices_mask(sl, nq, nk) if nq * nk <= 4e7 else None
@@ -253,7 +253,7 @@ def test_schedule_kv_errors():
         ops.schedule_kv(np.array([(0, 8, 0, 8, 1), (0, 8, 6, 12, 0)]), 8, 12, 16, 1, 24, 0)
     assert e.value.status == _lib.MAGI_ERR_OVERLAP
     with pytest.raises(_lib.MagiError) as e:
-        ops.schedule_kv(np.array([(0, 4, 0, 4, 0)]), 4, 4, 16, 1, 24, 0, tile_k=300)
+        ops.schedule_kv(np.array([(0, 4, 0, 4, 0)]), 4, 4, 16, 1, 24, 0, tile_k=200)
     assert e.value.status == _lib.MAGI_ERR_INVALID_ARG
 
 
