@@ -128,6 +128,56 @@ def run_backward(wl, steps, warmup, seed=0):
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
+TEXT_TOKENS = 800  # condition tokens per sample for the cross-attention record
+
+
+def run_cross(wl, steps, warmup, seed=0):
+    """Cross-attention of the parallel block: the workload's video tokens over
+    TEXT_TOKENS condition tokens (one sample), QK-Norm on both sides without
+    rotation, then FFA over the cross slice.  Returns (ms per step, kernel ms)."""
+    import torch
+    from block_causal_attention_amd import ops
+
+    dev = "cuda"
+    g = torch.Generator(device="cpu").manual_seed(seed + 7)
+    mk = lambda *shape: torch.randn(shape, generator=g).to(torch.bfloat16).to(dev)
+    q, k, v = mk(wl.nq, wl.hq, wl.head_dim), mk(TEXT_TOKENS, wl.hkv, wl.head_dim), mk(TEXT_TOKENS, wl.hkv, wl.head_dim)
+    gq = (0.8 + 0.4 * torch.rand(wl.head_dim, generator=g)).to(dev)
+    gk = (0.8 + 0.4 * torch.rand(wl.head_dim, generator=g)).to(dev)
+    zq = torch.zeros((wl.nq, 3), dtype=torch.int32, device=dev)
+    zk = torch.zeros((TEXT_TOKENS, 3), dtype=torch.int32, device=dev)
+    base = torch.tensor(wl.rope_base, dtype=torch.float32, device=dev)
+    qh, kh = torch.empty_like(q), torch.empty_like(k)
+    knm = torch.empty(wl.hkv, dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(record):
+        sl = ops.build_cross_slices([(0, wl.nq, 0, TEXT_TOKENS)])
+        plan = ops.make_plan(sl, wl.nq, TEXT_TOKENS, wl.hq, wl.hkv, wl.head_dim, q.dtype, dev)
+        ops.qknorm_rope(q, k, gq, gk, zq, zk, base, wl.eps, q_out=qh, k_out=kh,
+                        k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm)
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+        ops.ffa_fwd(qh, kh, v, plan, out=out, lse=lse, softmax_scale=ops.LN2, k_norm_max=knm)
+        if record:
+            b.record(stream)
+            ev.append((a, b))
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
 def committed_traffic(wl_name: str):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary (profiles/traffic_<workload>.json), or None when the kernel
@@ -247,6 +297,14 @@ def main():
             bwd[name] = {"avg_launch_ms": round(kb, 4), "tflops": round(fb / (kb * 1e-3) / 1e12, 2),
                          "pct_of_bf16_peak": round(100.0 * fb / (kb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
         rec["backward"] = bwd
+        cross = {}
+        for name in ("magi4.5b", "magi24b"):
+            w = W.make_workload(name)
+            ms_s, ms_k = run_cross(w, 10, 3)
+            fc = 4.0 * w.head_dim * w.hq * w.nq * TEXT_TOKENS
+            cross[name] = {"text_tokens": TEXT_TOKENS, "ms_per_step": round(ms_s, 4), "avg_launch_ms": round(ms_k, 4),
+                           "kernel_tflops": round(fc / (ms_k * 1e-3) / 1e12, 2)}
+        rec["cross_attention"] = cross
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(rec), flush=True)

@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "MAGI_OK", -1: "MAGI_ERR_INVALID_ARG", -2: "MAGI_ERR_UNSUPPOR
 
 EXPORTS = ("magi_version", "magi_last_error", "magi_slices_build", "magi_default_tile_q",
            "magi_schedule", "magi_qknorm_rope", "magi_ffa_fwd", "magi_default_tile_k",
-           "magi_schedule_kv", "magi_ffa_bwd")
+           "magi_schedule_kv", "magi_ffa_bwd", "magi_slices_cross")
 
 
 class AttnSlice(C.Structure):
@@ -37,6 +37,10 @@ class AttnSlice(C.Structure):
 class WorkItem(C.Structure):
     _fields_ = [("q_start", C.c_int32), ("q_len", C.c_int32), ("slice_begin", C.c_int32),
                 ("slice_end", C.c_int32), ("kv_group", C.c_int32), ("cost", C.c_int32)]
+
+
+class CrossDesc(C.Structure):
+    _fields_ = [("q_offset", C.c_int32), ("q_len", C.c_int32), ("k_offset", C.c_int32), ("k_len", C.c_int32)]
 
 
 class SeqDesc(C.Structure):
@@ -74,11 +78,13 @@ def lib() -> C.CDLL:
         L.magi_ffa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i64, i64, i64,
                                    C.c_float, vp, vp, i32, vp, i32, vp, i32, vp]
         L.magi_default_tile_k.argtypes = [i32, i32, i32, i32]
+        L.magi_slices_cross.argtypes = [C.POINTER(CrossDesc), i32, C.POINTER(AttnSlice), i32, C.POINTER(i32)]
         L.magi_schedule_kv.argtypes = L.magi_schedule.argtypes
         L.magi_ffa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32,
                                    i64, i64, i64, C.c_float, vp, i32, vp, i32, vp, i32, vp, i32, vp, i32, vp]
         for name in ("magi_slices_build", "magi_default_tile_q", "magi_schedule", "magi_qknorm_rope",
-                     "magi_ffa_fwd", "magi_default_tile_k", "magi_schedule_kv", "magi_ffa_bwd"):
+                     "magi_ffa_fwd", "magi_default_tile_k", "magi_schedule_kv", "magi_ffa_bwd",
+                     "magi_slices_cross"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib

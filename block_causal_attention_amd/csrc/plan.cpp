@@ -337,3 +337,39 @@ extern "C" int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_s
   }
   return ok();
 }
+
+extern "C" int32_t magi_slices_cross(const magi_cross_desc* descs, int32_t num_descs, magi_attn_slice* slices,
+                                     int32_t slice_cap, int32_t* num_slices) {
+  if (num_slices == nullptr) return fail(MAGI_ERR_INVALID_ARG, "num_slices is NULL");
+  if (num_descs < 0) return fail(MAGI_ERR_INVALID_ARG, "num_descs < 0");
+  if (num_descs > 0 && descs == nullptr) return fail(MAGI_ERR_INVALID_ARG, "descs is NULL");
+  if (slice_cap < 0) return fail(MAGI_ERR_INVALID_ARG, "slice_cap < 0");
+  if (slices == nullptr && slice_cap != 0) return fail(MAGI_ERR_INVALID_ARG, "slices is NULL but slice_cap > 0");
+  struct Span { int64_t a, b; int idx; };
+  std::vector<Span> qs;
+  int32_t need = 0;
+  for (int i = 0; i < num_descs; ++i) {
+    const magi_cross_desc& d = descs[i];
+    if (d.q_offset < 0 || d.k_offset < 0 || d.q_len < 0 || d.k_len < 0)
+      return fail(MAGI_ERR_INVALID_ARG, "sample %d: negative offset or length", i);
+    if ((int64_t)d.q_offset + d.q_len > INT32_MAX || (int64_t)d.k_offset + d.k_len > INT32_MAX)
+      return fail(MAGI_ERR_INVALID_ARG, "sample %d: ranges exceed int32", i);
+    if (d.q_len == 0 || d.k_len == 0) continue;
+    qs.push_back({d.q_offset, (int64_t)d.q_offset + d.q_len, i});
+    ++need;
+  }
+  std::sort(qs.begin(), qs.end(), [](const Span& x, const Span& y) { return x.a < y.a; });
+  for (size_t j = 1; j < qs.size(); ++j)
+    if (qs[j].a < qs[j - 1].b)
+      return fail(MAGI_ERR_OVERLAP, "samples %d and %d overlap in the query index space", qs[j - 1].idx, qs[j].idx);
+  *num_slices = need;
+  if (slices == nullptr && slice_cap == 0) return ok();
+  if (slice_cap < need) return fail(MAGI_ERR_BUFFER_TOO_SMALL, "slice_cap %d < %d", slice_cap, need);
+  int32_t n = 0;
+  for (int i = 0; i < num_descs; ++i) {
+    const magi_cross_desc& d = descs[i];
+    if (d.q_len == 0 || d.k_len == 0) continue;
+    slices[n++] = {d.q_offset, d.q_offset + d.q_len, d.k_offset, d.k_offset + d.k_len, MAGI_MASK_FULL};
+  }
+  return ok();
+}

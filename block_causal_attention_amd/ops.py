@@ -14,7 +14,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import AttnSlice, SeqDesc, WorkItem, check, lib
+from ._lib import AttnSlice, CrossDesc, SeqDesc, WorkItem, check, lib
 
 LN2 = 0.6931471805599453
 LOG2E = 1.4426950408889634
@@ -65,6 +65,20 @@ def build_slices(seqs: Sequence) -> np.ndarray:
             check(st)
             return out[:cnt.value]
         cap = cnt.value
+
+
+def build_cross_slices(samples: Sequence) -> np.ndarray:
+    """magi_slices_cross: samples (q_offset, q_len, k_offset, k_len) of a packed
+    cross-attention (video tokens over their own condition tokens) -> int32
+    [n, 5] FULL slices."""
+    n = len(samples)
+    descs = (CrossDesc * max(n, 1))()
+    for i, (qo, ql, ko, kl) in enumerate(samples):
+        descs[i] = CrossDesc(int(qo), int(ql), int(ko), int(kl))
+    cnt = C.c_int32(0)
+    out = np.empty((max(n, 1), 5), np.int32)
+    check(lib().magi_slices_cross(descs, n, out.ctypes.data_as(C.POINTER(AttnSlice)), out.shape[0], C.byref(cnt)))
+    return out[:cnt.value]
 
 
 def default_tile_q(hq: int, hkv: int, head_dim: int, dtype: int) -> int:

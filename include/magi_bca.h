@@ -79,6 +79,13 @@ typedef struct {
                               r >= 0 = the chunk sees itself and its r preceding chunks */
 } magi_seq_desc;
 
+/* One packed sample of a cross-attention: its video query rows and its
+ * condition (text) key rows. */
+typedef struct {
+  int32_t q_offset, q_len;  /* video tokens of the sample in the packed Q index space */
+  int32_t k_offset, k_len;  /* its condition tokens in the packed K index space */
+} magi_cross_desc;
+
 /* Library version string (static storage). */
 const char* magi_version(void);
 
@@ -102,6 +109,24 @@ const char* magi_last_error(void);
  * With slices == NULL and slice_cap == 0 this is a size query and returns MAGI_OK.
  */
 int32_t magi_slices_build(const magi_seq_desc* seqs, int32_t num_seqs,
+                          magi_attn_slice* slices, int32_t slice_cap, int32_t* num_slices);
+
+/*
+ * magi_slices_cross -- packed cross-attention mask -> AttnSlices.  [host only]
+ *
+ * The parallel attention block runs a cross-attention from the video tokens
+ * to the external condition (text) next to the block-causal self-attention,
+ * on the same query projection, with GQA at 128 heads over 8 groups (study
+ * notes, "自回归去噪 DiT", Parallel Attention Block bullet; "模型规格（Table 2）",
+ * Cross-Attn row).  Every video token of a sample sees every condition
+ * token of that sample and nothing else: one FULL slice
+ * q = [q_offset, q_offset + q_len), k = [k_offset, k_offset + k_len) per
+ * sample with both lengths > 0.  Query ranges must not overlap
+ * (MAGI_ERR_OVERLAP); samples may share key ranges.  Output, size query and
+ * errors as magi_slices_build; the slices feed magi_schedule / magi_ffa_fwd /
+ * magi_ffa_bwd unchanged.
+ */
+int32_t magi_slices_cross(const magi_cross_desc* descs, int32_t num_descs,
                           magi_attn_slice* slices, int32_t slice_cap, int32_t* num_slices);
 
 /*

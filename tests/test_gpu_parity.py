@@ -347,3 +347,32 @@ def test_packing_equals_separate_videos_gpu():
                              ops.plan_for_videos([one], s.nq, s.nk, 16, 2, 24, torch.bfloat16))
         torch.cuda.synchronize()
         assert torch.equal(Os, O[a:b]) and torch.equal(Ls, L[a:b])
+
+
+# --------------------------------------------------------------------------- cross-attention
+
+def test_cross_attention_packed_samples():
+    # the parallel block's cross-attention: each sample's video tokens see its
+    # own condition tokens (FULL slices from magi_slices_cross); QK-Norm on
+    # both sides and no rotation (zero positions), GQA 32/2, d = 24
+    note("cross-attention packed samples")
+    d, hq, hkv = 24, 32, 2
+    samples = [(0, 300, 0, 77), (300, 240, 77, 50)]
+    nq, nk = 540, 127
+    q, k, v = rand((nq, hq, d), 40), rand((nk, hkv, d), 41), rand((nk, hkv, d), 42)
+    gq = np.random.Generator(np.random.PCG64(43)).uniform(0.8, 1.2, d).astype(np.float32)
+    gk = np.random.Generator(np.random.PCG64(44)).uniform(0.8, 1.2, d).astype(np.float32)
+    qd, kd, vd = (torch.from_numpy(x).to(torch.bfloat16).to(DEV) for x in (q, k, v))
+    zq = torch.zeros((nq, 3), dtype=torch.int32, device=DEV)
+    zk = torch.zeros((nk, 3), dtype=torch.int32, device=DEV)
+    base = torch.tensor((1e4, 1e4, 1e4), dtype=torch.float32, device=DEV)
+    qh, kh = ops.qknorm_rope(qd, kd, torch.from_numpy(gq).to(DEV), torch.from_numpy(gk).to(DEV), zq, zk, base, 1e-6)
+    sl = ops.build_cross_slices(samples)
+    plan = ops.make_plan(sl, nq, nk, hq, hkv, d, torch.bfloat16)
+    O, L = ops.ffa_fwd(qh, kh, vd, plan)
+    torch.cuda.synchronize()
+    mask = oracle.slices_mask([tuple(int(x) for x in s) for s in sl], nq, nk)
+    Ow, Lw = oracle.forward(np64(qd), np64(kd), np64(vd), gq, gk, np.zeros((nq, 3)), np.zeros((nk, 3)),
+                            (1e4, 1e4, 1e4), 1e-6, mask, d ** -0.5)
+    compare(np64(O), Ow, "bf16")
+    compare(np64(L), Lw, "bf16", "LSE")

@@ -23,7 +23,7 @@ def header_functions():
 def test_library_exports_every_header_symbol():
     L = _lib.lib()
     names = header_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -369,3 +369,23 @@ def test_device_entry_points_validate_before_any_hip_call():
     assert ffa(nq=-2) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(nq=0, q=None, out=None) == _lib.MAGI_ERR_INVALID_ARG  # work for no rows
     assert b"work" in L.magi_last_error()
+
+
+def test_cross_slices():
+    # one FULL slice per sample with both lengths > 0, matching the dense
+    # "video rows of a sample see that sample's condition rows" mask
+    samples = [(0, 50, 0, 7), (50, 30, 7, 0), (80, 40, 7, 13), (120, 0, 20, 5), (120, 10, 0, 7)]
+    sl = ops.build_cross_slices(samples)
+    assert len(sl) == 3
+    m = oracle.slices_mask([tuple(int(x) for x in s) for s in sl], 130, 20)
+    want = np.zeros((130, 20), bool)
+    for qo, ql, ko, kl in samples:
+        want[qo:qo + ql, ko:ko + kl] = True
+    np.testing.assert_array_equal(m, want)
+    check_schedule(sl, 130, 20, 16, 1, 24)
+    with pytest.raises(_lib.MagiError) as e:
+        ops.build_cross_slices([(0, 10, 0, 5), (5, 10, 5, 5)])
+    assert e.value.status == _lib.MAGI_ERR_OVERLAP
+    with pytest.raises(_lib.MagiError) as e:
+        ops.build_cross_slices([(0, -1, 0, 5)])
+    assert e.value.status == _lib.MAGI_ERR_INVALID_ARG
