@@ -178,6 +178,67 @@ def run_cross(wl, steps, warmup, seed=0):
     return (t1 - t0) * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
+def run_ring(steps, warmup, seed=0):
+    """One streaming step over a ring-buffer KV cache at the streaming
+    workload's shape (chunks of 3600 tokens = 6 x 24x25, 128/8 heads, d=48):
+    24 chunk slots holding global chunks 100..123, the newest 4 in flight
+    (so the ring wraps).  A step = slices of the ring + schedule + upload,
+    the prologue on the in-flight queries and on the in-flight keys written
+    straight into their ring slots, and FFA over the wrapped slices.
+    Returns (ms per step, kernel ms, masked FLOPs)."""
+    import torch
+    from block_causal_attention_amd import ops
+
+    C, S, first, count, n, hq, hkv, d = 3600, 24, 100, 24, 4, 128, 8, 48
+    dev = "cuda"
+    g = torch.Generator(device="cpu").manual_seed(seed + 11)
+    mk = lambda *shape: torch.randn(shape, generator=g).to(torch.bfloat16).to(dev)
+    ring_k, ring_v = mk(S * C, hkv, d), mk(S * C, hkv, d)   # cached chunks: already processed
+    q, knew = mk(n * C, hq, d), mk(n * C, hkv, d)
+    gq = (0.8 + 0.4 * torch.rand(d, generator=g)).to(dev)
+    gk = (0.8 + 0.4 * torch.rand(d, generator=g)).to(dev)
+    pos = torch.randint(0, 24, (n * C, 3), generator=g, dtype=torch.int32).to(dev)
+    base = torch.tensor((1e4, 1e4, 1e4), dtype=torch.float32, device=dev)
+    qh = torch.empty_like(q)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], hq, dtype=torch.float32, device=dev)
+    scale = d ** -0.5
+    stream = torch.cuda.current_stream()
+    runs = ops.ring_slot_runs(S, first + count - n, n)
+    ev = []
+    visible = 0
+
+    def step(record):
+        nonlocal visible
+        sl = ops.build_ring_slices(C, S, first, count, n)
+        visible = int(((sl[:, 1] - sl[:, 0]).astype(np.int64) * (sl[:, 3] - sl[:, 2])).sum())
+        plan = ops.make_plan(sl, n * C, S * C, hq, hkv, d, q.dtype, dev)
+        done = 0
+        for s0, m in runs:   # in-flight keys into their slots (the ring wraps at most once)
+            ops.qknorm_rope(q[:1] if done else q, knew[done * C:(done + m) * C], gq, gk,
+                            pos[:1] if done else pos, pos[done * C:(done + m) * C], base, 1e-6,
+                            q_out=qh[:1] if done else qh, k_out=ring_k[s0 * C:(s0 + m) * C],
+                            k_scale=scale * ops.LOG2E)
+            done += m
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+        ops.ffa_fwd(qh, ring_k, ring_v, plan, out=out, lse=lse, softmax_scale=ops.LN2)
+        if record:
+            b.record(stream)
+            ev.append((a, b))
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev])), 4.0 * d * hq * visible
+
+
 def committed_traffic(wl_name: str):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary (profiles/traffic_<workload>.json), or None when the kernel
@@ -305,6 +366,10 @@ def main():
             cross[name] = {"text_tokens": TEXT_TOKENS, "ms_per_step": round(ms_s, 4), "avg_launch_ms": round(ms_k, 4),
                            "kernel_tflops": round(fc / (ms_k * 1e-3) / 1e12, 2)}
         rec["cross_attention"] = cross
+        ms_s, ms_k, fr = run_ring(5, 2)
+        rec["streaming_ring"] = {"shape": "4 in-flight x 3600 queries over a 24-slot ring (86400 keys), 128/8, d=48",
+                                 "ms_per_step": round(ms_s, 4), "avg_launch_ms": round(ms_k, 4),
+                                 "kernel_tflops": round(fr / (ms_k * 1e-3) / 1e12, 2)}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(rec), flush=True)

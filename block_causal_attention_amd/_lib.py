@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "MAGI_OK", -1: "MAGI_ERR_INVALID_ARG", -2: "MAGI_ERR_UNSUPPOR
 
 EXPORTS = ("magi_version", "magi_last_error", "magi_slices_build", "magi_default_tile_q",
            "magi_schedule", "magi_qknorm_rope", "magi_ffa_fwd", "magi_default_tile_k",
-           "magi_schedule_kv", "magi_ffa_bwd", "magi_slices_cross")
+           "magi_schedule_kv", "magi_ffa_bwd", "magi_slices_cross", "magi_slices_ring")
 
 
 class AttnSlice(C.Structure):
@@ -37,6 +37,12 @@ class AttnSlice(C.Structure):
 class WorkItem(C.Structure):
     _fields_ = [("q_start", C.c_int32), ("q_len", C.c_int32), ("slice_begin", C.c_int32),
                 ("slice_end", C.c_int32), ("kv_group", C.c_int32), ("cost", C.c_int32)]
+
+
+class RingDesc(C.Structure):
+    _fields_ = [("chunk_len", C.c_int32), ("ring_slots", C.c_int32), ("first_chunk", C.c_int32),
+                ("num_chunks", C.c_int32), ("num_inflight", C.c_int32), ("q_offset", C.c_int32),
+                ("k_offset", C.c_int32), ("kv_range", C.POINTER(C.c_int32))]
 
 
 class CrossDesc(C.Structure):
@@ -79,12 +85,13 @@ def lib() -> C.CDLL:
                                    C.c_float, vp, vp, i32, vp, i32, vp, i32, vp]
         L.magi_default_tile_k.argtypes = [i32, i32, i32, i32]
         L.magi_slices_cross.argtypes = [C.POINTER(CrossDesc), i32, C.POINTER(AttnSlice), i32, C.POINTER(i32)]
+        L.magi_slices_ring.argtypes = [C.POINTER(RingDesc), C.POINTER(AttnSlice), i32, C.POINTER(i32)]
         L.magi_schedule_kv.argtypes = L.magi_schedule.argtypes
         L.magi_ffa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32,
                                    i64, i64, i64, C.c_float, vp, i32, vp, i32, vp, i32, vp, i32, vp, i32, vp]
         for name in ("magi_slices_build", "magi_default_tile_q", "magi_schedule", "magi_qknorm_rope",
                      "magi_ffa_fwd", "magi_default_tile_k", "magi_schedule_kv", "magi_ffa_bwd",
-                     "magi_slices_cross"):
+                     "magi_slices_cross", "magi_slices_ring"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib

@@ -373,3 +373,49 @@ extern "C" int32_t magi_slices_cross(const magi_cross_desc* descs, int32_t num_d
   }
   return ok();
 }
+
+extern "C" int32_t magi_slices_ring(const magi_ring_desc* d, magi_attn_slice* slices, int32_t slice_cap,
+                                    int32_t* num_slices) {
+  if (num_slices == nullptr || d == nullptr) return fail(MAGI_ERR_INVALID_ARG, "desc / num_slices is NULL");
+  if (slice_cap < 0) return fail(MAGI_ERR_INVALID_ARG, "slice_cap < 0");
+  if (slices == nullptr && slice_cap != 0) return fail(MAGI_ERR_INVALID_ARG, "slices is NULL but slice_cap > 0");
+  const int64_t C = d->chunk_len, S = d->ring_slots;
+  if (C < 1 || S < 1) return fail(MAGI_ERR_INVALID_ARG, "chunk_len and ring_slots must be >= 1");
+  if (d->first_chunk < 0) return fail(MAGI_ERR_INVALID_ARG, "first_chunk < 0");
+  if (d->num_chunks < 1 || d->num_chunks > S)
+    return fail(MAGI_ERR_INVALID_ARG, "num_chunks %d not in [1, ring_slots]", d->num_chunks);
+  if (d->num_inflight < 1 || d->num_inflight > d->num_chunks)
+    return fail(MAGI_ERR_INVALID_ARG, "num_inflight %d not in [1, num_chunks]", d->num_inflight);
+  if (d->q_offset < 0 || d->k_offset < 0) return fail(MAGI_ERR_INVALID_ARG, "negative offset");
+  if (d->q_offset + (int64_t)d->num_inflight * C > INT32_MAX || d->k_offset + S * C > INT32_MAX ||
+      (int64_t)d->first_chunk + d->num_chunks > INT32_MAX)
+    return fail(MAGI_ERR_INVALID_ARG, "ranges exceed int32");
+  if (d->kv_range)
+    for (int j = 0; j < d->num_inflight; ++j)
+      if (d->kv_range[j] < -1) return fail(MAGI_ERR_INVALID_ARG, "kv_range[%d] = %d < -1", j, d->kv_range[j]);
+  // chunk c lives in ring slot c mod S; in-flight chunk j is global chunk
+  // first_chunk + num_chunks - num_inflight + j and sees the chunks from
+  // max(first_chunk, c - r) to c, a run of slots that wraps at most once
+  struct Piece { int32_t q0, q1, k0, k1; };
+  std::vector<Piece> out;
+  const int64_t c_first = (int64_t)d->first_chunk + d->num_chunks - d->num_inflight;
+  for (int j = 0; j < d->num_inflight; ++j) {
+    const int64_t c = c_first + j;
+    const int32_t r = d->kv_range ? d->kv_range[j] : -1;
+    const int64_t lo = r < 0 ? d->first_chunk : std::max<int64_t>(d->first_chunk, c - r);
+    const int32_t q0 = (int32_t)(d->q_offset + j * C), q1 = (int32_t)(q0 + C);
+    const int64_t s_lo = lo % S, s_hi = c % S;
+    if (s_lo <= s_hi) {
+      out.push_back({q0, q1, (int32_t)(d->k_offset + s_lo * C), (int32_t)(d->k_offset + (s_hi + 1) * C)});
+    } else {
+      out.push_back({q0, q1, (int32_t)(d->k_offset + s_lo * C), (int32_t)(d->k_offset + S * C)});
+      out.push_back({q0, q1, (int32_t)d->k_offset, (int32_t)(d->k_offset + (s_hi + 1) * C)});
+    }
+  }
+  *num_slices = (int32_t)out.size();
+  if (slices == nullptr && slice_cap == 0) return ok();
+  if (slice_cap < (int32_t)out.size())
+    return fail(MAGI_ERR_BUFFER_TOO_SMALL, "slice_cap %d < %d", slice_cap, (int32_t)out.size());
+  for (size_t i = 0; i < out.size(); ++i) slices[i] = {out[i].q0, out[i].q1, out[i].k0, out[i].k1, MAGI_MASK_FULL};
+  return ok();
+}

@@ -14,7 +14,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import AttnSlice, CrossDesc, SeqDesc, WorkItem, check, lib
+from ._lib import AttnSlice, CrossDesc, RingDesc, SeqDesc, WorkItem, check, lib
 
 LN2 = 0.6931471805599453
 LOG2E = 1.4426950408889634
@@ -79,6 +79,36 @@ def build_cross_slices(samples: Sequence) -> np.ndarray:
     out = np.empty((max(n, 1), 5), np.int32)
     check(lib().magi_slices_cross(descs, n, out.ctypes.data_as(C.POINTER(AttnSlice)), out.shape[0], C.byref(cnt)))
     return out[:cnt.value]
+
+
+def build_ring_slices(chunk_len: int, ring_slots: int, first_chunk: int, num_chunks: int, num_inflight: int,
+                      kv_range=None, q_offset: int = 0, k_offset: int = 0) -> np.ndarray:
+    """magi_slices_ring: a streaming step over a ring-buffer KV cache -> int32
+    [n, 5] FULL slices (global chunk c in slot c mod ring_slots)."""
+    arr = None
+    if kv_range is not None:
+        arr = (C.c_int32 * max(len(kv_range), 1))(*[int(x) for x in kv_range])
+    desc = RingDesc(chunk_len, ring_slots, first_chunk, num_chunks, num_inflight, q_offset, k_offset,
+                    C.cast(arr, C.POINTER(C.c_int32)) if arr is not None else None)
+    cnt = C.c_int32(0)
+    out = np.empty((2 * max(num_inflight, 1), 5), np.int32)
+    check(lib().magi_slices_ring(C.byref(desc), out.ctypes.data_as(C.POINTER(AttnSlice)), out.shape[0],
+                                 C.byref(cnt)))
+    return out[:cnt.value]
+
+
+def ring_slot_runs(ring_slots: int, first: int, count: int):
+    """Contiguous slot runs [(slot0, n_chunks), ...] holding global chunks
+    first .. first + count - 1 (at most two: the ring wraps once)."""
+    runs = []
+    c = first
+    end = first + count
+    while c < end:
+        s0 = c % ring_slots
+        n = min(end - c, ring_slots - s0)
+        runs.append((s0, n))
+        c += n
+    return runs
 
 
 def default_tile_q(hq: int, hkv: int, head_dim: int, dtype: int) -> int:

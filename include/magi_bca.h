@@ -79,6 +79,25 @@ typedef struct {
                               r >= 0 = the chunk sees itself and its r preceding chunks */
 } magi_seq_desc;
 
+/* A KV cache kept as a ring of chunk slots for streaming generation.
+ * Global chunk c lives in slot c mod ring_slots, i.e. key rows
+ * [k_offset + (c mod ring_slots) * chunk_len, + chunk_len).  The ring holds
+ * global chunks [first_chunk, first_chunk + num_chunks); the newest
+ * num_inflight of them are being denoised and carry the queries, chunk j of
+ * them at query rows [q_offset + j * chunk_len, + chunk_len). */
+typedef struct {
+  int32_t chunk_len;       /* tokens per chunk, >= 1 */
+  int32_t ring_slots;      /* chunks the ring holds, >= num_chunks */
+  int32_t first_chunk;     /* global index of the oldest chunk in the ring, >= 0 */
+  int32_t num_chunks;      /* chunks present, 1..ring_slots */
+  int32_t num_inflight;    /* newest chunks carrying queries, 1..num_chunks */
+  int32_t q_offset;        /* first query row of in-flight chunk 0 */
+  int32_t k_offset;        /* first key row of slot 0 */
+  const int32_t* kv_range; /* [host] [num_inflight] or NULL: -1 = every chunk in the ring up to
+                              itself, r >= 0 = itself and its r preceding chunks (clipped to
+                              the ring) */
+} magi_ring_desc;
+
 /* One packed sample of a cross-attention: its video query rows and its
  * condition (text) key rows. */
 typedef struct {
@@ -110,6 +129,26 @@ const char* magi_last_error(void);
  */
 int32_t magi_slices_build(const magi_seq_desc* seqs, int32_t num_seqs,
                           magi_attn_slice* slices, int32_t slice_cap, int32_t* num_slices);
+
+/*
+ * magi_slices_ring -- streaming step over a ring-buffer KV cache ->
+ * AttnSlices.                                                    [host only]
+ *
+ * The pages cache the keys and values of denoised chunks and reuse them for
+ * new chunks, with up to 4 chunks in flight, a KV range that bounds the
+ * history a chunk sees (constant peak memory), and per-denoising-stage KV
+ * ranges for controllable transitions (study notes, "推理 Infra", KV Cache
+ * bullet; InfoQ article, inference paragraph).  A ring of ring_slots chunk
+ * slots holds exactly that history: the prologue writes each in-flight
+ * chunk's keys (and the caller its values) into the chunk's slot, and a
+ * chunk stays there once denoised until the ring wraps over it.  In-flight
+ * chunk c sees the chunks max(first_chunk, c - r) .. c: one FULL slice per
+ * contiguous run of their slots (two when the run wraps).  Per-stage KV
+ * ranges are simply this call's kv_range values.  Output, size query and
+ * errors as magi_slices_build.
+ */
+int32_t magi_slices_ring(const magi_ring_desc* desc, magi_attn_slice* slices, int32_t slice_cap,
+                         int32_t* num_slices);
 
 /*
  * magi_slices_cross -- packed cross-attention mask -> AttnSlices.  [host only]

@@ -376,3 +376,60 @@ def test_cross_attention_packed_samples():
                             (1e4, 1e4, 1e4), 1e-6, mask, d ** -0.5)
     compare(np64(O), Ow, "bf16")
     compare(np64(L), Lw, "bf16", "LSE")
+
+
+# --------------------------------------------------------------------------- streaming ring KV cache
+
+def test_streaming_step_over_ring_cache():
+    # ring of 6 chunk slots holding global chunks 4..9, chunks 7..9 in flight
+    # (slots 1..3 after wrapping) with per-chunk KV ranges 2, unlimited, 1.
+    # The prologue writes every chunk's keys straight into its slot (cached
+    # chunks in "earlier steps"); the oracle runs the same chunks laid out
+    # linearly, so the ring order of the keys must not matter
+    note("streaming step over a ring KV cache")
+    C, S, first, count, n = 48, 6, 4, 6, 3
+    d, hq, hkv = 24, 32, 2
+    kvr = [2, -1, 1]
+    nchunks = first + count
+    frames, gh, gw = 3, 4, 4
+    kraw, vraw = rand((nchunks * C, hkv, d), 50), rand((nchunks * C, hkv, d), 51)
+    qraw = rand((n * C, hq, d), 52)
+    gq = np.random.Generator(np.random.PCG64(53)).uniform(0.8, 1.2, d).astype(np.float32)
+    gk = np.random.Generator(np.random.PCG64(54)).uniform(0.8, 1.2, d).astype(np.float32)
+
+    def pos_of(c):   # (t, h, w) of chunk c's tokens: t continues across chunks
+        f, y, x = np.meshgrid(np.arange(frames), np.arange(gh), np.arange(gw), indexing="ij")
+        return np.stack([c * frames + f.ravel(), y.ravel(), x.ravel()], 1).astype(np.int32)
+
+    dv_ = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    base = torch.tensor((1e4, 1e4, 1e4), dtype=torch.float32, device=DEV)
+    gqd, gkd = dv_(gq), dv_(gk)
+    scale = d ** -0.5
+    ring_k = torch.zeros((S * C, hkv, d), dtype=torch.bfloat16, device=DEV)
+    ring_v = torch.zeros_like(ring_k)
+    for c in range(first, nchunks):
+        s = c % S
+        kc = dv_(kraw[c * C:(c + 1) * C]).to(torch.bfloat16)
+        # the prologue call needs a query tensor; one dummy row rides along
+        ops.qknorm_rope(dv_(qraw[:1]).to(torch.bfloat16), kc, gqd, gkd, dv_(np.zeros((1, 3), np.int32)),
+                        dv_(pos_of(c)), base, 1e-6, k_out=ring_k[s * C:(s + 1) * C], k_scale=scale * ops.LOG2E)
+        ring_v[s * C:(s + 1) * C] = dv_(vraw[c * C:(c + 1) * C]).to(torch.bfloat16)
+    qpos = np.concatenate([pos_of(c) for c in range(nchunks - n, nchunks)])
+    qd = dv_(qraw).to(torch.bfloat16)
+    qh, _ = ops.qknorm_rope(qd, None, gqd, None, dv_(qpos), None, base, 1e-6)
+    sl = ops.build_ring_slices(C, S, first, count, n, kvr)
+    plan = ops.make_plan(sl, n * C, S * C, hq, hkv, d, torch.bfloat16)
+    O, L = ops.ffa_fwd(qh, ring_k, ring_v, plan, softmax_scale=ops.LN2)
+    torch.cuda.synchronize()
+    # oracle: chunks first..nchunks-1 in linear order, the same windows
+    klin = np64(dv_(kraw[first * C:]).to(torch.bfloat16))
+    vlin = np64(dv_(vraw[first * C:]).to(torch.bfloat16))
+    kpos = np.concatenate([pos_of(c) for c in range(first, nchunks)])
+    mask = np.zeros((n * C, count * C), bool)
+    for j in range(n):
+        c = nchunks - n + j
+        lo = first if kvr[j] < 0 else max(first, c - kvr[j])
+        mask[j * C:(j + 1) * C, (lo - first) * C:(c + 1 - first) * C] = True
+    Ow, Lw = oracle.forward(np64(qd), klin, vlin, gq, gk, qpos, kpos, (1e4, 1e4, 1e4), 1e-6, mask, scale)
+    compare(np64(O), Ow, "bf16")
+    compare(np64(L), Lw, "bf16", "LSE")

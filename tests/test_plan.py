@@ -23,7 +23,7 @@ def header_functions():
 def test_library_exports_every_header_symbol():
     L = _lib.lib()
     names = header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -389,3 +389,31 @@ def test_cross_slices():
     with pytest.raises(_lib.MagiError) as e:
         ops.build_cross_slices([(0, -1, 0, 5)])
     assert e.value.status == _lib.MAGI_ERR_INVALID_ARG
+
+
+def test_ring_slices_match_chunk_windows():
+    # brute force: in-flight chunk c sees exactly the slots of chunks
+    # max(first, c - r) .. c of the ring, whatever the wrap
+    rng = np.random.Generator(np.random.PCG64(77))
+    for _ in range(200):
+        C, S = int(rng.integers(1, 5)), int(rng.integers(1, 9))
+        cnt = int(rng.integers(1, S + 1))
+        n = int(rng.integers(1, cnt + 1))
+        first = int(rng.integers(0, 20))
+        kvr = [int(x) for x in rng.integers(-1, 6, n)]
+        sl = ops.build_ring_slices(C, S, first, cnt, n, kvr, q_offset=3, k_offset=5)
+        nq, nk = 3 + n * C, 5 + S * C
+        m = oracle.slices_mask([tuple(int(x) for x in s) for s in sl], nq, nk)
+        want = np.zeros((nq, nk), bool)
+        for j in range(n):
+            c = first + cnt - n + j
+            lo = first if kvr[j] < 0 else max(first, c - kvr[j])
+            for cc in range(lo, c + 1):
+                s = cc % S
+                want[3 + j * C:3 + (j + 1) * C, 5 + s * C:5 + (s + 1) * C] = True
+        np.testing.assert_array_equal(m, want)
+    with pytest.raises(_lib.MagiError):
+        ops.build_ring_slices(4, 3, 0, 4, 1)          # more chunks than slots
+    with pytest.raises(_lib.MagiError):
+        ops.build_ring_slices(4, 3, 0, 3, 4)          # more in flight than present
+    assert ops.ring_slot_runs(6, 4, 6) == [(4, 2), (0, 4)]
