@@ -16,6 +16,7 @@ sample of the same workload on this host's cores.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -46,6 +47,9 @@ def visible_pairs(wl) -> int:
 
 def masked_flops(wl) -> float:
     return 4.0 * wl.head_dim * wl.hq * visible_pairs(wl)
+
+
+MIN_WARM_S = 0.5
 
 
 def run_gpu(wl, steps, warmup, seed=0):
@@ -80,14 +84,30 @@ def run_gpu(wl, steps, warmup, seed=0):
             ev.append((a, b))
         return plan
 
-    for _ in range(warmup):
+    # W untimed steps, and at least MIN_WARM_S of them: the shader clock of
+    # an idle GPU takes a few hundred ms of load to settle
+    t_w, i = time.perf_counter(), 0
+    while i < warmup or time.perf_counter() - t_w < MIN_WARM_S:
         step(False)
+        i += 1
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        plan = step(True)
+    # the first call after a long burst of launches pays the runtime's
+    # deferred clean-up of that burst (a few ms of host time); one more
+    # untimed step takes it, so the timed region starts in steady state
+    step(False)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    # as timeit does: no garbage-collection pass inside the timed region (a
+    # full pass over the warm-up's garbage can stall the host for ms)
+    gc.collect()
+    gc.disable()
+    try:
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            plan = step(True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    finally:
+        gc.enable()
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
     return (t1 - t0) * 1e3 / steps, float(np.mean(kernel_ms)), plan.num_work
 
@@ -288,8 +308,8 @@ def cpu_baseline(wl, target_s=15.0, seed=0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="magi4.5b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")

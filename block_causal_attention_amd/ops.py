@@ -187,21 +187,23 @@ def make_plan(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim:
         kwork, kts = schedule_kv(slices, nq, nk, hq, hkv, head_dim, code)
         parts += [kwork.reshape(-1), kts.reshape(-1)]
     sizes = [max(p.size, 1) for p in parts]     # an empty list still gets one valid word
-    host = torch.zeros(sum(sizes), dtype=torch.int32, pin_memory=True)
-    hv = host.numpy()
-    off = 0
-    for p, n in zip(parts, sizes):
-        hv[off:off + p.size] = p
-        off += n
     # The copy runs on a side stream so it does not queue behind the work
     # already on the caller's stream (the previous attention launch); only
     # ffa_fwd waits for it, through ``ready``.
     main = torch.cuda.current_stream(device)
     side = _upload_stream(main.device)
+    host, slot_done = _staging_slot(main.device, sum(sizes))
+    hv = host.numpy()
+    off = 0
+    for p, n in zip(parts, sizes):
+        hv[off:off + p.size] = p
+        off += n
     with torch.cuda.stream(side):
-        dev = host.to(device, non_blocking=True)
+        dev = torch.empty(sum(sizes), dtype=torch.int32, device=main.device)
+        dev.copy_(host, non_blocking=True)
         ready = torch.cuda.Event()
         ready.record(side)
+        slot_done.record(side)
     dev.record_stream(main)
     offs = np.cumsum([0] + sizes)
     views = [dev[offs[i]:offs[i + 1]] for i in range(len(parts))]
@@ -214,6 +216,32 @@ def make_plan(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim:
 
 
 _UPLOAD_STREAMS = {}
+_STAGING = {}
+_STAGING_SLOTS = 8  # plan uploads that may be in flight at once per device
+
+
+def _staging_slot(device, words: int):
+    """A pinned int32 staging buffer of at least ``words`` entries from a
+    fixed ring per device, and the event that marks its copy as done.
+
+    Allocating pinned memory per upload is slow and, when the host runs far
+    ahead of the GPU, turns every plan into a fresh pinned allocation.  The
+    ring reuses a slot once the copy that last read it has finished; when all
+    slots are still in flight the host waits for the oldest, which bounds how
+    far plan building runs ahead of the GPU."""
+    idx = torch.device(device).index
+    idx = torch.cuda.current_device() if idx is None else idx
+    ring = _STAGING.setdefault(idx, {"next": 0, "slots": [None] * _STAGING_SLOTS})
+    i = ring["next"]
+    ring["next"] = (i + 1) % _STAGING_SLOTS
+    slot = ring["slots"][i]
+    if slot is not None:
+        slot[1].synchronize()   # the copy that last read this slot has finished
+    if slot is None or slot[0].numel() < words:
+        cap = max(words, 2 * slot[0].numel() if slot is not None else 4096)
+        slot = (torch.empty(cap, dtype=torch.int32, pin_memory=True), torch.cuda.Event())
+        ring["slots"][i] = slot
+    return slot[0][:words], slot[1]
 
 
 def _upload_stream(device) -> torch.cuda.Stream:
