@@ -63,7 +63,10 @@ def run_gpu(wl, steps, warmup, seed=0):
     gq, gk, pq, pk = (t.to(dev) for t in (inp.gain_q, inp.gain_k, inp.pos_q, inp.pos_k))
     base = torch.tensor(wl.rope_base, dtype=torch.float32, device=dev)
     tdt = q.dtype
-    qh, kh = torch.empty_like(q), torch.empty_like(k)
+    # K and V reach the attention group-major (written so by the prologue)
+    qh = torch.empty_like(q)
+    kh = ops.kv_group_major(wl.nk, wl.hkv, wl.head_dim, tdt, dev)
+    vh = ops.kv_group_major(wl.nk, wl.hkv, wl.head_dim, tdt, dev)
     knm = torch.empty(wl.hkv, dtype=torch.float32, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
@@ -74,11 +77,11 @@ def run_gpu(wl, steps, warmup, seed=0):
         plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, tdt, dev)
         # the softmax scale (times log2 e) is folded into K by the prologue
         ops.qknorm_rope(q, k, gq, gk, pq, pk, base, wl.eps, q_out=qh, k_out=kh,
-                        k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm)
+                        k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm, v=v, v_out=vh)
         if record:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-        ops.ffa_fwd(qh, kh, v, plan, out=out, lse=lse, softmax_scale=ops.LN2, k_norm_max=knm)
+        ops.ffa_fwd(qh, kh, vh, plan, out=out, lse=lse, softmax_scale=ops.LN2, k_norm_max=knm)
         if record:
             b.record(stream)
             ev.append((a, b))
@@ -126,13 +129,14 @@ def run_backward(wl, steps, warmup, seed=0):
     gq, gk, pq, pk = (t.to(dev) for t in (inp.gain_q, inp.gain_k, inp.pos_q, inp.pos_k))
     base = torch.tensor(wl.rope_base, dtype=torch.float32, device=dev)
     knm = torch.empty(wl.hkv, dtype=torch.float32, device=dev)
-    qh, kh = ops.qknorm_rope(q, k, gq, gk, pq, pk, base, wl.eps, k_scale=wl.softmax_scale * ops.LOG2E,
-                             k_norm_max=knm)
+    qh, kh, vh = ops.qknorm_rope(q, k, gq, gk, pq, pk, base, wl.eps, k_scale=wl.softmax_scale * ops.LOG2E,
+                                 k_norm_max=knm, k_out=ops.kv_group_major(wl.nk, wl.hkv, wl.head_dim, q.dtype, dev),
+                                 v=v)
     plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, q.dtype, dev, backward=True)
-    out, lse = ops.ffa_fwd(qh, kh, v, plan, softmax_scale=ops.LN2, k_norm_max=knm)
+    out, lse = ops.ffa_fwd(qh, kh, vh, plan, softmax_scale=ops.LN2, k_norm_max=knm)
     g = torch.Generator(device="cpu").manual_seed(seed + 1)
     dout = torch.randn(out.shape, generator=g).to(out.dtype).to(dev)
-    dq, dk, dv = torch.empty_like(qh), torch.empty_like(kh), torch.empty_like(v)
+    dq, dk, dv = torch.empty_like(qh), torch.empty_like(kh), torch.empty_like(vh)
     stream = torch.cuda.current_stream()
     ev = []
     for i in range(warmup + steps):
@@ -140,7 +144,7 @@ def run_backward(wl, steps, warmup, seed=0):
         if rec:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-        ops.ffa_bwd(qh, kh, v, out, dout, lse, plan, softmax_scale=ops.LN2, dq=dq, dk=dk, dv=dv)
+        ops.ffa_bwd(qh, kh, vh, out, dout, lse, plan, softmax_scale=ops.LN2, dq=dq, dk=dk, dv=dv)
         if rec:
             b.record(stream)
             ev.append((a, b))
@@ -167,7 +171,9 @@ def run_cross(wl, steps, warmup, seed=0):
     zq = torch.zeros((wl.nq, 3), dtype=torch.int32, device=dev)
     zk = torch.zeros((TEXT_TOKENS, 3), dtype=torch.int32, device=dev)
     base = torch.tensor(wl.rope_base, dtype=torch.float32, device=dev)
-    qh, kh = torch.empty_like(q), torch.empty_like(k)
+    qh = torch.empty_like(q)
+    kh = ops.kv_group_major(TEXT_TOKENS, wl.hkv, wl.head_dim, q.dtype, dev)
+    vh = ops.kv_group_major(TEXT_TOKENS, wl.hkv, wl.head_dim, q.dtype, dev)
     knm = torch.empty(wl.hkv, dtype=torch.float32, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
@@ -178,11 +184,11 @@ def run_cross(wl, steps, warmup, seed=0):
         sl = ops.build_cross_slices([(0, wl.nq, 0, TEXT_TOKENS)])
         plan = ops.make_plan(sl, wl.nq, TEXT_TOKENS, wl.hq, wl.hkv, wl.head_dim, q.dtype, dev)
         ops.qknorm_rope(q, k, gq, gk, zq, zk, base, wl.eps, q_out=qh, k_out=kh,
-                        k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm)
+                        k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm, v=v, v_out=vh)
         if record:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-        ops.ffa_fwd(qh, kh, v, plan, out=out, lse=lse, softmax_scale=ops.LN2, k_norm_max=knm)
+        ops.ffa_fwd(qh, kh, vh, plan, out=out, lse=lse, softmax_scale=ops.LN2, k_norm_max=knm)
         if record:
             b.record(stream)
             ev.append((a, b))
@@ -213,7 +219,11 @@ def run_ring(steps, warmup, seed=0):
     dev = "cuda"
     g = torch.Generator(device="cpu").manual_seed(seed + 11)
     mk = lambda *shape: torch.randn(shape, generator=g).to(torch.bfloat16).to(dev)
-    ring_k, ring_v = mk(S * C, hkv, d), mk(S * C, hkv, d)   # cached chunks: already processed
+    # cached chunks (already processed), stored group-major like the prologue writes them
+    ring_k, ring_v = ops.kv_group_major(S * C, hkv, d, torch.bfloat16, dev), \
+        ops.kv_group_major(S * C, hkv, d, torch.bfloat16, dev)
+    ring_k.copy_(mk(S * C, hkv, d))
+    ring_v.copy_(mk(S * C, hkv, d))
     q, knew = mk(n * C, hq, d), mk(n * C, hkv, d)
     gq = (0.8 + 0.4 * torch.rand(d, generator=g)).to(dev)
     gk = (0.8 + 0.4 * torch.rand(d, generator=g)).to(dev)
@@ -353,7 +363,8 @@ def main():
         "data": "synthetic (seeded N(0,1) Q/K/V, U(0.8,1.2) QK-Norm gains; no weights)",
         "config": {"workload": wl.name, "description": wl.description, "tokens": wl.nq,
                    "query_heads": wl.hq, "kv_groups": wl.hkv, "head_dim": wl.head_dim,
-                   "masked_flops_per_step": flops, "work_items": nwork, "parallelism": "single GPU"},
+                   "masked_flops_per_step": flops, "work_items": nwork, "parallelism": "single GPU",
+                   "kv_layout": "group-major [hkv][nk][d], written by the prologue"},
         "pct_of_bf16_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

@@ -79,16 +79,18 @@ def lib() -> C.CDLL:
         L.magi_schedule.argtypes = [C.POINTER(AttnSlice), i32, i64, i64, i32, i32, i32, i32, i32,
                                     C.POINTER(WorkItem), i32, C.POINTER(i32), C.POINTER(i32), i32,
                                     C.POINTER(i32)]
-        L.magi_qknorm_rope.argtypes = [vp, vp, i64, i32, i64, vp, vp, i64, i32, i64, i32, i32,
-                                       vp, vp, i32, C.c_float, vp, vp, vp, C.c_float, C.c_float, vp, vp]
-        L.magi_ffa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i64, i64, i64,
+        L.magi_qknorm_rope.argtypes = [vp, vp, i64, i32, i64, vp, vp, i64, i32, i64, i64, i64, vp, vp,
+                                       i32, i32, vp, vp, i32, C.c_float, vp, vp, vp, C.c_float, C.c_float,
+                                       vp, vp]
+        L.magi_ffa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i64, i64, i64, i64,
                                    C.c_float, vp, vp, i32, vp, i32, vp, i32, vp]
         L.magi_default_tile_k.argtypes = [i32, i32, i32, i32]
         L.magi_slices_cross.argtypes = [C.POINTER(CrossDesc), i32, C.POINTER(AttnSlice), i32, C.POINTER(i32)]
         L.magi_slices_ring.argtypes = [C.POINTER(RingDesc), C.POINTER(AttnSlice), i32, C.POINTER(i32)]
         L.magi_schedule_kv.argtypes = L.magi_schedule.argtypes
         L.magi_ffa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32,
-                                   i64, i64, i64, C.c_float, vp, i32, vp, i32, vp, i32, vp, i32, vp, i32, vp]
+                                   i64, i64, i64, i64, C.c_float, vp, i32, vp, i32, vp, i32, vp, i32, vp, i32,
+                                   vp]
         for name in ("magi_slices_build", "magi_default_tile_q", "magi_schedule", "magi_qknorm_rope",
                      "magi_ffa_fwd", "magi_default_tile_k", "magi_schedule_kv", "magi_ffa_bwd",
                      "magi_slices_cross", "magi_slices_ring"):

@@ -24,25 +24,44 @@ int32_t check_common(int32_t head_dim, int32_t dtype) {
   return MAGI_OK;
 }
 
-int32_t check_tensor(const char* name, const void* p, int64_t n, int32_t heads, int64_t stride, int32_t head_dim,
-                     int32_t dtype) {
+// A tensor of n tokens x heads vectors of head_dim contiguous elements; the
+// vector of (token i, head h) starts at element i * tok_stride + h * head_stride.
+// Vectors must not overlap: either the heads of a token sit side by side
+// (head_stride >= head_dim, tok_stride >= heads * head_stride: token-major)
+// or the tokens of a head do (tok_stride >= head_dim, head_stride >=
+// n * tok_stride: group-major).
+int32_t check_layout(const char* name, const void* p, int64_t n, int32_t heads, int64_t tok_stride,
+                     int64_t head_stride, int32_t head_dim, int32_t dtype) {
   if (n < 0 || n > INT32_MAX) return fail(MAGI_ERR_INVALID_ARG, "%s: row count %lld not in [0, 2^31)", name, (long long)n);
   if (heads < 1) return fail(MAGI_ERR_INVALID_ARG, "%s: heads %d < 1", name, heads);
-  if (stride < (int64_t)heads * head_dim)
-    return fail(MAGI_ERR_INVALID_ARG, "%s: row stride %lld < heads*head_dim = %lld", name, (long long)stride,
-                (long long)heads * head_dim);
-  if ((stride * elem_size(dtype)) % 16)
-    return fail(MAGI_ERR_INVALID_ARG, "%s: row stride must be a multiple of 16 bytes", name);
+  const bool token_major = head_stride >= head_dim && tok_stride >= (int64_t)heads * head_stride;
+  const bool group_major = tok_stride >= head_dim && head_stride >= n * tok_stride;
+  if (!token_major && !group_major)
+    return fail(MAGI_ERR_INVALID_ARG,
+                "%s: strides (token %lld, head %lld) make vectors overlap (need token-major or group-major)", name,
+                (long long)tok_stride, (long long)head_stride);
+  if ((tok_stride * elem_size(dtype)) % 16 || (head_stride * elem_size(dtype)) % 16)
+    return fail(MAGI_ERR_INVALID_ARG, "%s: strides must be multiples of 16 bytes", name);
   if (n > 0 && p == nullptr) return fail(MAGI_ERR_INVALID_ARG, "%s is NULL", name);
   if (n > 0 && !aligned16(p)) return fail(MAGI_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
   return MAGI_OK;
+}
+
+// token-major with the heads of a token contiguous
+int32_t check_tensor(const char* name, const void* p, int64_t n, int32_t heads, int64_t stride, int32_t head_dim,
+                     int32_t dtype) {
+  if (stride < (int64_t)heads * head_dim)
+    return fail(MAGI_ERR_INVALID_ARG, "%s: row stride %lld < heads*head_dim = %lld", name, (long long)stride,
+                (long long)heads * head_dim);
+  return check_layout(name, p, n, heads, stride, head_dim, head_dim, dtype);
 }
 
 }  // namespace
 
 extern "C" int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, int32_t hq, int64_t q_tok_stride,
                                     const void* k_in, void* k_out, int64_t nk, int32_t hkv, int64_t k_tok_stride,
-                                    int32_t head_dim, int32_t dtype, const float* gain_q, const float* gain_k,
+                                    int64_t k_out_tok_stride, int64_t k_out_head_stride, const void* v_in,
+                                    void* v_out, int32_t head_dim, int32_t dtype, const float* gain_q, const float* gain_k,
                                     int32_t gain_head_stride, float eps, const int32_t* pos_q,
                                     const int32_t* pos_k, const float* rope_base, float q_scale, float k_scale,
                                     float* k_norm_max, void* stream) {
@@ -50,12 +69,25 @@ extern "C" int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, i
   if ((st = check_common(head_dim, dtype)) != MAGI_OK) return st;
   if ((st = check_tensor("q_in", q_in, nq, hq, q_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
   if ((st = check_tensor("q_out", q_out, nq, hq, q_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
+  if ((v_in == nullptr) != (v_out == nullptr)) return fail(MAGI_ERR_INVALID_ARG, "v_in and v_out go together");
   if (nk > 0) {
     if ((st = check_tensor("k_in", k_in, nk, hkv, k_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
-    if ((st = check_tensor("k_out", k_out, nk, hkv, k_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
+    if ((st = check_layout("k_out", k_out, nk, hkv, k_out_tok_stride, k_out_head_stride, head_dim, dtype)) != MAGI_OK)
+      return st;
+    if (k_out == k_in && (k_out_tok_stride != k_tok_stride || k_out_head_stride != head_dim))
+      return fail(MAGI_ERR_INVALID_ARG, "k_out may alias k_in only with the same layout");
+    if (v_in != nullptr) {
+      if ((st = check_tensor("v_in", v_in, nk, hkv, k_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
+      if ((st = check_layout("v_out", v_out, nk, hkv, k_out_tok_stride, k_out_head_stride, head_dim, dtype)) !=
+          MAGI_OK)
+        return st;
+      if (v_out == v_in) return fail(MAGI_ERR_INVALID_ARG, "v_out must not alias v_in");
+    }
     if (gain_k == nullptr || pos_k == nullptr) return fail(MAGI_ERR_INVALID_ARG, "gain_k / pos_k is NULL");
   } else if (nk < 0) {
     return fail(MAGI_ERR_INVALID_ARG, "nk < 0");
+  } else if (v_in != nullptr) {
+    return fail(MAGI_ERR_INVALID_ARG, "v_in needs K (nk > 0)");
   }
   if (nq > 0 && (gain_q == nullptr || pos_q == nullptr)) return fail(MAGI_ERR_INVALID_ARG, "gain_q / pos_q is NULL");
   if (gain_head_stride != 0 && gain_head_stride != head_dim)
@@ -66,8 +98,11 @@ extern "C" int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, i
     return fail(MAGI_ERR_INVALID_ARG, "q_scale and k_scale must be finite and non-zero");
 
   QkArgs a{};
-  a.side[0] = {q_in, q_out, nq, hq, q_tok_stride, gain_q, pos_q, q_scale};
-  a.side[1] = {k_in, k_out, nk > 0 ? nk : 0, nk > 0 ? hkv : 1, k_tok_stride, gain_k, pos_k, k_scale};
+  a.side[0] = {q_in, q_out, nq, hq, q_tok_stride, q_tok_stride, head_dim, gain_q, pos_q, q_scale};
+  a.side[1] = {k_in, k_out, nk > 0 ? nk : 0, nk > 0 ? hkv : 1, k_tok_stride, k_out_tok_stride, k_out_head_stride,
+               gain_k, pos_k, k_scale};
+  a.side[2] = {v_in, v_out, nk > 0 && v_in != nullptr ? nk : 0, nk > 0 ? hkv : 1, k_tok_stride, k_out_tok_stride,
+               k_out_head_stride, nullptr, nullptr, 1.0f};
   a.head_dim = head_dim;
   a.dtype = dtype;
   a.gain_head_stride = gain_head_stride;
@@ -85,8 +120,9 @@ extern "C" int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, i
 
 extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t nq,
                                 int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
-                                int64_t q_tok_stride, int64_t kv_tok_stride, int64_t o_tok_stride,
-                                float softmax_scale, const float* k_norm_max, const magi_attn_slice* slices,
+                                int64_t q_tok_stride, int64_t kv_tok_stride, int64_t kv_head_stride,
+                                int64_t o_tok_stride, float softmax_scale, const float* k_norm_max,
+                                const magi_attn_slice* slices,
                                 int32_t num_slices,
                                 const magi_work_item* work, int32_t num_work, const int32_t* tile_slices,
                                 int32_t num_tile_slices, void* stream) {
@@ -97,8 +133,8 @@ extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, voi
   if (hq / hkv > 256) return fail(MAGI_ERR_UNSUPPORTED, "group size %d > 256", hq / hkv);
   if ((st = check_tensor("q", q, nq, hq, q_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
   if ((st = check_tensor("out", out, nq, hq, o_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
-  if ((st = check_tensor("k", k, nk, hkv, kv_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
-  if ((st = check_tensor("v", v, nk, hkv, kv_tok_stride, head_dim, dtype)) != MAGI_OK) return st;
+  if ((st = check_layout("k", k, nk, hkv, kv_tok_stride, kv_head_stride, head_dim, dtype)) != MAGI_OK) return st;
+  if ((st = check_layout("v", v, nk, hkv, kv_tok_stride, kv_head_stride, head_dim, dtype)) != MAGI_OK) return st;
   // the kernel addresses one K/V tile with 32-bit byte offsets
   if (kv_tok_stride >= (int64_t)1 << 23)
     return fail(MAGI_ERR_UNSUPPORTED, "kv row stride %lld >= 2^23 elements", (long long)kv_tok_stride);
@@ -129,6 +165,7 @@ extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, voi
   a.dtype = dtype;
   a.q_stride = q_tok_stride;
   a.kv_stride = kv_tok_stride;
+  a.kv_hstride = kv_head_stride;
   a.o_stride = o_tok_stride;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   a.k_norm_max = dtype == MAGI_DTYPE_BF16 ? k_norm_max : nullptr;
@@ -146,9 +183,9 @@ extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, voi
 extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                                 const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t nq,
                                 int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
-                                int64_t q_tok_stride, int64_t kv_tok_stride, int64_t o_tok_stride,
-                                float softmax_scale, const magi_attn_slice* slices, int32_t num_slices,
-                                const magi_work_item* qwork, int32_t num_qwork, const int32_t* q_tile_slices,
+                                int64_t q_tok_stride, int64_t kv_tok_stride, int64_t kv_head_stride,
+                                int64_t o_tok_stride, float softmax_scale, const magi_attn_slice* slices,
+                                int32_t num_slices, const magi_work_item* qwork, int32_t num_qwork, const int32_t* q_tile_slices,
                                 int32_t num_q_tile_slices, const magi_work_item* kwork, int32_t num_kwork,
                                 const int32_t* k_tile_slices, int32_t num_k_tile_slices, void* stream) {
   int32_t st;
@@ -158,11 +195,12 @@ extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, con
   if (hq / hkv > 64) return fail(MAGI_ERR_UNSUPPORTED, "group size %d > 64", hq / hkv);
   const struct { const char* name; const void* p; int64_t n; int32_t heads; int64_t stride; } tensors[] = {
       {"q", q, nq, hq, q_tok_stride},        {"dq", dq, nq, hq, q_tok_stride},
-      {"out", out, nq, hq, o_tok_stride},    {"dout", dout, nq, hq, o_tok_stride},
-      {"k", k, nk, hkv, kv_tok_stride},      {"v", v, nk, hkv, kv_tok_stride},
-      {"dk", dk, nk, hkv, kv_tok_stride},    {"dv", dv, nk, hkv, kv_tok_stride}};
+      {"out", out, nq, hq, o_tok_stride},    {"dout", dout, nq, hq, o_tok_stride}};
   for (const auto& t : tensors)
     if ((st = check_tensor(t.name, t.p, t.n, t.heads, t.stride, head_dim, dtype)) != MAGI_OK) return st;
+  const struct { const char* name; const void* p; } kv[] = {{"k", k}, {"v", v}, {"dk", dk}, {"dv", dv}};
+  for (const auto& t : kv)
+    if ((st = check_layout(t.name, t.p, nk, hkv, kv_tok_stride, kv_head_stride, head_dim, dtype)) != MAGI_OK) return st;
   if (kv_tok_stride >= (int64_t)1 << 23)
     return fail(MAGI_ERR_UNSUPPORTED, "kv row stride %lld >= 2^23 elements", (long long)kv_tok_stride);
   if (nq > 0 && (lse == nullptr || delta == nullptr)) return fail(MAGI_ERR_INVALID_ARG, "lse and delta are required");
@@ -198,6 +236,7 @@ extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, con
   a.dtype = dtype;
   a.q_stride = q_tok_stride;
   a.kv_stride = kv_tok_stride;
+  a.kv_hstride = kv_head_stride;
   a.o_stride = o_tok_stride;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   a.slices = slices;

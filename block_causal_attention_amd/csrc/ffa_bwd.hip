@@ -164,7 +164,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
   }
   const int32_t kv_row_bytes = (int32_t)a.kv_stride * 2;
   auto load_tile = [&](int32_t kt, int32_t khi) {
-    const int64_t elem0 = (int64_t)kt * a.kv_stride + (int64_t)g * D;
+    const int64_t elem0 = (int64_t)kt * a.kv_stride + (int64_t)g * a.kv_hstride;
     const int32_t rows = khi - kt < TK ? khi - kt : TK;
     const int nrec = (rows - 1) * kv_row_bytes + D * 2;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kp + elem0), (short)0, nrec, kBufCfg);
@@ -378,8 +378,8 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
   bf16x8 kreg[C::KS], vreg[C::KS];
   {
     const int32_t kk = kvalid ? key : k0;
-    const __bf16* krow = reinterpret_cast<const __bf16*>(a.k) + (int64_t)kk * a.kv_stride + (int64_t)g * D;
-    const __bf16* vrow = reinterpret_cast<const __bf16*>(a.v) + (int64_t)kk * a.kv_stride + (int64_t)g * D;
+    const __bf16* krow = reinterpret_cast<const __bf16*>(a.k) + (int64_t)kk * a.kv_stride + (int64_t)g * a.kv_hstride;
+    const __bf16* vrow = reinterpret_cast<const __bf16*>(a.v) + (int64_t)kk * a.kv_stride + (int64_t)g * a.kv_hstride;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       const int d0 = 16 * ks + 8 * h;
@@ -539,8 +539,8 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
 
   // epilogue: lane (key) holds d = mb 32 + 8 grp + 4 h + r of dK^T / dV^T
   if (kvalid) {
-    __bf16* dkp = reinterpret_cast<__bf16*>(a.dk) + (int64_t)key * a.kv_stride + (int64_t)g * D;
-    __bf16* dvp = reinterpret_cast<__bf16*>(a.dv) + (int64_t)key * a.kv_stride + (int64_t)g * D;
+    __bf16* dkp = reinterpret_cast<__bf16*>(a.dk) + (int64_t)key * a.kv_stride + (int64_t)g * a.kv_hstride;
+    __bf16* dvp = reinterpret_cast<__bf16*>(a.dv) + (int64_t)key * a.kv_stride + (int64_t)g * a.kv_hstride;
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
@@ -598,8 +598,8 @@ __global__ __launch_bounds__(kThreads32) void bwd_dq_f32(BwdArgs a) {
       const int64_t ke = sl.k_end < a.nk ? sl.k_end : a.nk;
       const int64_t re = sl.mask_type == MAGI_MASK_CAUSAL ? causal_end(sl, ke, qi) : ke;
       for (int64_t kk = ks; kk < re; ++kk) {
-        const float* kr = kp + kk * a.kv_stride + (int64_t)g * D;
-        const float* vr = vp + kk * a.kv_stride + (int64_t)g * D;
+        const float* kr = kp + kk * a.kv_stride + (int64_t)g * a.kv_hstride;
+        const float* vr = vp + kk * a.kv_stride + (int64_t)g * a.kv_hstride;
         float s = 0.f, dpv = 0.f;
 #pragma unroll
         for (int i = 0; i < D; ++i) {
@@ -629,8 +629,8 @@ __global__ __launch_bounds__(kThreads32) void bwd_dkdv_f32(BwdArgs a) {
   if ((int)threadIdx.x >= klen) return;
   const int64_t key = (int64_t)wi.q_start + threadIdx.x;
   const int g = wi.kv_group;
-  const float* kr = reinterpret_cast<const float*>(a.k) + key * a.kv_stride + (int64_t)g * D;
-  const float* vr = reinterpret_cast<const float*>(a.v) + key * a.kv_stride + (int64_t)g * D;
+  const float* kr = reinterpret_cast<const float*>(a.k) + key * a.kv_stride + (int64_t)g * a.kv_hstride;
+  const float* vr = reinterpret_cast<const float*>(a.v) + key * a.kv_stride + (int64_t)g * a.kv_hstride;
   float kv[D], vv[D], dkacc[D], dvacc[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
@@ -673,8 +673,8 @@ __global__ __launch_bounds__(kThreads32) void bwd_dkdv_f32(BwdArgs a) {
         }
       }
   }
-  float* dkp = reinterpret_cast<float*>(a.dk) + key * a.kv_stride + (int64_t)g * D;
-  float* dvp = reinterpret_cast<float*>(a.dv) + key * a.kv_stride + (int64_t)g * D;
+  float* dkp = reinterpret_cast<float*>(a.dk) + key * a.kv_stride + (int64_t)g * a.kv_hstride;
+  float* dvp = reinterpret_cast<float*>(a.dv) + key * a.kv_stride + (int64_t)g * a.kv_hstride;
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     dkp[i] = dkacc[i] * a.scale;

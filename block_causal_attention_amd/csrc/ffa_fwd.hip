@@ -242,7 +242,7 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
     }
   };
   auto load_tile = [&](const TileRef& t, u32x4 (&kd)[NCH], u32x4 (&vd)[NCH]) {
-    const int64_t elem0 = (int64_t)t.kt * a.kv_stride + (int64_t)g * D;
+    const int64_t elem0 = (int64_t)t.kt * a.kv_stride + (int64_t)g * a.kv_hstride;
     const int32_t rows = t.geo.khi - t.kt < TK ? t.geo.khi - t.kt : TK;  // >= 1
     const int nrec = (rows - 1) * kv_row_bytes + D * 2;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kp + elem0), (short)0, nrec, kBufCfg);
@@ -508,8 +508,8 @@ __global__ __launch_bounds__(kThreads) void ffa_fwd_f32(FfaArgs a) {
     const int64_t ke = sl.k_end < a.nk ? sl.k_end : a.nk;
     const int64_t re = sl.mask_type == MAGI_MASK_CAUSAL ? causal_end(sl, ke, qi) : ke;
     for (int64_t key = ks; key < re; ++key) {
-      const float* kr = kp + key * a.kv_stride + (int64_t)g * D;
-      const float* vr = vp + key * a.kv_stride + (int64_t)g * D;
+      const float* kr = kp + key * a.kv_stride + (int64_t)g * a.kv_hstride;
+      const float* vr = vp + key * a.kv_stride + (int64_t)g * a.kv_hstride;
       float sdot = 0.f;
 #pragma unroll
       for (int i = 0; i < D; ++i) sdot = fmaf(qv[i], kr[i], sdot);

@@ -14,14 +14,15 @@ struct QkSide {
   void* out;
   int64_t n;           // tokens
   int32_t heads;
-  int64_t tok_stride;  // elements between consecutive tokens
-  const float* gain;
+  int64_t tok_stride;  // input: elements between consecutive tokens (heads contiguous)
+  int64_t out_tok_stride, out_head_stride;  // output layout
+  const float* gain;   // nullptr: plain copy into the output layout (V)
   const int32_t* pos;  // [n][3]
   float out_scale;     // factor applied to the result before it is stored
 };
 
 struct QkArgs {
-  QkSide side[2];  // Q, then K (side[1].n == 0 to skip)
+  QkSide side[3];  // Q, K, V (n == 0 to skip a side); V is only re-laid out
   float* k_norm_max;  // device [hkv] out: bound on the norm of every output key of a group, or nullptr
   int32_t head_dim;
   int32_t dtype;
@@ -41,6 +42,7 @@ struct FfaArgs {
   int64_t nq, nk;
   int32_t hq, hkv, head_dim, dtype;
   int64_t q_stride, kv_stride, o_stride;
+  int64_t kv_hstride;  // elements between consecutive KV heads of K and V
   float scale;
   const float* k_norm_max;  // device [hkv] upper bounds on key norms, or nullptr
   const magi_attn_slice* slices;
@@ -67,6 +69,7 @@ struct BwdArgs {
   int64_t nq, nk;
   int32_t hq, hkv, head_dim, dtype;
   int64_t q_stride, kv_stride, o_stride;
+  int64_t kv_hstride;  // elements between consecutive KV heads of K, V, dK, dV
   float scale;
   const magi_attn_slice* slices;
   int32_t num_slices;

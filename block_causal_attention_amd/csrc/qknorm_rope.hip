@@ -16,6 +16,11 @@
 // channel pair) is shared by all heads of a token, so it is built once per
 // token in LDS and every head of the token reads it.  Each thread then owns
 // one (token, head) vector and moves it with 16-byte loads and stores.
+//
+// Outputs have a layout of their own: token-major ([n][heads][d]) like the
+// inputs, or group-major ([heads][n][d]), where the attention reads each K/V
+// tile of a group as one contiguous block.  A third side moves V into K's
+// output layout unchanged, in the same launch.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -42,14 +47,15 @@ template <typename T>
 __device__ inline T from_f32(float x) { return (T)x; }
 
 template <int D, typename T>
-__global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(QkArgs a, int blocks_q) {
+__global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(QkArgs a, int end_q, int end_k) {
   constexpr int P = D / 2;   // channel pairs
   constexpr int PS = D / 6;  // pairs per axis section
   constexpr int PC = Vec<T>::kPerChunk;
   constexpr int CHUNKS = D / PC;
-  const int sidx = blockIdx.x < (unsigned)blocks_q ? 0 : 1;
+  // blocks [0, end_q) take Q, [end_q, end_k) K, the rest V
+  const int sidx = blockIdx.x < (unsigned)end_q ? 0 : (blockIdx.x < (unsigned)end_k ? 1 : 2);
   const QkSide& s = a.side[sidx];
-  const int b = sidx ? blockIdx.x - blocks_q : blockIdx.x;
+  const int b = blockIdx.x - (sidx == 0 ? 0 : (sidx == 1 ? end_q : end_k));
   const int tpb = s.heads >= kThreads ? 1 : kThreads / s.heads;  // tokens per block
   const int64_t tok0 = (int64_t)b * tpb;
   if (tok0 >= s.n) return;
@@ -70,6 +76,20 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(QkArgs a, int blo
 
   extern __shared__ float2 table[];  // [tpb][P] (cos, sin)
 
+  if (s.gain == nullptr) {
+    // V: the same rows, moved into the output layout
+    for (int v = threadIdx.x; v < ntok * s.heads; v += kThreads) {
+      const int t = v / s.heads, h = v % s.heads;
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(s.in) + (tok0 + t) * s.tok_stride +
+                                                        (int64_t)h * D);
+      uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<T*>(s.out) + (tok0 + t) * s.out_tok_stride +
+                                            (int64_t)h * s.out_head_stride);
+#pragma unroll
+      for (int c = 0; c < CHUNKS; ++c) dst[c] = src[c];
+    }
+    return;
+  }
+
   for (int i = threadIdx.x; i < ntok * P; i += kThreads) {
     const int t = i / P, p = i % P;
     const int axis = p / PS, j = p % PS;
@@ -86,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(QkArgs a, int blo
   for (int v = threadIdx.x; v < nvec; v += kThreads) {
     const int t = v / s.heads, h = v % s.heads;
     const T* src = reinterpret_cast<const T*>(s.in) + (tok0 + t) * s.tok_stride + (int64_t)h * D;
-    T* dst = reinterpret_cast<T*>(s.out) + (tok0 + t) * s.tok_stride + (int64_t)h * D;
+    T* dst = reinterpret_cast<T*>(s.out) + (tok0 + t) * s.out_tok_stride + (int64_t)h * s.out_head_stride;
     float x[D];
 #pragma unroll
     for (int c = 0; c < CHUNKS; ++c) {
@@ -123,19 +143,20 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(QkArgs a, int blo
 
 template <int D, typename T>
 hipError_t launch_typed(const QkArgs& a, hipStream_t stream) {
-  int blocks[2] = {0, 0};
+  int blocks[3] = {0, 0, 0};
   int tpb_max = 1;
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 3; ++i) {
     const QkSide& s = a.side[i];
     if (s.n == 0) continue;
     const int tpb = s.heads >= kThreads ? 1 : kThreads / s.heads;
     tpb_max = tpb > tpb_max ? tpb : tpb_max;
     blocks[i] = (int)((s.n + tpb - 1) / tpb);
   }
-  const int total = blocks[0] + blocks[1];
+  const int total = blocks[0] + blocks[1] + blocks[2];
   if (total == 0) return hipSuccess;
   const size_t lds = (size_t)tpb_max * (D / 2) * sizeof(float2);
-  hipLaunchKernelGGL((qknorm_rope_kernel<D, T>), dim3(total), dim3(kThreads), lds, stream, a, blocks[0]);
+  hipLaunchKernelGGL((qknorm_rope_kernel<D, T>), dim3(total), dim3(kThreads), lds, stream, a, blocks[0],
+                     blocks[0] + blocks[1]);
   return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@ LN2 = 0.6931471805599453
 LOG2E = 1.4426950408889634
 
 __all__ = ["build_slices", "schedule", "Plan", "make_plan", "plan_for_videos", "qknorm_rope",
-           "ffa_fwd", "default_tile_q", "dtype_code"]
+           "ffa_fwd", "ffa_bwd", "kv_group_major", "default_tile_q", "dtype_code"]
 
 
 def dtype_code(dt: torch.dtype) -> int:
@@ -260,23 +260,37 @@ def plan_for_videos(seqs: Sequence, nq: int, nk: int, hq: int, hkv: int, head_di
     return make_plan(build_slices(seqs), nq, nk, hq, hkv, head_dim, dtype, device, tile_q, backward)
 
 
-def _check_3d(name, t, heads, d):
+def _check_3d(name, t, heads, d, any_head_stride=False):
+    """[n, heads, d] on the GPU with contiguous channels; the heads of a token
+    must be contiguous too unless ``any_head_stride`` (K/V layouts, checked
+    for overlap by the library)."""
     if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != d:
         raise ValueError(f"{name}: expected [n, {heads}, {d}], got {list(t.shape)}")
-    if t.stride(2) != 1 or t.stride(1) != d:
+    if t.stride(2) != 1 or (t.stride(1) != d and not any_head_stride):
         raise ValueError(f"{name}: heads and channels must be contiguous (strides {t.stride()})")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+
+
+def kv_group_major(nk: int, hkv: int, d: int, dtype, device="cuda") -> torch.Tensor:
+    """An empty [nk, hkv, d] K or V tensor stored group-major ([hkv][nk][d]
+    underneath): each K/V tile of a group is then one contiguous block, which
+    the attention kernels load faster than the token-major layout."""
+    return torch.empty((hkv, nk, d), dtype=dtype, device=device).transpose(0, 1)
 
 
 def qknorm_rope(q: torch.Tensor, k: Optional[torch.Tensor], gain_q: torch.Tensor,
                 gain_k: Optional[torch.Tensor], pos_q: torch.Tensor, pos_k: Optional[torch.Tensor],
                 rope_base: torch.Tensor, eps: float = 1e-6, q_out: Optional[torch.Tensor] = None,
                 k_out: Optional[torch.Tensor] = None, q_scale: float = 1.0, k_scale: float = 1.0,
-                k_norm_max: Optional[torch.Tensor] = None):
+                k_norm_max: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None,
+                v_out: Optional[torch.Tensor] = None):
     """magi_qknorm_rope: QK-Norm then 3D RoPE (results times q_scale / k_scale);
-    returns (q_out, k_out).  ``k_norm_max`` (float32 [hkv], optional) receives
-    an upper bound on the norm of every output key of each head."""
+    returns (q_out, k_out), or (q_out, k_out, v_out) when ``v`` is given.
+    ``k_norm_max`` (float32 [hkv], optional) receives an upper bound on the
+    norm of every output key of each head.  ``k_out`` may be any [nk, hkv, d]
+    view with contiguous channels, e.g. kv_group_major(); ``v`` (laid out like
+    k) is then copied into ``v_out`` (default: a tensor laid out like k_out)."""
     d = q.shape[-1]
     _check_3d("q", q, q.shape[1], d)
     q_out = torch.empty_like(q) if q_out is None else q_out
@@ -287,12 +301,27 @@ def qknorm_rope(q: torch.Tensor, k: Optional[torch.Tensor], gain_q: torch.Tensor
     if gain_k is not None and gain_k.dim() != gain_q.dim():
         raise ValueError("gain_q and gain_k must both be shared [d] or both per head [heads, d]")
     nk, hkv, ks = 0, 1, q.shape[1] * d
+    kos, kohs = ks, d
     if k is not None:
         _check_3d("k", k, k.shape[1], d)
         k_out = torch.empty_like(k) if k_out is None else k_out
-        if k_out.stride(0) != k.stride(0):
-            raise ValueError("k and k_out must share the row stride")
+        _check_3d("k_out", k_out, k.shape[1], d, any_head_stride=True)
+        if k_out.shape != k.shape:
+            raise ValueError("k_out must have k's shape")
         nk, hkv, ks = k.shape[0], k.shape[1], k.stride(0)
+        kos, kohs = k_out.stride(0), k_out.stride(1)
+    if v is not None:
+        if k is None:
+            raise ValueError("v needs k")
+        _check_3d("v", v, hkv, d)
+        if v.shape != k.shape or v.stride() != k.stride() or v.dtype != k.dtype:
+            raise ValueError("v must match k in shape, strides and dtype")
+        v_out = torch.empty_strided(k_out.shape, k_out.stride(), dtype=v.dtype, device=v.device) \
+            if v_out is None else v_out
+        if v_out.shape != k_out.shape or v_out.stride() != k_out.stride() or v_out.dtype != v.dtype:
+            raise ValueError("v_out must match k_out in shape, strides and dtype")
+    elif v_out is not None:
+        raise ValueError("v_out needs v")
     if k_norm_max is not None and (k_norm_max.dtype != torch.float32 or k_norm_max.numel() < hkv):
         raise ValueError("k_norm_max must be float32 with one entry per K head")
     for t in (gain_q, gain_k, rope_base):
@@ -303,10 +332,10 @@ def qknorm_rope(q: torch.Tensor, k: Optional[torch.Tensor], gain_q: torch.Tensor
             raise ValueError("positions must be contiguous int32 [n, 3]")
     check(lib().magi_qknorm_rope(
         _ptr(q), _ptr(q_out), q.shape[0], q.shape[1], q.stride(0),
-        _ptr(k), _ptr(k_out), nk, hkv, ks, d, dtype_code(q.dtype),
+        _ptr(k), _ptr(k_out), nk, hkv, ks, kos, kohs, _ptr(v), _ptr(v_out), d, dtype_code(q.dtype),
         _ptr(gain_q), _ptr(gain_k), ghs, float(eps), _ptr(pos_q), _ptr(pos_k), _ptr(rope_base),
         float(q_scale), float(k_scale), _ptr(k_norm_max), _stream(q)))
-    return q_out, k_out
+    return (q_out, k_out) if v is None else (q_out, k_out, v_out)
 
 
 def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
@@ -315,14 +344,16 @@ def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
             k_norm_max: Optional[torch.Tensor] = None):
     """magi_ffa_fwd over ``plan``; returns (out [nq, hq, d], lse [nq, hq] fp32 or None).
     ``k_norm_max`` (float32 [hkv], optional) must bound the norm of every key
-    row of each group (qknorm_rope writes one)."""
+    row of each group (qknorm_rope writes one).  k and v are [nk, hkv, d]
+    views with contiguous channels and one common layout (token-major, or
+    group-major as from kv_group_major)."""
     d = q.shape[-1]
     hq, hkv = q.shape[1], k.shape[1]
     _check_3d("q", q, hq, d)
-    _check_3d("k", k, hkv, d)
-    _check_3d("v", v, hkv, d)
-    if k.stride(0) != v.stride(0):
-        raise ValueError("k and v must share the row stride")
+    _check_3d("k", k, hkv, d, any_head_stride=True)
+    _check_3d("v", v, hkv, d, any_head_stride=True)
+    if k.stride() != v.stride():
+        raise ValueError("k and v must share their strides")
     if (plan.nq, plan.nk, plan.hq, plan.hkv, plan.head_dim, plan.dtype) != \
             (q.shape[0], k.shape[0], hq, hkv, d, dtype_code(q.dtype)):
         raise ValueError("plan was made for a different shape or dtype")
@@ -334,7 +365,7 @@ def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
         torch.cuda.current_stream(q.device).wait_event(plan.ready)
     check(lib().magi_ffa_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q.shape[0], k.shape[0], hq, hkv, d,
-        dtype_code(q.dtype), q.stride(0), k.stride(0), out.stride(0),
+        dtype_code(q.dtype), q.stride(0), k.stride(0), k.stride(1), out.stride(0),
         0.0 if softmax_scale is None else float(softmax_scale), _ptr(k_norm_max),
         _ptr(plan.slices), int(plan.host["slices"].shape[0]), _ptr(plan.work), plan.num_work,
         _ptr(plan.tile_slices), int(plan.host["tile_slices"].shape[0]), _stream(q)))
@@ -351,9 +382,9 @@ def ffa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor
     d = q.shape[-1]
     hq, hkv = q.shape[1], k.shape[1]
     for name, t, heads in (("q", q, hq), ("k", k, hkv), ("v", v, hkv), ("out", out, hq), ("dout", dout, hq)):
-        _check_3d(name, t, heads, d)
-    if k.stride(0) != v.stride(0) or out.stride(0) != dout.stride(0):
-        raise ValueError("k/v and out/dout must share their row strides")
+        _check_3d(name, t, heads, d, any_head_stride=name in ("k", "v"))
+    if k.stride() != v.stride() or out.stride(0) != dout.stride(0):
+        raise ValueError("k/v must share their strides and out/dout their row strides")
     if plan.kwork is None:
         raise ValueError("plan has no key-major lists: make it with backward=True")
     if (plan.nq, plan.nk, plan.hq, plan.hkv, plan.head_dim, plan.dtype) != \
@@ -373,7 +404,7 @@ def ffa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor
     H = plan.host
     check(lib().magi_ffa_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
-        q.shape[0], k.shape[0], hq, hkv, d, dtype_code(q.dtype), q.stride(0), k.stride(0), out.stride(0),
+        q.shape[0], k.shape[0], hq, hkv, d, dtype_code(q.dtype), q.stride(0), k.stride(0), k.stride(1), out.stride(0),
         0.0 if softmax_scale is None else float(softmax_scale),
         _ptr(plan.slices), int(H["slices"].shape[0]), _ptr(plan.work), plan.num_work,
         _ptr(plan.tile_slices), int(H["tile_slices"].shape[0]),

@@ -218,7 +218,18 @@ int32_t magi_schedule(const magi_attn_slice* slices, int32_t num_slices,
  *
  * q_in, q_out   [device] [nq rows] x [hq heads] x [head_dim], row stride q_tok_stride
  *               elements (>= hq*head_dim), heads contiguous; 16-byte aligned
- * k_in, k_out   [device] same for K with hkv heads (both NULL and nk = 0 to skip K)
+ * k_in         [device] same for K with hkv heads, row stride k_tok_stride (NULL
+ *               and nk = 0 to skip K)
+ * k_out        [device] K's output; the vector of (token i, head h) starts at
+ *               element i * k_out_tok_stride + h * k_out_head_stride: either
+ *               token-major (k_out_head_stride = head_dim, k_out_tok_stride >=
+ *               hkv * head_dim) or group-major (k_out_tok_stride = head_dim,
+ *               k_out_head_stride >= nk * head_dim), whose K/V tiles
+ *               magi_ffa_fwd reads as contiguous blocks (faster).  Strides are
+ *               multiples of 16 bytes.  May alias k_in only with k_in's layout.
+ * v_in, v_out  [device] optional (both NULL to skip): V, laid out like k_in, is
+ *               copied unchanged into k_out's layout (v_out must not alias
+ *               v_in), so that K and V reach magi_ffa_fwd in one layout
  * head_dim      24 or 48 (must be divisible by 6)
  * gain_q/gain_k [device] fp32 [head_dim] (gain_head_stride 0) or [heads][head_dim]
  *               (gain_head_stride = head_dim)
@@ -233,6 +244,8 @@ int32_t magi_schedule(const magi_attn_slice* slices, int32_t num_slices,
  */
 int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, int32_t hq, int64_t q_tok_stride,
                          const void* k_in, void* k_out, int64_t nk, int32_t hkv, int64_t k_tok_stride,
+                         int64_t k_out_tok_stride, int64_t k_out_head_stride,
+                         const void* v_in, void* v_out,
                          int32_t head_dim, int32_t dtype,
                          const float* gain_q, const float* gain_k, int32_t gain_head_stride,
                          float eps, const int32_t* pos_q, const int32_t* pos_k,
@@ -252,7 +265,12 @@ int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, int32_t hq, 
  * fp32: fp32 arithmetic throughout.  The result is bitwise deterministic.
  *
  * q            [device] [nq][hq][head_dim], row stride q_tok_stride elements
- * k, v         [device] [nk][hkv][head_dim], row stride kv_tok_stride elements
+ * k, v         [device] nk tokens x hkv heads x head_dim; the vector of (token
+ *              i, head h) starts at element i * kv_tok_stride + h *
+ *              kv_head_stride: token-major (kv_head_stride = head_dim) or
+ *              group-major (kv_tok_stride = head_dim, kv_head_stride >= nk *
+ *              head_dim; each K/V tile is then one contiguous block, which
+ *              the kernel loads faster), vectors never overlapping
  * out          [device] [nq][hq][head_dim], row stride o_tok_stride elements
  * lse          [device] fp32 [nq][hq] (row stride hq), or NULL
  *              All tensor pointers 16-byte aligned, strides multiples of 8.
@@ -274,8 +292,8 @@ int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, int32_t hq, 
  */
 int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                      int64_t nq, int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
-                     int64_t q_tok_stride, int64_t kv_tok_stride, int64_t o_tok_stride,
-                     float softmax_scale, const float* k_norm_max,
+                     int64_t q_tok_stride, int64_t kv_tok_stride, int64_t kv_head_stride,
+                     int64_t o_tok_stride, float softmax_scale, const float* k_norm_max,
                      const magi_attn_slice* slices, int32_t num_slices,
                      const magi_work_item* work, int32_t num_work,
                      const int32_t* tile_slices, int32_t num_tile_slices,
@@ -328,7 +346,7 @@ int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_slices,
  *              keys has gradients with respect to those prescaled keys)
  * dout         [device] [nq][hq][head_dim], row stride o_tok_stride
  * dq           [device] out, layout of q (row stride q_tok_stride)
- * dk, dv       [device] out, layout of k / v (row stride kv_tok_stride);
+ * dk, dv       [device] out, layout of k / v (kv_tok_stride, kv_head_stride);
  *              rows no query sees are written as 0
  * delta        [device] fp32 [nq][hq] scratch the call fills first (caller
  *              owned, no other contents needed)
@@ -340,9 +358,9 @@ int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_slices,
 int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                      const float* lse, void* dq, void* dk, void* dv, float* delta,
                      int64_t nq, int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
-                     int64_t q_tok_stride, int64_t kv_tok_stride, int64_t o_tok_stride,
-                     float softmax_scale, const magi_attn_slice* slices, int32_t num_slices,
-                     const magi_work_item* qwork, int32_t num_qwork,
+                     int64_t q_tok_stride, int64_t kv_tok_stride, int64_t kv_head_stride,
+                     int64_t o_tok_stride, float softmax_scale, const magi_attn_slice* slices,
+                     int32_t num_slices, const magi_work_item* qwork, int32_t num_qwork,
                      const int32_t* q_tile_slices, int32_t num_q_tile_slices,
                      const magi_work_item* kwork, int32_t num_kwork,
                      const int32_t* k_tile_slices, int32_t num_k_tile_slices,

@@ -52,14 +52,21 @@ def dev_inputs(wl, inp):
                 pk=g(inp.pos_k), base=torch.tensor(wl.rope_base, dtype=torch.float32, device=DEV))
 
 
-def gpu_forward(wl, d):
-    """prologue (Q and K, softmax scale folded into K) then FFA over the
-    builder's slices, exactly as the benchmark runs it."""
+def gpu_forward(wl, d, group_major=True):
+    """prologue (Q and K, softmax scale folded into K; K and V written
+    group-major) then FFA over the builder's slices, exactly as the benchmark
+    runs it (group_major=False keeps K and V token-major)."""
     knm = torch.empty(wl.hkv, dtype=torch.float32, device=DEV)
-    qh, kh = ops.qknorm_rope(d["q"], d["k"], d["gq"], d["gk"], d["pq"], d["pk"], d["base"], wl.eps,
-                             k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm)
+    if group_major:
+        kg = ops.kv_group_major(wl.nk, wl.hkv, wl.head_dim, d["k"].dtype)
+        qh, kh, vh = ops.qknorm_rope(d["q"], d["k"], d["gq"], d["gk"], d["pq"], d["pk"], d["base"], wl.eps,
+                                     k_out=kg, k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm, v=d["v"])
+    else:
+        qh, kh = ops.qknorm_rope(d["q"], d["k"], d["gq"], d["gk"], d["pq"], d["pk"], d["base"], wl.eps,
+                                 k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm)
+        vh = d["v"]
     plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, d["q"].dtype)
-    O, L = ops.ffa_fwd(qh, kh, d["v"], plan, softmax_scale=ops.LN2, k_norm_max=knm)
+    O, L = ops.ffa_fwd(qh, kh, vh, plan, softmax_scale=ops.LN2, k_norm_max=knm)
     torch.cuda.synchronize()
     return qh, kh, O, L
 
@@ -246,6 +253,76 @@ def test_ffa_no_keys_and_scale():
     assert torch.all(O == 0) and torch.all(torch.isneginf(L))
     sl = np.array([(0, 30, 0, 50, 0)])
     ffa_case(rand((30, 16, 24), 11, 3.0), rand((50, 1, 24), 12, 3.0), rand((50, 1, 24), 13), sl, "bf16", scale=0.05)
+
+
+def to_group_major(t):
+    """a copy of a token-major [n, heads, d] tensor stored group-major"""
+    g = ops.kv_group_major(t.shape[0], t.shape[1], t.shape[2], t.dtype, t.device)
+    g.copy_(t)
+    return g
+
+
+@pytest.mark.parametrize("d", [24, 48])
+@pytest.mark.parametrize("bound", [False, True])
+def test_kv_layouts_give_identical_results(d, bound):
+    # only the addressing of K/V tiles differs between the layouts, so the
+    # results must agree bit for bit (and the token-major run matches the
+    # oracle in the tests above)
+    note(f"ffa K/V group-major vs token-major d={d} bound={bound}")
+    hkv, G = 2, 16
+    seqs = [W.SeqDesc(70, 3, 3, 0, 0, (-1, -1, 1), 1, 1, 70)]
+    sl = ops.build_slices(seqs)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(DEV) for x in
+               (rand((210, G * hkv, d), 40), rand((210, hkv, d), 41), rand((210, hkv, d), 42)))
+    knm = k.float().norm(dim=-1).amax(dim=0) * 1.01 if bound else None
+    plan = ops.make_plan(sl, 210, 210, G * hkv, hkv, d, torch.bfloat16)
+    O1, L1 = ops.ffa_fwd(q, k, v, plan, k_norm_max=knm)
+    kg, vg = to_group_major(k), to_group_major(v)
+    assert kg.stride() == (d, 210 * d, 1)
+    O2, L2 = ops.ffa_fwd(q, kg, vg, plan, k_norm_max=knm)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
+def test_kv_layouts_fp32_identical():
+    note("ffa fp32 K/V group-major vs token-major")
+    wl = W.make_workload("tiny")
+    inp = W.make_inputs(wl, 0)
+    q, k, v = (t.to(DEV) for t in (inp.q, inp.k, inp.v))
+    plan = ops.make_plan(ops.build_slices(wl.seqs), wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, torch.float32)
+    O1, L1 = ops.ffa_fwd(q, k, v, plan)
+    O2, L2 = ops.ffa_fwd(q, to_group_major(k), to_group_major(v), plan)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
+@pytest.mark.parametrize("name", ["tiny", "magi4.5b"])
+def test_prologue_group_major_output_and_v_copy(name):
+    # group-major K output holds the same values as the token-major one; V is
+    # moved unchanged; the key-norm bound does not depend on the layout
+    note(f"prologue group-major K and V copy {name}")
+    wl = W.make_workload(name)
+    d = dev_inputs(wl, W.make_inputs(wl, 0))
+    args = (d["q"], d["k"], d["gq"], d["gk"], d["pq"], d["pk"], d["base"], wl.eps)
+    n1 = torch.empty(wl.hkv, dtype=torch.float32, device=DEV)
+    n2 = torch.empty(wl.hkv, dtype=torch.float32, device=DEV)
+    q1, k1 = ops.qknorm_rope(*args, k_scale=0.5, k_norm_max=n1)
+    kg = ops.kv_group_major(wl.nk, wl.hkv, wl.head_dim, d["k"].dtype)
+    q2, k2, v2 = ops.qknorm_rope(*args, k_out=kg, k_scale=0.5, k_norm_max=n2, v=d["v"])
+    torch.cuda.synchronize()
+    assert k2.data_ptr() == kg.data_ptr() and v2.stride() == kg.stride()
+    assert torch.equal(q1, q2) and torch.equal(k1, k2) and torch.equal(v2, d["v"]) and torch.equal(n1, n2)
+
+
+def test_end_to_end_magi45b_token_major():
+    # the full 4.5B layer with K and V left token-major
+    wl = W.make_workload("magi4.5b", 0)
+    inp = W.make_inputs(wl, 0)
+    d = dev_inputs(wl, inp)
+    note("end-to-end magi4.5b token-major K/V")
+    _, _, O1, L1 = gpu_forward(wl, d, group_major=False)
+    _, _, O2, L2 = gpu_forward(wl, d, group_major=True)
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
 
 
 # --------------------------------------------------------------------------- full workloads

@@ -322,36 +322,43 @@ def test_device_entry_points_validate_before_any_hip_call():
     p = C.c_void_p(4096)  # never dereferenced: every call below fails validation
     f = C.c_void_p(4096)
     # magi_qknorm_rope
-    assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 32, 0, f, None, 0, 1e-6, p, None, f,
-                              1.0, 1.0, None, None) == _lib.MAGI_ERR_UNSUPPORTED
-    assert L.magi_qknorm_rope(p, p, 10, 8, 100, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, f,
-                              1.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # stride < heads*d
-    assert L.magi_qknorm_rope(C.c_void_p(4098), p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6,
-                              p, None, f, 1.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # misaligned
-    assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, -1.0, p, None, f,
-                              1.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # eps < 0
-    assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 7, 1e-6, p, None, f,
-                              1.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # gain stride
-    assert L.magi_qknorm_rope(p, p, 10, 8, 192, p, p, 5, 2, 48, 24, 0, f, None, 0, 1e-6, p, p, f,
-                              1.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # gain_k NULL
-    assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, None,
-                              1.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # rope_base NULL
-    assert L.magi_qknorm_rope(None, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, f,
-                              1.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # q NULL
-    assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, f,
-                              0.0, 1.0, None, None) == _lib.MAGI_ERR_INVALID_ARG   # zero scale
-    assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, f,
-                              1.0, 1.0, f, None) == _lib.MAGI_ERR_INVALID_ARG   # k_norm_max without K
-    assert L.magi_qknorm_rope(p, p, 10, 8, 192, None, None, 0, 1, 0, 24, 0, f, None, 0, 1e-6, p, None, f,
-                              1.0, float("inf"), None, None) == _lib.MAGI_ERR_INVALID_ARG   # inf scale
+    def qk(**kw):
+        a = dict(qi=p, qo=p, nq=10, hq=8, qs=192, ki=None, ko=None, nk=0, hkv=1, ks=0, kos=0, kohs=24, vi=None,
+                 vo=None, d=24, dt=0, gq=f, gk=None, ghs=0, eps=1e-6, pq=p, pk=None, base=f, qsc=1.0, ksc=1.0,
+                 knm=None)
+        a.update(kw)
+        return L.magi_qknorm_rope(a["qi"], a["qo"], a["nq"], a["hq"], a["qs"], a["ki"], a["ko"], a["nk"], a["hkv"],
+                                  a["ks"], a["kos"], a["kohs"], a["vi"], a["vo"], a["d"], a["dt"], a["gq"], a["gk"],
+                                  a["ghs"], a["eps"], a["pq"], a["pk"], a["base"], a["qsc"], a["ksc"], a["knm"], None)
+    assert qk(d=32) == _lib.MAGI_ERR_UNSUPPORTED
+    assert qk(qs=100) == _lib.MAGI_ERR_INVALID_ARG                    # stride < heads*d
+    assert qk(qi=C.c_void_p(4098)) == _lib.MAGI_ERR_INVALID_ARG       # misaligned
+    assert qk(eps=-1.0) == _lib.MAGI_ERR_INVALID_ARG
+    assert qk(ghs=7) == _lib.MAGI_ERR_INVALID_ARG                     # gain stride
+    kside = dict(ki=p, ko=C.c_void_p(8192), nk=5, hkv=2, ks=48, kos=48, kohs=24, gk=f, pk=p)
+    assert qk(**dict(kside, gk=None)) == _lib.MAGI_ERR_INVALID_ARG    # gain_k NULL
+    assert qk(base=None) == _lib.MAGI_ERR_INVALID_ARG                 # rope_base NULL
+    assert qk(qi=None) == _lib.MAGI_ERR_INVALID_ARG                   # q NULL
+    assert qk(qsc=0.0) == _lib.MAGI_ERR_INVALID_ARG                   # zero scale
+    assert qk(knm=f) == _lib.MAGI_ERR_INVALID_ARG                     # k_norm_max without K
+    assert qk(ksc=float("inf")) == _lib.MAGI_ERR_INVALID_ARG          # inf scale
+    # K output layouts: overlapping vectors, misaligned strides, in-place with a new layout
+    assert qk(**dict(kside, kos=24, kohs=24)) == _lib.MAGI_ERR_INVALID_ARG
+    assert qk(**dict(kside, kos=24, kohs=100)) == _lib.MAGI_ERR_INVALID_ARG   # group-major needs >= 5*24
+    assert qk(**dict(kside, kos=24, kohs=124)) == _lib.MAGI_ERR_INVALID_ARG   # not a 16-byte multiple
+    assert qk(**dict(kside, ko=p, kos=24, kohs=120)) == _lib.MAGI_ERR_INVALID_ARG
+    # V goes with K, needs both pointers and must not be updated in place
+    assert qk(vi=p, vo=f) == _lib.MAGI_ERR_INVALID_ARG
+    assert qk(**dict(kside, vi=p)) == _lib.MAGI_ERR_INVALID_ARG
+    assert qk(**dict(kside, vi=C.c_void_p(12288), vo=C.c_void_p(12288))) == _lib.MAGI_ERR_INVALID_ARG
     # magi_ffa_fwd
     def ffa(**kw):
-        a = dict(q=p, k=p, v=p, out=p, lse=None, nq=16, nk=16, hq=16, hkv=1, d=24, dt=0, qs=384, kvs=24, os_=384,
-                 scale=0.0, knm=None, sl=p, ns=1, w=p, nw=1, ts=p, nts=1)
+        a = dict(q=p, k=p, v=p, out=p, lse=None, nq=16, nk=16, hq=16, hkv=1, d=24, dt=0, qs=384, kvs=24, kvhs=24,
+                 os_=384, scale=0.0, knm=None, sl=p, ns=1, w=p, nw=1, ts=p, nts=1)
         a.update(kw)
         return L.magi_ffa_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["nq"], a["nk"], a["hq"], a["hkv"],
-                              a["d"], a["dt"], a["qs"], a["kvs"], a["os_"], a["scale"], a["knm"], a["sl"], a["ns"],
-                              a["w"], a["nw"], a["ts"], a["nts"], None)
+                              a["d"], a["dt"], a["qs"], a["kvs"], a["kvhs"], a["os_"], a["scale"], a["knm"], a["sl"],
+                              a["ns"], a["w"], a["nw"], a["ts"], a["nts"], None)
     assert ffa(d=64) == _lib.MAGI_ERR_UNSUPPORTED
     assert ffa(dt=3) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(hq=12, hkv=8) == _lib.MAGI_ERR_INVALID_ARG
@@ -360,6 +367,11 @@ def test_device_entry_points_validate_before_any_hip_call():
     assert ffa(kvs=20) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(kvs=28) == _lib.MAGI_ERR_INVALID_ARG      # not a 16-byte multiple
     assert ffa(kvs=1 << 23) == _lib.MAGI_ERR_UNSUPPORTED  # a K/V tile would pass 2^31 bytes
+    # K/V layouts: token-major needs kvs >= hkv * kvhs, group-major kvhs >= nk * kvs
+    assert ffa(hq=32, hkv=2, qs=768, os_=768, kvs=24, kvhs=24) == _lib.MAGI_ERR_INVALID_ARG
+    assert ffa(hq=32, hkv=2, qs=768, os_=768, kvs=24, kvhs=16 * 24 - 8) == _lib.MAGI_ERR_INVALID_ARG
+    assert ffa(hq=32, hkv=2, qs=768, os_=768, kvs=48, kvhs=20) == _lib.MAGI_ERR_INVALID_ARG
+    assert ffa(hq=32, hkv=2, qs=768, os_=768, kvs=24, kvhs=16 * 24 + 4) == _lib.MAGI_ERR_INVALID_ARG  # 16-byte
     assert ffa(out=C.c_void_p(4100)) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(lse=C.c_void_p(4098)) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(scale=float("nan")) == _lib.MAGI_ERR_INVALID_ARG
