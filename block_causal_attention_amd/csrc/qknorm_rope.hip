@@ -75,11 +75,25 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(QkArgs a, int end
   }
 
   extern __shared__ float2 table[];  // [tpb][P] (cos, sin)
+  // Consecutive threads take consecutive heads of a token when the output
+  // is token-major, consecutive tokens of a head when it is group-major, so
+  // that the stores of a wave cover contiguous memory either way.
+  const bool group_out = s.out_head_stride != D;
+  auto vec_of = [&](int v, int& t, int& h) {
+    if (group_out) {
+      t = v % ntok;
+      h = v / ntok;
+    } else {
+      t = v / s.heads;
+      h = v % s.heads;
+    }
+  };
 
   if (s.gain == nullptr) {
     // V: the same rows, moved into the output layout
     for (int v = threadIdx.x; v < ntok * s.heads; v += kThreads) {
-      const int t = v / s.heads, h = v % s.heads;
+      int t, h;
+      vec_of(v, t, h);
       const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(s.in) + (tok0 + t) * s.tok_stride +
                                                         (int64_t)h * D);
       uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<T*>(s.out) + (tok0 + t) * s.out_tok_stride +
@@ -104,7 +118,8 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(QkArgs a, int end
 
   const int nvec = ntok * s.heads;
   for (int v = threadIdx.x; v < nvec; v += kThreads) {
-    const int t = v / s.heads, h = v % s.heads;
+    int t, h;
+    vec_of(v, t, h);
     const T* src = reinterpret_cast<const T*>(s.in) + (tok0 + t) * s.tok_stride + (int64_t)h * D;
     T* dst = reinterpret_cast<T*>(s.out) + (tok0 + t) * s.out_tok_stride + (int64_t)h * s.out_head_stride;
     float x[D];
