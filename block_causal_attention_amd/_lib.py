@@ -45,6 +45,11 @@ class RingDesc(C.Structure):
                 ("k_offset", C.c_int32), ("kv_range", C.POINTER(C.c_int32))]
 
 
+class KvReduce(C.Structure):
+    _fields_ = [("key_start", C.c_int32), ("key_len", C.c_int32), ("kv_group", C.c_int32),
+                ("slot_begin", C.c_int32), ("slot_count", C.c_int32)]
+
+
 class CrossDesc(C.Structure):
     _fields_ = [("q_offset", C.c_int32), ("q_len", C.c_int32), ("k_offset", C.c_int32), ("k_len", C.c_int32)]
 
@@ -87,10 +92,11 @@ def lib() -> C.CDLL:
         L.magi_default_tile_k.argtypes = [i32, i32, i32, i32]
         L.magi_slices_cross.argtypes = [C.POINTER(CrossDesc), i32, C.POINTER(AttnSlice), i32, C.POINTER(i32)]
         L.magi_slices_ring.argtypes = [C.POINTER(RingDesc), C.POINTER(AttnSlice), i32, C.POINTER(i32)]
-        L.magi_schedule_kv.argtypes = L.magi_schedule.argtypes
+        L.magi_schedule_kv.argtypes = L.magi_schedule.argtypes + [C.POINTER(i32), C.POINTER(KvReduce), i32,
+                                                                   C.POINTER(i32), C.POINTER(i32)]
         L.magi_ffa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32,
                                    i64, i64, i64, i64, C.c_float, vp, i32, vp, i32, vp, i32, vp, i32, vp, i32,
-                                   vp]
+                                   vp, vp, i32, i32, vp, i64, vp]
         for name in ("magi_slices_build", "magi_default_tile_q", "magi_schedule", "magi_qknorm_rope",
                      "magi_ffa_fwd", "magi_default_tile_k", "magi_schedule_kv", "magi_ffa_bwd",
                      "magi_slices_cross", "magi_slices_ring"):

@@ -185,9 +185,12 @@ extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, con
                                 int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
                                 int64_t q_tok_stride, int64_t kv_tok_stride, int64_t kv_head_stride,
                                 int64_t o_tok_stride, float softmax_scale, const magi_attn_slice* slices,
-                                int32_t num_slices, const magi_work_item* qwork, int32_t num_qwork, const int32_t* q_tile_slices,
-                                int32_t num_q_tile_slices, const magi_work_item* kwork, int32_t num_kwork,
-                                const int32_t* k_tile_slices, int32_t num_k_tile_slices, void* stream) {
+                                int32_t num_slices, const magi_work_item* qwork, int32_t num_qwork,
+                                const int32_t* q_tile_slices, int32_t num_q_tile_slices,
+                                const magi_work_item* kwork, int32_t num_kwork, const int32_t* k_tile_slices,
+                                int32_t num_k_tile_slices, const int32_t* kitem_slot,
+                                const magi_kv_reduce* reduce, int32_t num_reduce, int32_t num_slots,
+                                float* partial, int64_t partial_floats, void* stream) {
   int32_t st;
   if ((st = check_common(head_dim, dtype)) != MAGI_OK) return st;
   if (hq < 1 || hkv < 1) return fail(MAGI_ERR_INVALID_ARG, "hq and hkv must be >= 1");
@@ -215,6 +218,16 @@ extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, con
       (num_k_tile_slices > 0 && k_tile_slices == nullptr))
     return fail(MAGI_ERR_INVALID_ARG, "a non-empty list pointer is NULL");
   if (num_qwork > 0 && nq == 0) return fail(MAGI_ERR_INVALID_ARG, "query work items for an empty query tensor");
+  if (num_reduce < 0 || num_slots < 0) return fail(MAGI_ERR_INVALID_ARG, "negative reduce or slot count");
+  if (num_reduce > 0 || num_slots > 0) {
+    if (reduce == nullptr || kitem_slot == nullptr || partial == nullptr)
+      return fail(MAGI_ERR_INVALID_ARG, "a split schedule needs kitem_slot, reduce and partial");
+    // slot layout fixed by the dK/dV kernel: 2 x 128 keys x head_dim fp32
+    if (partial_floats < (int64_t)num_slots * 2 * 128 * head_dim)
+      return fail(MAGI_ERR_INVALID_ARG, "partial holds %lld floats, %d slots need %lld", (long long)partial_floats,
+                  num_slots, (long long)num_slots * 2 * 128 * head_dim);
+    if (!aligned16(partial)) return fail(MAGI_ERR_INVALID_ARG, "partial is not 16-byte aligned");
+  }
   if (num_kwork > 0 && nk == 0) return fail(MAGI_ERR_INVALID_ARG, "key work items for an empty key tensor");
 
   BwdArgs a{};
@@ -249,6 +262,11 @@ extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, con
   a.num_kwork = num_kwork;
   a.k_tile_slices = k_tile_slices;
   a.num_k_tile_slices = num_k_tile_slices;
+  a.kitem_slot = kitem_slot;
+  a.reduce = reduce;
+  a.num_reduce = num_reduce;
+  a.num_slots = num_slots;
+  a.partial = partial;
   const hipError_t e = launch_ffa_bwd(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MAGI_ERR_HIP, "ffa_bwd launch: %s", hipGetErrorString(e));
   return ok();

@@ -537,8 +537,26 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
     buf ^= 1;
   }
 
-  // epilogue: lane (key) holds d = mb 32 + 8 grp + 4 h + r of dK^T / dV^T
-  if (kvalid) {
+  // epilogue: lane (key) holds d = mb 32 + 8 grp + 4 h + r of dK^T / dV^T.
+  // One part of a split tile stores its fp32 sums (dK unscaled) in its slot;
+  // bwd_reduce adds the parts and writes dK, dV.
+  const int32_t slot = a.kitem_slot != nullptr ? const_ld(&a.kitem_slot[blockIdx.x]) : -1;
+  if (kvalid && slot >= 0 && slot < a.num_slots) {
+    float* pk = a.partial + (int64_t)slot * 2 * kKeys * D + (int64_t)(key - k0) * D;
+    float* pv = pk + kKeys * D;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const int d = mb * 32 + 8 * grp + 4 * h;
+        if (d < D) {
+          *reinterpret_cast<float4*>(pk + d) =
+              make_float4(dk[mb][4 * grp], dk[mb][4 * grp + 1], dk[mb][4 * grp + 2], dk[mb][4 * grp + 3]);
+          *reinterpret_cast<float4*>(pv + d) =
+              make_float4(dv[mb][4 * grp], dv[mb][4 * grp + 1], dv[mb][4 * grp + 2], dv[mb][4 * grp + 3]);
+        }
+      }
+  } else if (kvalid && slot < 0) {
     __bf16* dkp = reinterpret_cast<__bf16*>(a.dk) + (int64_t)key * a.kv_stride + (int64_t)g * a.kv_hstride;
     __bf16* dvp = reinterpret_cast<__bf16*>(a.dv) + (int64_t)key * a.kv_stride + (int64_t)g * a.kv_hstride;
 #pragma unroll
@@ -673,12 +691,64 @@ __global__ __launch_bounds__(kThreads32) void bwd_dkdv_f32(BwdArgs a) {
         }
       }
   }
+  const int32_t slot = a.kitem_slot != nullptr ? a.kitem_slot[blockIdx.x] : -1;
+  if (slot >= 0) {
+    if (slot >= a.num_slots || key - wi.q_start >= kKeys) return;
+    float* pk = a.partial + (int64_t)slot * 2 * kKeys * D + (key - wi.q_start) * D;
+    float* pv = pk + kKeys * D;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      pk[i] = dkacc[i];
+      pv[i] = dvacc[i];
+    }
+    return;
+  }
   float* dkp = reinterpret_cast<float*>(a.dk) + key * a.kv_stride + (int64_t)g * a.kv_hstride;
   float* dvp = reinterpret_cast<float*>(a.dv) + key * a.kv_stride + (int64_t)g * a.kv_hstride;
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     dkp[i] = dkacc[i] * a.scale;
     dvp[i] = dvacc[i];
+  }
+}
+
+// Sums of a split dK/dV pass: one block per reduce entry; each thread owns
+// 4 channels of one key of dK or dV and adds the entry's slots in slot
+// order (a fixed order, so the result is deterministic), then scales dK.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
+  const magi_kv_reduce r = a.reduce[blockIdx.x];
+  if (r.key_len <= 0 || r.key_len > kKeys || r.key_start < 0 || (int64_t)r.key_start + r.key_len > a.nk ||
+      r.kv_group < 0 || r.kv_group >= a.hkv || r.slot_begin < 0 || r.slot_count < 1 ||
+      (int64_t)r.slot_begin + r.slot_count > a.num_slots)
+    return;
+  constexpr int Q4 = D / 4;
+  const int n = 2 * r.key_len * Q4;  // (dK | dV, key, 4 channels)
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int which = i / (r.key_len * Q4), rem = i % (r.key_len * Q4);
+    const int kr = rem / Q4, d = 4 * (rem % Q4);
+    const float* src = a.partial + (int64_t)r.slot_begin * 2 * kKeys * D + (int64_t)which * kKeys * D +
+                       (int64_t)kr * D + d;
+    float4 acc = *reinterpret_cast<const float4*>(src);
+    for (int sl = 1; sl < r.slot_count; ++sl) {
+      const float4 x = *reinterpret_cast<const float4*>(src + (int64_t)sl * 2 * kKeys * D);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    if (which == 0) {
+      acc.x *= a.scale;
+      acc.y *= a.scale;
+      acc.z *= a.scale;
+      acc.w *= a.scale;
+    }
+    T* dst = reinterpret_cast<T*>(which == 0 ? a.dk : a.dv) + (int64_t)(r.key_start + kr) * a.kv_stride +
+             (int64_t)r.kv_group * a.kv_hstride + d;
+    dst[0] = (T)acc.x;
+    dst[1] = (T)acc.y;
+    dst[2] = (T)acc.z;
+    dst[3] = (T)acc.w;
   }
 }
 
@@ -711,6 +781,13 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((bwd_dkdv_bf16<D, true>), grid, dim3(NTK), 0, stream, a);
     else
       hipLaunchKernelGGL((bwd_dkdv_bf16<D, false>), grid, dim3(NTK), 0, stream, a);
+  }
+  if (a.num_reduce > 0) {
+    const dim3 grid(a.num_reduce);
+    if (bf)
+      hipLaunchKernelGGL((bwd_reduce<D, __bf16>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_reduce<D, float>), grid, dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }

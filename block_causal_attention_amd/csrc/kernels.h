@@ -81,6 +81,11 @@ struct BwdArgs {
   int32_t num_kwork;
   const int32_t* k_tile_slices;
   int32_t num_k_tile_slices;
+  const int32_t* kitem_slot;     // [num_kwork] partial slot of a key-major item, or -1
+  const magi_kv_reduce* reduce;  // sums of the partial slots
+  int32_t num_reduce;
+  int32_t num_slots;
+  float* partial;                // [num_slots][2][kKeys][head_dim] fp32 (dK, then dV)
 };
 
 hipError_t launch_ffa_bwd(const BwdArgs& a, hipStream_t stream);

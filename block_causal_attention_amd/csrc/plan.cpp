@@ -261,11 +261,14 @@ extern "C" int32_t magi_default_tile_k(int32_t hq, int32_t hkv, int32_t head_dim
 extern "C" int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_slices, int64_t nq, int64_t nk,
                                     int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype, int32_t tile_k,
                                     magi_work_item* work, int32_t work_cap, int32_t* num_work,
-                                    int32_t* tile_slices, int32_t ts_cap, int32_t* num_tile_slices) {
-  if (num_work == nullptr || num_tile_slices == nullptr)
-    return fail(MAGI_ERR_INVALID_ARG, "num_work / num_tile_slices is NULL");
-  if (work_cap < 0 || ts_cap < 0) return fail(MAGI_ERR_INVALID_ARG, "negative capacity");
-  if ((work == nullptr) != (work_cap == 0) || (tile_slices == nullptr) != (ts_cap == 0))
+                                    int32_t* tile_slices, int32_t ts_cap, int32_t* num_tile_slices,
+                                    int32_t* item_slot, magi_kv_reduce* reduce, int32_t reduce_cap,
+                                    int32_t* num_reduce, int32_t* num_slots) {
+  if (num_work == nullptr || num_tile_slices == nullptr || num_reduce == nullptr || num_slots == nullptr)
+    return fail(MAGI_ERR_INVALID_ARG, "a count pointer is NULL");
+  if (work_cap < 0 || ts_cap < 0 || reduce_cap < 0) return fail(MAGI_ERR_INVALID_ARG, "negative capacity");
+  if ((work == nullptr) != (work_cap == 0) || (tile_slices == nullptr) != (ts_cap == 0) ||
+      (item_slot == nullptr) != (work_cap == 0) || (reduce == nullptr) != (reduce_cap == 0))
     return fail(MAGI_ERR_INVALID_ARG, "output array and capacity disagree (NULL needs cap 0)");
   // the query-major size query validates the slices (ranges, types, overlap)
   int32_t nw_q = 0, nts_q = 0;
@@ -302,38 +305,95 @@ extern "C" int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_s
       return slices[x].q_start != slices[y].q_start ? slices[x].q_start < slices[y].q_start : x < y;
     });
 
-  struct Tile { int64_t k0, len, cost; size_t seg; };
+  // tiles, with the visible pairs each listed slice contributes
+  struct Tile { int64_t k0, len; size_t seg; std::vector<int64_t> pairs; };
   std::vector<Tile> tiles;
-  int64_t ts_total = 0;
+  int64_t ts_total = 0, total = 0, largest = 0;
   for (size_t g = 0; g < nseg; ++g) {
     for (int64_t t0 = cuts[g]; t0 < cuts[g + 1]; t0 += tile_k) {
-      const int64_t len = std::min<int64_t>(tile_k, cuts[g + 1] - t0);
-      int64_t cost = 0;
-      for (int32_t i : cover[g])
-        for (int64_t k = t0; k < t0 + len; ++k) cost += std::max<int64_t>(0, slices[i].q_end - col_first(slices[i], k));
-      tiles.push_back({t0, len, cost, g});
+      Tile t{t0, std::min<int64_t>(tile_k, cuts[g + 1] - t0), g, {}};
+      for (int32_t i : cover[g]) {
+        int64_t c = 0;
+        for (int64_t k = t0; k < t0 + t.len; ++k) c += std::max<int64_t>(0, slices[i].q_end - col_first(slices[i], k));
+        t.pairs.push_back(c);
+        total += c;
+        largest = std::max(largest, c);
+      }
       ts_total += (int64_t)cover[g].size();
+      tiles.push_back(std::move(t));
     }
   }
-  const int64_t nwork = (int64_t)tiles.size() * hkv;
-  if (nwork > INT32_MAX || ts_total > INT32_MAX) return fail(MAGI_ERR_INVALID_ARG, "work list exceeds int32");
+  // parts: runs of consecutive listed slices of at most T pairs (a single
+  // larger slice is a part of its own)
+  constexpr int64_t kTargetItems = 1536;  // ~3 items per workgroup slot of the whole GPU
+  const int64_t T = std::max<int64_t>(largest, (total * hkv + kTargetItems - 1) / kTargetItems);
+  struct Unit { size_t tile; int32_t a, b; int64_t cost; int32_t part, nparts; };
+  std::vector<Unit> units;
+  int64_t nslots = 0, nred = 0;
+  for (size_t ti = 0; ti < tiles.size(); ++ti) {
+    const Tile& t = tiles[ti];
+    const size_t first = units.size();
+    int32_t a = 0;
+    int64_t acc = 0;
+    for (int32_t j = 0; j < (int32_t)t.pairs.size(); ++j) {
+      if (j > a && acc + t.pairs[j] > T) {
+        units.push_back({ti, a, j, acc, 0, 0});
+        a = j;
+        acc = 0;
+      }
+      acc += t.pairs[j];
+    }
+    units.push_back({ti, a, (int32_t)t.pairs.size(), acc, 0, 0});
+    const int32_t np = (int32_t)(units.size() - first);
+    for (int32_t p = 0; p < np; ++p) {
+      units[first + p].part = p;
+      units[first + p].nparts = np;
+    }
+    if (np > 1) {
+      nslots += (int64_t)np * hkv;
+      nred += hkv;
+    }
+  }
+  const int64_t nwork = (int64_t)units.size() * hkv;
+  if (nwork > INT32_MAX || ts_total > INT32_MAX || nslots > INT32_MAX)
+    return fail(MAGI_ERR_INVALID_ARG, "work list exceeds int32");
   *num_work = (int32_t)nwork;
   *num_tile_slices = (int32_t)ts_total;
-  if (work == nullptr && tile_slices == nullptr) return ok();
-  if (work_cap < nwork || ts_cap < ts_total)
-    return fail(MAGI_ERR_BUFFER_TOO_SMALL, "need work_cap >= %lld and ts_cap >= %lld", (long long)nwork,
-                (long long)ts_total);
+  *num_reduce = (int32_t)nred;
+  *num_slots = (int32_t)nslots;
+  if (work == nullptr && tile_slices == nullptr && reduce == nullptr) return ok();
+  if (work_cap < nwork || ts_cap < ts_total || reduce_cap < nred)
+    return fail(MAGI_ERR_BUFFER_TOO_SMALL, "need work_cap >= %lld, ts_cap >= %lld and reduce_cap >= %lld",
+                (long long)nwork, (long long)ts_total, (long long)nred);
 
-  std::vector<size_t> ord(tiles.size());
-  std::iota(ord.begin(), ord.end(), 0);
-  std::stable_sort(ord.begin(), ord.end(), [&](size_t x, size_t y) { return tiles[x].cost > tiles[y].cost; });
-  int32_t ts = 0, w = 0;
-  for (size_t rank = 0; rank < ord.size(); ++rank) {
-    const Tile& t = tiles[ord[rank]];
-    const int32_t sb = ts;
-    for (int32_t i : cover[t.seg]) tile_slices[ts++] = i;
+  // tile lists in key order; slots of a split tile: group-major, parts in order
+  std::vector<int32_t> tile_sb(tiles.size()), slot0(tiles.size(), -1);
+  int32_t ts = 0, slot = 0, r = 0;
+  for (size_t ti = 0; ti < tiles.size(); ++ti) {
+    tile_sb[ti] = ts;
+    for (int32_t i : cover[tiles[ti].seg]) tile_slices[ts++] = i;
+  }
+  for (const Unit& u : units) {
+    if (u.nparts < 2 || u.part != 0) continue;
+    const Tile& t = tiles[u.tile];
+    slot0[u.tile] = slot;
     for (int32_t g = 0; g < hkv; ++g)
-      work[w++] = {(int32_t)t.k0, (int32_t)t.len, sb, ts, g, (int32_t)std::min<int64_t>(t.cost, INT32_MAX)};
+      reduce[r++] = {(int32_t)t.k0, (int32_t)t.len, g, slot + g * u.nparts, u.nparts};
+    slot += u.nparts * hkv;
+  }
+  // heaviest units first; ties keep key order (deterministic)
+  std::vector<size_t> ord(units.size());
+  std::iota(ord.begin(), ord.end(), 0);
+  std::stable_sort(ord.begin(), ord.end(), [&](size_t x, size_t y) { return units[x].cost > units[y].cost; });
+  int32_t w = 0;
+  for (size_t rank = 0; rank < ord.size(); ++rank) {
+    const Unit& u = units[ord[rank]];
+    const Tile& t = tiles[u.tile];
+    for (int32_t g = 0; g < hkv; ++g) {
+      item_slot[w] = u.nparts > 1 ? slot0[u.tile] + g * u.nparts + u.part : -1;
+      work[w++] = {(int32_t)t.k0, (int32_t)t.len, tile_sb[u.tile] + u.a, tile_sb[u.tile] + u.b, g,
+                   (int32_t)std::min<int64_t>(u.cost, INT32_MAX)};
+    }
   }
   return ok();
 }

@@ -14,7 +14,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import AttnSlice, CrossDesc, RingDesc, SeqDesc, WorkItem, check, lib
+from ._lib import AttnSlice, CrossDesc, KvReduce, RingDesc, SeqDesc, WorkItem, check, lib
 
 LN2 = 0.6931471805599453
 LOG2E = 1.4426950408889634
@@ -145,10 +145,26 @@ def schedule(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim: 
 
 def schedule_kv(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim: int, dtype: int,
                 tile_k: int = 0):
-    """magi_schedule_kv: slices -> key-major (work int32 [m, 6], tile_slices int32 [t])
-    for the backward's dK/dV pass (q_start/q_len of an item are its keys)."""
+    """magi_schedule_kv: slices -> key-major lists for the backward's dK/dV
+    pass: (work int32 [m, 6], tile_slices int32 [t], item_slot int32 [m],
+    reduce int32 [r, 5], num_slots).  q_start/q_len of an item are its keys;
+    item_slot is the partial slot of a part of a split key tile, else -1."""
     L = lib()
-    return _schedule(L.magi_schedule_kv, L.magi_default_tile_k, slices, nq, nk, hq, hkv, head_dim, dtype, tile_k)
+    s = np.ascontiguousarray(np.asarray(slices, np.int32).reshape(-1, 5))
+    sp = s.ctypes.data_as(C.POINTER(AttnSlice)) if len(s) else None
+    nw, nt, nr, ns = C.c_int32(0), C.c_int32(0), C.c_int32(0), C.c_int32(0)
+    check(L.magi_schedule_kv(sp, len(s), nq, nk, hq, hkv, head_dim, dtype, tile_k, None, 0, C.byref(nw),
+                             None, 0, C.byref(nt), None, None, 0, C.byref(nr), C.byref(ns)))
+    work = np.empty((max(nw.value, 1), 6), np.int32)
+    ts = np.empty(max(nt.value, 1), np.int32)
+    slot = np.empty(max(nw.value, 1), np.int32)
+    red = np.empty((max(nr.value, 1), 5), np.int32)
+    check(L.magi_schedule_kv(sp, len(s), nq, nk, hq, hkv, head_dim, dtype, tile_k,
+                             work.ctypes.data_as(C.POINTER(WorkItem)), work.shape[0], C.byref(nw),
+                             ts.ctypes.data_as(C.POINTER(C.c_int32)), ts.shape[0], C.byref(nt),
+                             slot.ctypes.data_as(C.POINTER(C.c_int32)),
+                             red.ctypes.data_as(C.POINTER(KvReduce)), red.shape[0], C.byref(nr), C.byref(ns)))
+    return work[:nw.value], ts[:nt.value], slot[:nw.value], red[:nr.value], ns.value
 
 
 @dataclass
@@ -168,6 +184,9 @@ class Plan:
     ready: Optional[torch.cuda.Event] = None  # recorded after the upload; ffa_fwd waits on it
     kwork: Optional[torch.Tensor] = None        # key-major lists (backward plans only)
     k_tile_slices: Optional[torch.Tensor] = None
+    kitem_slot: Optional[torch.Tensor] = None   # partial slot per key-major item, or -1
+    kreduce: Optional[torch.Tensor] = None      # int32 [r, 5] sums of split key tiles
+    num_slots: int = 0
 
     @property
     def num_work(self) -> int:
@@ -184,8 +203,8 @@ def make_plan(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim:
     work, ts = schedule(slices, nq, nk, hq, hkv, head_dim, code, tile_q)
     parts = [slices.reshape(-1), work.reshape(-1), ts.reshape(-1)]
     if backward:
-        kwork, kts = schedule_kv(slices, nq, nk, hq, hkv, head_dim, code)
-        parts += [kwork.reshape(-1), kts.reshape(-1)]
+        kwork, kts, kslot, kred, nslots = schedule_kv(slices, nq, nk, hq, hkv, head_dim, code)
+        parts += [kwork.reshape(-1), kts.reshape(-1), kslot.reshape(-1), kred.reshape(-1)]
     sizes = [max(p.size, 1) for p in parts]     # an empty list still gets one valid word
     # The copy runs on a side stream so it does not queue behind the work
     # already on the caller's stream (the previous attention launch); only
@@ -210,8 +229,9 @@ def make_plan(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim:
     host_arrays = {"slices": slices, "work": work, "tile_slices": ts}
     plan = Plan(nq, nk, hq, hkv, head_dim, code, views[0], views[1], views[2], host_arrays, ready)
     if backward:
-        plan.kwork, plan.k_tile_slices = views[3], views[4]
-        host_arrays.update(kwork=kwork, k_tile_slices=kts)
+        plan.kwork, plan.k_tile_slices, plan.kitem_slot, plan.kreduce = views[3], views[4], views[5], views[6]
+        plan.num_slots = nslots
+        host_arrays.update(kwork=kwork, k_tile_slices=kts, kitem_slot=kslot, kreduce=kred)
     return plan
 
 
@@ -399,6 +419,9 @@ def ffa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor
         if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype:
             raise ValueError(f"{name} must match {name[1:]} in shape, strides and dtype")
     delta = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
+    # partial sums of split key tiles: 2 x 128 keys x d fp32 per slot
+    nfl = plan.num_slots * 2 * 128 * d
+    partial = torch.empty(max(nfl, 4), dtype=torch.float32, device=q.device)
     if plan.ready is not None:
         torch.cuda.current_stream(q.device).wait_event(plan.ready)
     H = plan.host
@@ -409,5 +432,6 @@ def ffa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor
         _ptr(plan.slices), int(H["slices"].shape[0]), _ptr(plan.work), plan.num_work,
         _ptr(plan.tile_slices), int(H["tile_slices"].shape[0]),
         _ptr(plan.kwork), int(H["kwork"].shape[0]), _ptr(plan.k_tile_slices), int(H["k_tile_slices"].shape[0]),
+        _ptr(plan.kitem_slot), _ptr(plan.kreduce), int(H["kreduce"].shape[0]), plan.num_slots, _ptr(partial), nfl,
         _stream(q)))
     return dq, dk, dv

@@ -305,25 +305,48 @@ int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, void* out, flo
  */
 int32_t magi_default_tile_k(int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype);
 
+/* One sum of the split dK/dV pass: keys [key_start, key_start + key_len) of
+ * group kv_group are the sum, in slot order, of the partial results in
+ * slots slot_begin .. slot_begin + slot_count - 1. */
+typedef struct {
+  int32_t key_start, key_len, kv_group, slot_begin, slot_count;
+} magi_kv_reduce;
+
 /*
  * magi_schedule_kv -- AttnSlices -> key-major work list for the backward's
  * dK/dV pass.                                                    [host only]
  *
  * The transpose of magi_schedule: validates the slices the same way, cuts
- * the KEY axis at every slice boundary, tiles each piece into tiles of at
- * most tile_k keys (0 = magi_default_tile_k) and emits one item per (tile,
- * KV group), including tiles no row sees (their dK, dV are written as 0).
- * In these items q_start / q_len hold the first key and the key count;
- * [slice_begin, slice_end) indexes tile_slices, which lists the slices that
- * show some row a key of the tile, in query order.  cost = visible pairs of
- * the tile per head; order heaviest first with the KV groups interleaved.
- * Arguments, size query and errors as magi_schedule.
+ * the KEY axis at every slice boundary and tiles each piece into tiles of at
+ * most tile_k keys (0 = magi_default_tile_k).  tile_slices lists, per tile,
+ * the slices that show some row a key of the tile, in query order.
+ *
+ * A tile whose rows are many (the first chunk of a block-causal video is
+ * seen by every later chunk) would make one item far longer than the rest,
+ * so tiles are split into parts: runs of consecutive listed slices, closed
+ * when a part's visible pairs would pass T = max(largest single-slice part,
+ * total pairs / 1536 items).  A tile of one part gives one item per KV
+ * group that writes dK, dV directly (also tiles no row sees: their dK, dV
+ * are written as 0).  A tile of P > 1 parts gives P items per group, each
+ * writing an fp32 partial result into its own slot, and one reduce entry
+ * per group that sums the P slots in order (fixed order: deterministic).
+ *
+ * Items: q_start / q_len hold the first key and the key count;
+ * [slice_begin, slice_end) indexes tile_slices (the part's slices); cost =
+ * visible pairs of the item per head; heaviest first with the KV groups
+ * interleaved.  item_slot[i] (host, work_cap entries) is item i's slot or
+ * -1 (direct); reduce (host, reduce_cap entries) receives the sums;
+ * *num_slots the number of slots (each holds 2 x tile_k x head_dim fp32
+ * values: dK, then dV).  Size query: all output arrays NULL with caps 0
+ * fills the counts.  Errors as magi_schedule.
  */
 int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_slices,
                          int64_t nq, int64_t nk, int32_t hq, int32_t hkv,
                          int32_t head_dim, int32_t dtype, int32_t tile_k,
                          magi_work_item* work, int32_t work_cap, int32_t* num_work,
-                         int32_t* tile_slices, int32_t ts_cap, int32_t* num_tile_slices);
+                         int32_t* tile_slices, int32_t ts_cap, int32_t* num_tile_slices,
+                         int32_t* item_slot, magi_kv_reduce* reduce, int32_t reduce_cap,
+                         int32_t* num_reduce, int32_t* num_slots);
 
 /*
  * magi_ffa_bwd -- gradients of magi_ffa_fwd.              [device, async]
@@ -336,7 +359,9 @@ int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_slices,
  *   dq = scale dS k,  dk = scale dS^T q,  dv = P^T dout,
  * with dk and dv summed over the query heads of each KV group.  No atomics
  * and bitwise deterministic: a query-major pass (the forward's work list)
- * writes dq, a key-major pass (magi_schedule_kv's list) writes dk and dv.
+ * writes dq, a key-major pass (magi_schedule_kv's list) writes dk and dv
+ * (key tiles split into parts write partial sums that a last launch adds in
+ * a fixed order).
  * bf16: bf16 MFMA products with fp32 accumulation; P and dS are rounded to
  * bf16 for their products; the gradients are stored as bf16.  fp32: fp32
  * arithmetic throughout.
@@ -351,7 +376,13 @@ int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_slices,
  * delta        [device] fp32 [nq][hq] scratch the call fills first (caller
  *              owned, no other contents needed)
  * slices, qwork/q_tile_slices  the forward's schedule (magi_schedule)
- * kwork/k_tile_slices          magi_schedule_kv's output for the same slices
+ * kwork/k_tile_slices, kitem_slot, reduce/num_reduce, num_slots
+ *              [device] magi_schedule_kv's outputs for the same slices
+ *              (kitem_slot may be NULL when num_reduce = num_slots = 0)
+ * partial      [device] fp32 workspace of partial_floats >= num_slots x 2 x
+ *              128 x head_dim values, 16-byte aligned (caller owned, no
+ *              contents needed), for the parts of split key tiles; a last
+ *              launch sums them into dk, dv
  * Supported: head_dim 24 or 48; hq % hkv == 0; hq/hkv <= 64;
  * kv_tok_stride < 2^23.  Errors as magi_ffa_fwd.
  */
@@ -364,6 +395,8 @@ int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, const void* ou
                      const int32_t* q_tile_slices, int32_t num_q_tile_slices,
                      const magi_work_item* kwork, int32_t num_kwork,
                      const int32_t* k_tile_slices, int32_t num_k_tile_slices,
+                     const int32_t* kitem_slot, const magi_kv_reduce* reduce, int32_t num_reduce,
+                     int32_t num_slots, float* partial, int64_t partial_floats,
                      void* stream);
 
 #ifdef __cplusplus

@@ -187,44 +187,73 @@ def test_schedule_fuzz_raw_slices(trial):
 
 
 def check_schedule_kv(slices, nq, nk, hq, hkv, d, dtype=_lib.DTYPE_BF16, tile_k=0):
-    """Key-major schedule: every (key, group) owned once, each item's slice
-    list reproduces the mask's columns over its keys, costs are the visible
-    pairs, heaviest first with the groups interleaved, deterministic."""
-    work, ts = ops.schedule_kv(slices, nq, nk, hq, hkv, d, dtype, tile_k)
+    """Key-major schedule: every (key, group) owned once -- by a direct item
+    or by a reduce entry whose parts are items --, each owner's slices
+    reproduce the mask's columns over its keys, costs are the visible pairs,
+    heaviest first with the groups interleaved, deterministic."""
+    work, ts, slot, red, nslots = ops.schedule_kv(slices, nq, nk, hq, hkv, d, dtype, tile_k)
     tk = tile_k or 128
     owner = np.full((nk, hkv), -1)
     sl = [tuple(int(x) for x in s) for s in slices]
     full = oracle.slices_mask(sl, nq, nk) if nq * nk <= 4e7 else None
-    for i, (k0, kl, sb, se, g, cost) in enumerate(work):
-        assert 1 <= kl <= tk and 0 <= g < hkv and 0 <= sb <= se <= len(ts)
-        assert (owner[k0:k0 + kl, g] == -1).all(), "key owned twice"
-        owner[k0:k0 + kl, g] = i
-        mine = [sl[j] for j in ts[sb:se]]
+
+    def check_cols(k0, kl, idx, cost):
+        mine = [sl[j] for j in idx]
         assert [m[0] for m in mine] == sorted(m[0] for m in mine), "slices not in query order"
         if full is not None:
             sub = oracle.slices_mask(mine, nq, nk) if mine else np.zeros((nq, nk), bool)
             np.testing.assert_array_equal(sub[:, k0:k0 + kl], full[:, k0:k0 + kl])
-            assert cost == min(int(sub[:, k0:k0 + kl].sum()), 2 ** 31 - 1)
+            assert cost == int(sub[:, k0:k0 + kl].sum())
             for m in mine:   # every listed slice shows some row a key of the tile
                 assert oracle.slices_mask([m], nq, nk)[:, k0:k0 + kl].any()
+
+    by_slot = {}
+    for i, (k0, kl, sb, se, g, cost) in enumerate(work):
+        assert 1 <= kl <= tk and 0 <= g < hkv and 0 <= sb <= se <= len(ts)
+        if slot[i] < 0:
+            assert (owner[k0:k0 + kl, g] == -1).all(), "key owned twice"
+            owner[k0:k0 + kl, g] = i
+            check_cols(k0, kl, ts[sb:se], cost)
+        else:
+            assert 0 <= slot[i] < nslots and slot[i] not in by_slot and se > sb
+            by_slot[int(slot[i])] = i
+    assert sorted(by_slot) == list(range(nslots)), "slots not used exactly once"
+    for r, (k0, kl, g, s0, cnt) in enumerate(red):
+        assert cnt >= 2 and 0 <= g < hkv
+        items = [by_slot[s] for s in range(s0, s0 + cnt)]
+        for i in items:
+            assert tuple(work[i, [0, 1, 4]]) == (k0, kl, g)
+        # parts are consecutive runs of one tile list, in order
+        for a_, b_ in zip(items, items[1:]):
+            assert work[a_, 3] == work[b_, 2]
+        assert (owner[k0:k0 + kl, g] == -1).all(), "key owned twice"
+        owner[k0:k0 + kl, g] = len(work) + r
+        check_cols(k0, kl, ts[work[items[0], 2]:work[items[-1], 3]], int(work[items, 5].sum()))
+    assert sum(int(c) for c in red[:, 4]) == nslots if len(red) else nslots == 0
     assert (owner >= 0).all(), "a (key, group) has no owner"
     assert (np.diff(work[::hkv, 5]) <= 0).all(), "not heaviest-first"
     for r in range(len(work) // hkv):
         np.testing.assert_array_equal(work[r * hkv:(r + 1) * hkv, 4], np.arange(hkv))
-    w2, ts2 = ops.schedule_kv(slices, nq, nk, hq, hkv, d, dtype, tile_k)
-    np.testing.assert_array_equal(w2, work)
-    np.testing.assert_array_equal(ts2, ts)
-    return work, ts
+    again = ops.schedule_kv(slices, nq, nk, hq, hkv, d, dtype, tile_k)
+    for x, y in zip(again[:4], (work, ts, slot, red)):
+        np.testing.assert_array_equal(x, y)
+    assert again[4] == nslots
+    return work, ts, slot, red
 
 
 @pytest.mark.parametrize("name", ["tiny", "magi4.5b", "varlen", "stream"])
 def test_schedule_kv_workloads(name):
     wl = W.make_workload(name)
     sl = ops.build_slices(wl.seqs)
-    work, _ = check_schedule_kv(sl, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim,
-                                _lib.DTYPE_FP32 if wl.dtype == "fp32" else _lib.DTYPE_BF16)
+    work, _, slot, red = check_schedule_kv(sl, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim,
+                                           _lib.DTYPE_FP32 if wl.dtype == "fp32" else _lib.DTYPE_BF16)
     if wl.nq < 10000:
         assert work[:, 5].astype(np.int64).sum() == int(oracle.video_mask(wl.seqs, wl.nq, wl.nk).sum()) * wl.hkv
+    if name == "magi4.5b":
+        # block-causal, 4 chunks: a key tile of chunk c is seen by 4 - c chunks and
+        # is split into one part per chunk, so every item costs at most 128 x 1440
+        assert work[:, 5].max() <= 128 * 1440 and len(red) > 0
+        assert ((slot >= 0).sum()) == red[:, 4].sum()
 
 
 @pytest.mark.parametrize("trial", range(25))
@@ -381,6 +410,27 @@ def test_device_entry_points_validate_before_any_hip_call():
     assert ffa(nq=-2) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(nq=0, q=None, out=None) == _lib.MAGI_ERR_INVALID_ARG  # work for no rows
     assert b"work" in L.magi_last_error()
+
+
+def test_backward_entry_validates_split_workspace():
+    L = _lib.lib()
+    p = C.c_void_p(4096)  # never dereferenced: every call below fails validation
+
+    def bwd(**kw):
+        a = dict(nq=16, nk=16, hq=16, hkv=1, d=24, dt=0, qs=384, kvs=24, kvhs=24, os_=384, slot=p, red=p, nred=1,
+                 nslots=2, part=p, nfl=2 * 2 * 128 * 24, lse=p, delta=p)
+        a.update(kw)
+        return L.magi_ffa_bwd(p, p, p, p, p, a["lse"], p, p, p, a["delta"], a["nq"], a["nk"], a["hq"], a["hkv"],
+                              a["d"], a["dt"], a["qs"], a["kvs"], a["kvhs"], a["os_"], 0.0, p, 1, p, 1, p, 1, p, 1,
+                              p, 1, a["slot"], a["red"], a["nred"], a["nslots"], a["part"], a["nfl"], None)
+    assert bwd(part=None) == _lib.MAGI_ERR_INVALID_ARG            # split schedule without workspace
+    assert bwd(slot=None) == _lib.MAGI_ERR_INVALID_ARG
+    assert bwd(nfl=2 * 2 * 128 * 24 - 1) == _lib.MAGI_ERR_INVALID_ARG   # workspace too small
+    assert bwd(part=C.c_void_p(4100)) == _lib.MAGI_ERR_INVALID_ARG      # misaligned
+    assert bwd(nred=-1) == _lib.MAGI_ERR_INVALID_ARG
+    assert bwd(delta=None) == _lib.MAGI_ERR_INVALID_ARG
+    assert bwd(kvhs=20) == _lib.MAGI_ERR_INVALID_ARG                    # K/V layout overlaps
+    assert b"K/V" in L.magi_last_error() or b"overlap" in L.magi_last_error()
 
 
 def test_cross_slices():
