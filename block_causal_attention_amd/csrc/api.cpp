@@ -188,7 +188,7 @@ extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, con
                                 int32_t num_slices, const magi_work_item* qwork, int32_t num_qwork,
                                 const int32_t* q_tile_slices, int32_t num_q_tile_slices,
                                 const magi_work_item* kwork, int32_t num_kwork, const int32_t* k_tile_slices,
-                                int32_t num_k_tile_slices, const int32_t* kitem_slot,
+                                int32_t num_k_tile_slices, const int32_t* kitem_ext,
                                 const magi_kv_reduce* reduce, int32_t num_reduce, int32_t num_slots,
                                 float* partial, int64_t partial_floats, void* stream) {
   int32_t st;
@@ -220,8 +220,8 @@ extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, con
   if (num_qwork > 0 && nq == 0) return fail(MAGI_ERR_INVALID_ARG, "query work items for an empty query tensor");
   if (num_reduce < 0 || num_slots < 0) return fail(MAGI_ERR_INVALID_ARG, "negative reduce or slot count");
   if (num_reduce > 0 || num_slots > 0) {
-    if (reduce == nullptr || kitem_slot == nullptr || partial == nullptr)
-      return fail(MAGI_ERR_INVALID_ARG, "a split schedule needs kitem_slot, reduce and partial");
+    if (reduce == nullptr || kitem_ext == nullptr || partial == nullptr)
+      return fail(MAGI_ERR_INVALID_ARG, "a split schedule needs kitem_ext, reduce and partial");
     // slot layout fixed by the dK/dV kernel: 2 x 128 keys x head_dim fp32
     if (partial_floats < (int64_t)num_slots * 2 * 128 * head_dim)
       return fail(MAGI_ERR_INVALID_ARG, "partial holds %lld floats, %d slots need %lld", (long long)partial_floats,
@@ -262,7 +262,7 @@ extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, con
   a.num_kwork = num_kwork;
   a.k_tile_slices = k_tile_slices;
   a.num_k_tile_slices = num_k_tile_slices;
-  a.kitem_slot = kitem_slot;
+  a.kitem_ext = kitem_ext;
   a.reduce = reduce;
   a.num_reduce = num_reduce;
   a.num_slots = num_slots;

@@ -307,7 +307,7 @@ struct QRun {
 // First slice at or after list position si that shows some row one of the
 // item's keys [k0, k1); fills the run of rows that see them.
 __device__ __forceinline__ bool find_qrun(const SliceLists& L, int32_t slice_end, int32_t nq, int32_t nk,
-                                          int si, int32_t k0, int32_t k1, QRun& r) {
+                                          int si, int32_t k0, int32_t k1, int32_t w_lo, int32_t w_hi, QRun& r) {
   const int end = slice_end < L.num_tile_slices ? slice_end : L.num_tile_slices;
   for (si = si < 0 ? 0 : si; si < end; ++si) {
     const int sidx = const_ld(L.tile_slices + si);
@@ -315,7 +315,8 @@ __device__ __forceinline__ bool find_qrun(const SliceLists& L, int32_t slice_end
     const magi_attn_slice s = load_slice(L.slices, sidx);
     const int32_t ks = s.k_start > 0 ? s.k_start : 0;
     const int32_t ke = s.k_end < nk ? s.k_end : nk;
-    const int32_t qe = s.q_end < nq ? s.q_end : nq;
+    int32_t qe = s.q_end < nq ? s.q_end : nq;
+    if (qe > w_hi) qe = w_hi;  // the item's token window
     if (ks >= ke || s.q_start >= qe || ke <= k0 || ks >= k1) continue;
     const int32_t causal = s.mask_type == MAGI_MASK_CAUSAL;
     const int32_t koff = s.k_end - s.q_end;
@@ -323,6 +324,7 @@ __device__ __forceinline__ bool find_qrun(const SliceLists& L, int32_t slice_end
     const int32_t kmin = k0 > ks ? k0 : ks;
     int32_t t0 = s.q_start;
     if (causal && kmin - koff > t0) t0 = kmin - koff;
+    if (t0 < w_lo) t0 = w_lo;
     if (t0 >= qe) continue;
     r.si = si;
     r.t0 = t0;
@@ -355,6 +357,13 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
       wi.kv_group >= a.hkv)
     return;
   const int32_t k0 = wi.q_start;  // key-major item: [k0, k0 + klen) keys of group g
+  // partial slot (or -1) and token window of the item
+  int32_t slot = -1, w_lo = 0, w_hi = (int32_t)a.nq;
+  if (a.kitem_ext != nullptr) {
+    slot = const_ld(&a.kitem_ext[3 * blockIdx.x]);
+    w_lo = const_ld(&a.kitem_ext[3 * blockIdx.x + 1]);
+    w_hi = const_ld(&a.kitem_ext[3 * blockIdx.x + 2]);
+  }
   const int32_t klen = wi.q_len < kKeys ? wi.q_len : kKeys;
   const int32_t k1 = k0 + klen;
   const int g = wi.kv_group;
@@ -452,7 +461,7 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
     n.t0 = r.t0 + TQT;
     if (r.valid && n.t0 >= r.t_end)
       find_qrun(SliceLists{a.slices, a.num_slices, a.k_tile_slices, a.num_k_tile_slices}, wi.slice_end,
-                (int32_t)a.nq, (int32_t)a.nk, r.si + 1, k0, k1, n);
+                (int32_t)a.nq, (int32_t)a.nk, r.si + 1, k0, k1, w_lo, w_hi, n);
   };
 
   f32x16 dk[C::MB], dv[C::MB];
@@ -461,7 +470,7 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
 
   QRun cur;
   find_qrun(SliceLists{a.slices, a.num_slices, a.k_tile_slices, a.num_k_tile_slices}, wi.slice_end, (int32_t)a.nq,
-            (int32_t)a.nk, wi.slice_begin, k0, k1, cur);
+            (int32_t)a.nk, wi.slice_begin, k0, k1, w_lo, w_hi, cur);
   if (cur.valid) {
     load_tile(cur);
     store_tile(0);
@@ -540,7 +549,6 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
   // epilogue: lane (key) holds d = mb 32 + 8 grp + 4 h + r of dK^T / dV^T.
   // One part of a split tile stores its fp32 sums (dK unscaled) in its slot;
   // bwd_reduce adds the parts and writes dK, dV.
-  const int32_t slot = a.kitem_slot != nullptr ? const_ld(&a.kitem_slot[blockIdx.x]) : -1;
   if (kvalid && slot >= 0 && slot < a.num_slots) {
     float* pk = a.partial + (int64_t)slot * 2 * kKeys * D + (int64_t)(key - k0) * D;
     float* pv = pk + kKeys * D;
@@ -647,6 +655,12 @@ __global__ __launch_bounds__(kThreads32) void bwd_dkdv_f32(BwdArgs a) {
   if ((int)threadIdx.x >= klen) return;
   const int64_t key = (int64_t)wi.q_start + threadIdx.x;
   const int g = wi.kv_group;
+  int32_t slot = -1, w_lo = 0, w_hi = (int32_t)a.nq;
+  if (a.kitem_ext != nullptr) {
+    slot = a.kitem_ext[3 * blockIdx.x];
+    w_lo = a.kitem_ext[3 * blockIdx.x + 1];
+    w_hi = a.kitem_ext[3 * blockIdx.x + 2];
+  }
   const float* kr = reinterpret_cast<const float*>(a.k) + key * a.kv_stride + (int64_t)g * a.kv_hstride;
   const float* vr = reinterpret_cast<const float*>(a.v) + key * a.kv_stride + (int64_t)g * a.kv_hstride;
   float kv[D], vv[D], dkacc[D], dvacc[D];
@@ -668,7 +682,9 @@ __global__ __launch_bounds__(kThreads32) void bwd_dkdv_f32(BwdArgs a) {
       const int64_t f = key - ((int64_t)sl.k_end - sl.q_end);  // first row that sees the key
       r0 = f > r0 ? f : r0;
     }
-    const int64_t qe = sl.q_end < a.nq ? sl.q_end : a.nq;
+    if (r0 < w_lo) r0 = w_lo;
+    int64_t qe = sl.q_end < a.nq ? sl.q_end : a.nq;
+    if (qe > w_hi) qe = w_hi;
     for (int64_t r = r0; r < qe; ++r)
       for (int hh = 0; hh < G; ++hh) {
         const int head = g * G + hh;
@@ -691,7 +707,6 @@ __global__ __launch_bounds__(kThreads32) void bwd_dkdv_f32(BwdArgs a) {
         }
       }
   }
-  const int32_t slot = a.kitem_slot != nullptr ? a.kitem_slot[blockIdx.x] : -1;
   if (slot >= 0) {
     if (slot >= a.num_slots || key - wi.q_start >= kKeys) return;
     float* pk = a.partial + (int64_t)slot * 2 * kKeys * D + (key - wi.q_start) * D;

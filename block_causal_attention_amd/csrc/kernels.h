@@ -81,7 +81,7 @@ struct BwdArgs {
   int32_t num_kwork;
   const int32_t* k_tile_slices;
   int32_t num_k_tile_slices;
-  const int32_t* kitem_slot;     // [num_kwork] partial slot of a key-major item, or -1
+  const int32_t* kitem_ext;      // [num_kwork][3] {partial slot or -1, token window lo, hi} per key-major item
   const magi_kv_reduce* reduce;  // sums of the partial slots
   int32_t num_reduce;
   int32_t num_slots;

@@ -262,13 +262,13 @@ extern "C" int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_s
                                     int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype, int32_t tile_k,
                                     magi_work_item* work, int32_t work_cap, int32_t* num_work,
                                     int32_t* tile_slices, int32_t ts_cap, int32_t* num_tile_slices,
-                                    int32_t* item_slot, magi_kv_reduce* reduce, int32_t reduce_cap,
+                                    int32_t* item_ext, magi_kv_reduce* reduce, int32_t reduce_cap,
                                     int32_t* num_reduce, int32_t* num_slots) {
   if (num_work == nullptr || num_tile_slices == nullptr || num_reduce == nullptr || num_slots == nullptr)
     return fail(MAGI_ERR_INVALID_ARG, "a count pointer is NULL");
   if (work_cap < 0 || ts_cap < 0 || reduce_cap < 0) return fail(MAGI_ERR_INVALID_ARG, "negative capacity");
   if ((work == nullptr) != (work_cap == 0) || (tile_slices == nullptr) != (ts_cap == 0) ||
-      (item_slot == nullptr) != (work_cap == 0) || (reduce == nullptr) != (reduce_cap == 0))
+      (item_ext == nullptr) != (work_cap == 0) || (reduce == nullptr) != (reduce_cap == 0))
     return fail(MAGI_ERR_INVALID_ARG, "output array and capacity disagree (NULL needs cap 0)");
   // the query-major size query validates the slices (ranges, types, overlap)
   int32_t nw_q = 0, nts_q = 0;
@@ -323,27 +323,73 @@ extern "C" int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_s
       tiles.push_back(std::move(t));
     }
   }
-  // parts: runs of consecutive listed slices of at most T pairs (a single
-  // larger slice is a part of its own)
-  constexpr int64_t kTargetItems = 1536;  // ~3 items per workgroup slot of the whole GPU
-  const int64_t T = std::max<int64_t>(largest, (total * hkv + kTargetItems - 1) / kTargetItems);
-  struct Unit { size_t tile; int32_t a, b; int64_t cost; int32_t part, nparts; };
+  // Parts of at most T pairs: runs of consecutive listed slices, or one
+  // slice's rows cut into token windows of about equal pairs.  T aims at
+  // about 3072 items for the whole list (a few workgroups per SIMD over the
+  // whole pass), never below 128 x 128 pairs.
+  constexpr int64_t kTargetItems = 3072;
+  constexpr int64_t kMinPart = 128 * 128;
+  const int64_t T = std::max<int64_t>(kMinPart, (total * hkv + kTargetItems - 1) / kTargetItems);
+  (void)largest;
+  struct Unit { size_t tile; int32_t a, b; int64_t cost; int32_t part, nparts; int32_t lo, hi; };
   std::vector<Unit> units;
   int64_t nslots = 0, nred = 0;
+  const int32_t nq32 = (int32_t)nq;
   for (size_t ti = 0; ti < tiles.size(); ++ti) {
     const Tile& t = tiles[ti];
+    const std::vector<int32_t>& cv = cover[t.seg];
     const size_t first = units.size();
     int32_t a = 0;
     int64_t acc = 0;
+    auto close_run = [&](int32_t b) {
+      if (b > a) units.push_back({ti, a, b, acc, 0, 0, 0, nq32});
+      a = b;
+      acc = 0;
+    };
     for (int32_t j = 0; j < (int32_t)t.pairs.size(); ++j) {
-      if (j > a && acc + t.pairs[j] > T) {
-        units.push_back({ti, a, j, acc, 0, 0});
-        a = j;
-        acc = 0;
+      const int64_t c = t.pairs[j];
+      if (c > T) {
+        // this slice alone, its rows cut into windows of about c / nw pairs
+        close_run(j);
+        const magi_attn_slice& sl = slices[cv[j]];
+        const int64_t nw = (c + T - 1) / T;
+        int64_t run = 0, cut = 1;
+        const size_t wfirst = units.size();
+        int32_t lo = (int32_t)col_first(sl, t.k0);
+        const int32_t k_hi = (int32_t)std::min<int64_t>(t.k0 + t.len, sl.k_end);
+        const int32_t k_lo = (int32_t)std::max<int64_t>(t.k0, sl.k_start);
+        for (int32_t r = lo; r < sl.q_end; ++r) {
+          // keys of the tile row r sees
+          int64_t kend = k_hi;
+          if (sl.mask_type == MAGI_MASK_CAUSAL)
+            kend = std::min<int64_t>(kend, (int64_t)sl.k_end - sl.q_end + r + 1);
+          run += std::max<int64_t>(0, kend - k_lo);
+          if (cut < nw && run * nw >= c * cut) {
+            units.push_back({ti, j, j + 1, 0, 0, 0, lo, r + 1});
+            lo = r + 1;
+            ++cut;
+          }
+        }
+        if (lo < sl.q_end) units.push_back({ti, j, j + 1, 0, 0, 0, lo, sl.q_end});
+        // pairs of each window
+        for (size_t u = wfirst; u < units.size(); ++u) {
+          int64_t pc = 0;
+          for (int32_t r = units[u].lo; r < units[u].hi; ++r) {
+            int64_t kend = k_hi;
+            if (sl.mask_type == MAGI_MASK_CAUSAL)
+              kend = std::min<int64_t>(kend, (int64_t)sl.k_end - sl.q_end + r + 1);
+            pc += std::max<int64_t>(0, kend - k_lo);
+          }
+          units[u].cost = pc;
+        }
+        a = j + 1;
+        continue;
       }
-      acc += t.pairs[j];
+      if (j > a && acc + c > T) close_run(j);
+      acc += c;
     }
-    units.push_back({ti, a, (int32_t)t.pairs.size(), acc, 0, 0});
+    close_run((int32_t)t.pairs.size());
+    if (units.size() == first) units.push_back({ti, 0, 0, 0, 0, 0, 0, nq32});  // a tile no row sees
     const int32_t np = (int32_t)(units.size() - first);
     for (int32_t p = 0; p < np; ++p) {
       units[first + p].part = p;
@@ -390,7 +436,9 @@ extern "C" int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_s
     const Unit& u = units[ord[rank]];
     const Tile& t = tiles[u.tile];
     for (int32_t g = 0; g < hkv; ++g) {
-      item_slot[w] = u.nparts > 1 ? slot0[u.tile] + g * u.nparts + u.part : -1;
+      item_ext[3 * w] = u.nparts > 1 ? slot0[u.tile] + g * u.nparts + u.part : -1;
+      item_ext[3 * w + 1] = u.lo;
+      item_ext[3 * w + 2] = u.hi;
       work[w++] = {(int32_t)t.k0, (int32_t)t.len, tile_sb[u.tile] + u.a, tile_sb[u.tile] + u.b, g,
                    (int32_t)std::min<int64_t>(u.cost, INT32_MAX)};
     }

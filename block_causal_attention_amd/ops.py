@@ -146,9 +146,10 @@ def schedule(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim: 
 def schedule_kv(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim: int, dtype: int,
                 tile_k: int = 0):
     """magi_schedule_kv: slices -> key-major lists for the backward's dK/dV
-    pass: (work int32 [m, 6], tile_slices int32 [t], item_slot int32 [m],
+    pass: (work int32 [m, 6], tile_slices int32 [t], item_ext int32 [m, 3],
     reduce int32 [r, 5], num_slots).  q_start/q_len of an item are its keys;
-    item_slot is the partial slot of a part of a split key tile, else -1."""
+    item_ext holds {partial slot of a part of a split key tile or -1, first
+    query token, one past the last query token} of each item."""
     L = lib()
     s = np.ascontiguousarray(np.asarray(slices, np.int32).reshape(-1, 5))
     sp = s.ctypes.data_as(C.POINTER(AttnSlice)) if len(s) else None
@@ -157,14 +158,14 @@ def schedule_kv(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_di
                              None, 0, C.byref(nt), None, None, 0, C.byref(nr), C.byref(ns)))
     work = np.empty((max(nw.value, 1), 6), np.int32)
     ts = np.empty(max(nt.value, 1), np.int32)
-    slot = np.empty(max(nw.value, 1), np.int32)
+    ext = np.empty((max(nw.value, 1), 3), np.int32)
     red = np.empty((max(nr.value, 1), 5), np.int32)
     check(L.magi_schedule_kv(sp, len(s), nq, nk, hq, hkv, head_dim, dtype, tile_k,
                              work.ctypes.data_as(C.POINTER(WorkItem)), work.shape[0], C.byref(nw),
                              ts.ctypes.data_as(C.POINTER(C.c_int32)), ts.shape[0], C.byref(nt),
-                             slot.ctypes.data_as(C.POINTER(C.c_int32)),
+                             ext.ctypes.data_as(C.POINTER(C.c_int32)),
                              red.ctypes.data_as(C.POINTER(KvReduce)), red.shape[0], C.byref(nr), C.byref(ns)))
-    return work[:nw.value], ts[:nt.value], slot[:nw.value], red[:nr.value], ns.value
+    return work[:nw.value], ts[:nt.value], ext[:nw.value], red[:nr.value], ns.value
 
 
 @dataclass
@@ -184,7 +185,7 @@ class Plan:
     ready: Optional[torch.cuda.Event] = None  # recorded after the upload; ffa_fwd waits on it
     kwork: Optional[torch.Tensor] = None        # key-major lists (backward plans only)
     k_tile_slices: Optional[torch.Tensor] = None
-    kitem_slot: Optional[torch.Tensor] = None   # partial slot per key-major item, or -1
+    kitem_ext: Optional[torch.Tensor] = None    # {partial slot or -1, token window} per key-major item
     kreduce: Optional[torch.Tensor] = None      # int32 [r, 5] sums of split key tiles
     num_slots: int = 0
 
@@ -203,8 +204,8 @@ def make_plan(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim:
     work, ts = schedule(slices, nq, nk, hq, hkv, head_dim, code, tile_q)
     parts = [slices.reshape(-1), work.reshape(-1), ts.reshape(-1)]
     if backward:
-        kwork, kts, kslot, kred, nslots = schedule_kv(slices, nq, nk, hq, hkv, head_dim, code)
-        parts += [kwork.reshape(-1), kts.reshape(-1), kslot.reshape(-1), kred.reshape(-1)]
+        kwork, kts, kext, kred, nslots = schedule_kv(slices, nq, nk, hq, hkv, head_dim, code)
+        parts += [kwork.reshape(-1), kts.reshape(-1), kext.reshape(-1), kred.reshape(-1)]
     sizes = [max(p.size, 1) for p in parts]     # an empty list still gets one valid word
     # The copy runs on a side stream so it does not queue behind the work
     # already on the caller's stream (the previous attention launch); only
@@ -229,9 +230,9 @@ def make_plan(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim:
     host_arrays = {"slices": slices, "work": work, "tile_slices": ts}
     plan = Plan(nq, nk, hq, hkv, head_dim, code, views[0], views[1], views[2], host_arrays, ready)
     if backward:
-        plan.kwork, plan.k_tile_slices, plan.kitem_slot, plan.kreduce = views[3], views[4], views[5], views[6]
+        plan.kwork, plan.k_tile_slices, plan.kitem_ext, plan.kreduce = views[3], views[4], views[5], views[6]
         plan.num_slots = nslots
-        host_arrays.update(kwork=kwork, k_tile_slices=kts, kitem_slot=kslot, kreduce=kred)
+        host_arrays.update(kwork=kwork, k_tile_slices=kts, kitem_ext=kext, kreduce=kred)
     return plan
 
 
@@ -432,6 +433,6 @@ def ffa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor
         _ptr(plan.slices), int(H["slices"].shape[0]), _ptr(plan.work), plan.num_work,
         _ptr(plan.tile_slices), int(H["tile_slices"].shape[0]),
         _ptr(plan.kwork), int(H["kwork"].shape[0]), _ptr(plan.k_tile_slices), int(H["k_tile_slices"].shape[0]),
-        _ptr(plan.kitem_slot), _ptr(plan.kreduce), int(H["kreduce"].shape[0]), plan.num_slots, _ptr(partial), nfl,
+        _ptr(plan.kitem_ext), _ptr(plan.kreduce), int(H["kreduce"].shape[0]), plan.num_slots, _ptr(partial), nfl,
         _stream(q)))
     return dq, dk, dv

@@ -323,29 +323,32 @@ typedef struct {
  *
  * A tile whose rows are many (the first chunk of a block-causal video is
  * seen by every later chunk) would make one item far longer than the rest,
- * so tiles are split into parts: runs of consecutive listed slices, closed
- * when a part's visible pairs would pass T = max(largest single-slice part,
- * total pairs / 1536 items).  A tile of one part gives one item per KV
- * group that writes dK, dV directly (also tiles no row sees: their dK, dV
- * are written as 0).  A tile of P > 1 parts gives P items per group, each
- * writing an fp32 partial result into its own slot, and one reduce entry
- * per group that sums the P slots in order (fixed order: deterministic).
+ * and a short key list would leave the GPU with too few items, so tiles are
+ * split into parts of at most T visible pairs (T = max(128 x 128, total
+ * pairs / 3072 items)): runs of consecutive listed slices, or one slice's
+ * rows cut into query-token windows of about equal pairs.  A tile of one
+ * part gives one item per KV group that writes dK, dV directly (also tiles
+ * no row sees: their dK, dV are written as 0).  A tile of P > 1 parts gives
+ * P items per group, each writing an fp32 partial result into its own
+ * slot, and one reduce entry per group that sums the P slots in order
+ * (fixed order: deterministic, no atomics).
  *
  * Items: q_start / q_len hold the first key and the key count;
  * [slice_begin, slice_end) indexes tile_slices (the part's slices); cost =
  * visible pairs of the item per head; heaviest first with the KV groups
- * interleaved.  item_slot[i] (host, work_cap entries) is item i's slot or
- * -1 (direct); reduce (host, reduce_cap entries) receives the sums;
- * *num_slots the number of slots (each holds 2 x tile_k x head_dim fp32
- * values: dK, then dV).  Size query: all output arrays NULL with caps 0
- * fills the counts.  Errors as magi_schedule.
+ * interleaved.  item_ext (host, 3 x work_cap entries) receives per item
+ * {slot or -1 (direct), first query token, one past the last}: the item
+ * only takes rows of tokens in that window.  reduce (host, reduce_cap
+ * entries) receives the sums; *num_slots the number of slots (each holds 2
+ * x tile_k x head_dim fp32 values: dK, then dV).  Size query: all output
+ * arrays NULL with caps 0 fills the counts.  Errors as magi_schedule.
  */
 int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_slices,
                          int64_t nq, int64_t nk, int32_t hq, int32_t hkv,
                          int32_t head_dim, int32_t dtype, int32_t tile_k,
                          magi_work_item* work, int32_t work_cap, int32_t* num_work,
                          int32_t* tile_slices, int32_t ts_cap, int32_t* num_tile_slices,
-                         int32_t* item_slot, magi_kv_reduce* reduce, int32_t reduce_cap,
+                         int32_t* item_ext, magi_kv_reduce* reduce, int32_t reduce_cap,
                          int32_t* num_reduce, int32_t* num_slots);
 
 /*
@@ -376,9 +379,10 @@ int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_slices,
  * delta        [device] fp32 [nq][hq] scratch the call fills first (caller
  *              owned, no other contents needed)
  * slices, qwork/q_tile_slices  the forward's schedule (magi_schedule)
- * kwork/k_tile_slices, kitem_slot, reduce/num_reduce, num_slots
+ * kwork/k_tile_slices, kitem_ext, reduce/num_reduce, num_slots
  *              [device] magi_schedule_kv's outputs for the same slices
- *              (kitem_slot may be NULL when num_reduce = num_slots = 0)
+ *              (kitem_ext may be NULL when num_reduce = num_slots = 0: every
+ *              item then writes directly and takes all rows)
  * partial      [device] fp32 workspace of partial_floats >= num_slots x 2 x
  *              128 x head_dim values, 16-byte aligned (caller owned, no
  *              contents needed), for the parts of split key tiles; a last
@@ -395,7 +399,7 @@ int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, const void* ou
                      const int32_t* q_tile_slices, int32_t num_q_tile_slices,
                      const magi_work_item* kwork, int32_t num_kwork,
                      const int32_t* k_tile_slices, int32_t num_k_tile_slices,
-                     const int32_t* kitem_slot, const magi_kv_reduce* reduce, int32_t num_reduce,
+                     const int32_t* kitem_ext, const magi_kv_reduce* reduce, int32_t num_reduce,
                      int32_t num_slots, float* partial, int64_t partial_floats,
                      void* stream);
 

@@ -191,29 +191,54 @@ def check_schedule_kv(slices, nq, nk, hq, hkv, d, dtype=_lib.DTYPE_BF16, tile_k=
     or by a reduce entry whose parts are items --, each owner's slices
     reproduce the mask's columns over its keys, costs are the visible pairs,
     heaviest first with the groups interleaved, deterministic."""
-    work, ts, slot, red, nslots = ops.schedule_kv(slices, nq, nk, hq, hkv, d, dtype, tile_k)
+    work, ts, ext, red, nslots = ops.schedule_kv(slices, nq, nk, hq, hkv, d, dtype, tile_k)
+    slot, wlo, whi = ext[:, 0], ext[:, 1], ext[:, 2]
     tk = tile_k or 128
     owner = np.full((nk, hkv), -1)
     sl = [tuple(int(x) for x in s) for s in slices]
     full = oracle.slices_mask(sl, nq, nk) if nq * nk <= 4e7 else None
 
-    def check_cols(k0, kl, idx, cost):
+    smask = {}
+
+    def slice_mask(j):
+        if j not in smask:
+            smask[j] = oracle.slices_mask([sl[j]], nq, nk)
+        return smask[j]
+
+    def part_mask(i, k0, kl):
+        """rows x tile keys an item covers: its slices, clipped to its token window"""
+        m = np.zeros((nq, kl), bool)
+        for j in ts[work[i, 2]:work[i, 3]]:
+            m |= slice_mask(int(j))[:, k0:k0 + kl]
+        m[:wlo[i]] = False
+        m[whi[i]:] = False
+        return m
+
+    def check_cols(k0, kl, items):
+        idx = [j for i in items for j in ts[work[i, 2]:work[i, 3]]]
         mine = [sl[j] for j in idx]
-        assert [m[0] for m in mine] == sorted(m[0] for m in mine), "slices not in query order"
+        for i in items:
+            s_ = [sl[j] for j in ts[work[i, 2]:work[i, 3]]]
+            assert [m[0] for m in s_] == sorted(m[0] for m in s_), "slices not in query order"
         if full is not None:
-            sub = oracle.slices_mask(mine, nq, nk) if mine else np.zeros((nq, nk), bool)
-            np.testing.assert_array_equal(sub[:, k0:k0 + kl], full[:, k0:k0 + kl])
-            assert cost == int(sub[:, k0:k0 + kl].sum())
-            for m in mine:   # every listed slice shows some row a key of the tile
-                assert oracle.slices_mask([m], nq, nk)[:, k0:k0 + kl].any()
+            cover = np.zeros((nq, kl), np.int32)
+            for i in items:
+                pm = part_mask(i, k0, kl)
+                assert int(work[i, 5]) == int(pm.sum()), "item cost is not its visible pairs"
+                cover += pm
+            assert cover.max(initial=0) <= 1, "a (row, key) pair covered twice"
+            np.testing.assert_array_equal(cover.astype(bool), full[:, k0:k0 + kl])
+            for j in set(int(x) for x in idx):   # every listed slice shows some row a key of the tile
+                assert slice_mask(j)[:, k0:k0 + kl].any()
 
     by_slot = {}
     for i, (k0, kl, sb, se, g, cost) in enumerate(work):
         assert 1 <= kl <= tk and 0 <= g < hkv and 0 <= sb <= se <= len(ts)
+        assert 0 <= wlo[i] <= whi[i] <= nq
         if slot[i] < 0:
             assert (owner[k0:k0 + kl, g] == -1).all(), "key owned twice"
             owner[k0:k0 + kl, g] = i
-            check_cols(k0, kl, ts[sb:se], cost)
+            check_cols(k0, kl, [i])
         else:
             assert 0 <= slot[i] < nslots and slot[i] not in by_slot and se > sb
             by_slot[int(slot[i])] = i
@@ -223,19 +248,20 @@ def check_schedule_kv(slices, nq, nk, hq, hkv, d, dtype=_lib.DTYPE_BF16, tile_k=
         items = [by_slot[s] for s in range(s0, s0 + cnt)]
         for i in items:
             assert tuple(work[i, [0, 1, 4]]) == (k0, kl, g)
-        # parts are consecutive runs of one tile list, in order
+        # parts follow the tile list in order: a run of slices, or windows of one slice
         for a_, b_ in zip(items, items[1:]):
-            assert work[a_, 3] == work[b_, 2]
+            assert work[a_, 3] == work[b_, 2] or (work[a_, 2] == work[b_, 2] and work[a_, 3] == work[b_, 3]
+                                                  and whi[a_] <= wlo[b_])
         assert (owner[k0:k0 + kl, g] == -1).all(), "key owned twice"
         owner[k0:k0 + kl, g] = len(work) + r
-        check_cols(k0, kl, ts[work[items[0], 2]:work[items[-1], 3]], int(work[items, 5].sum()))
+        check_cols(k0, kl, items)
     assert sum(int(c) for c in red[:, 4]) == nslots if len(red) else nslots == 0
     assert (owner >= 0).all(), "a (key, group) has no owner"
     assert (np.diff(work[::hkv, 5]) <= 0).all(), "not heaviest-first"
     for r in range(len(work) // hkv):
         np.testing.assert_array_equal(work[r * hkv:(r + 1) * hkv, 4], np.arange(hkv))
     again = ops.schedule_kv(slices, nq, nk, hq, hkv, d, dtype, tile_k)
-    for x, y in zip(again[:4], (work, ts, slot, red)):
+    for x, y in zip(again[:4], (work, ts, ext, red)):
         np.testing.assert_array_equal(x, y)
     assert again[4] == nslots
     return work, ts, slot, red
@@ -250,9 +276,10 @@ def test_schedule_kv_workloads(name):
     if wl.nq < 10000:
         assert work[:, 5].astype(np.int64).sum() == int(oracle.video_mask(wl.seqs, wl.nq, wl.nk).sum()) * wl.hkv
     if name == "magi4.5b":
-        # block-causal, 4 chunks: a key tile of chunk c is seen by 4 - c chunks and
-        # is split into one part per chunk, so every item costs at most 128 x 1440
-        assert work[:, 5].max() <= 128 * 1440 and len(red) > 0
+        # block-causal, 4 chunks: a key tile of chunk c is seen by 4 - c chunks;
+        # each chunk's rows are cut into token windows, so items cost at most a
+        # quarter of 128 x 1440 pairs and there are a few thousand of them
+        assert work[:, 5].max() <= 128 * 1440 // 3 and len(red) > 0 and len(work) >= 3000
         assert ((slot >= 0).sum()) == red[:, 4].sum()
 
 
