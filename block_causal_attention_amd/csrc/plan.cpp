@@ -325,9 +325,9 @@ extern "C" int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_s
   }
   // Parts of at most T pairs: runs of consecutive listed slices, or one
   // slice's rows cut into token windows of about equal pairs.  T aims at
-  // about 3072 items for the whole list (a few workgroups per SIMD over the
+  // about 8192 items for the whole list (several workgroups per SIMD over the
   // whole pass), never below 128 x 128 pairs.
-  constexpr int64_t kTargetItems = 3072;
+  constexpr int64_t kTargetItems = 8192;
   constexpr int64_t kMinPart = 128 * 128;
   const int64_t T = std::max<int64_t>(kMinPart, (total * hkv + kTargetItems - 1) / kTargetItems);
   (void)largest;

@@ -325,7 +325,7 @@ typedef struct {
  * seen by every later chunk) would make one item far longer than the rest,
  * and a short key list would leave the GPU with too few items, so tiles are
  * split into parts of at most T visible pairs (T = max(128 x 128, total
- * pairs / 3072 items)): runs of consecutive listed slices, or one slice's
+ * pairs / 8192 items)): runs of consecutive listed slices, or one slice's
  * rows cut into query-token windows of about equal pairs.  A tile of one
  * part gives one item per KV group that writes dK, dV directly (also tiles
  * no row sees: their dK, dV are written as 0).  A tile of P > 1 parts gives
