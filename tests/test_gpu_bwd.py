@@ -188,3 +188,17 @@ def test_bwd_group_major_kv_identical(d):
     assert b[1].stride() == kg.stride() and b[2].stride() == vg.stride()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_bwd_fuzz_raw_slices(case):
+    # seeded random shapes, group sizes and slice lists against the oracle's gradients
+    from test_gpu_parity import random_slices
+    rng = np.random.Generator(np.random.PCG64(5000 + case))
+    d, hkv = int(rng.choice([24, 48])), int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 3, 8, 16, 64]))
+    nq, nk = int(rng.integers(1, 200)), int(rng.integers(1, 260))
+    sl = random_slices(rng, nq, nk)
+    note(f"bwd fuzz case {case}: d={d} G={G} hkv={hkv} nq={nq} nk={nk} slices={len(sl)}")
+    bwd_case(rand((nq, G * hkv, d), 6000 + case), rand((nk, hkv, d), 7000 + case), rand((nk, hkv, d), 8000 + case),
+             rand((nq, G * hkv, d), 9000 + case), sl, "bf16")

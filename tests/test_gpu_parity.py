@@ -255,6 +255,44 @@ def test_ffa_no_keys_and_scale():
     ffa_case(rand((30, 16, 24), 11, 3.0), rand((50, 1, 24), 12, 3.0), rand((50, 1, 24), 13), sl, "bf16", scale=0.05)
 
 
+def random_slices(rng, nq, nk):
+    """Disjoint AttnSlices: query bands, each with a few disjoint key ranges,
+    FULL or CAUSAL (bottom-right aligned), some bands and gaps left empty."""
+    slices = []
+    q = 0
+    while q < nq:
+        qe = min(nq, q + int(rng.integers(1, 60)))
+        if rng.random() < 0.85:
+            k = int(rng.integers(0, 8))
+            while k < nk:
+                ke = min(nk, k + int(rng.integers(1, 90)))
+                slices.append((q, qe, k, ke, int(rng.random() < 0.4)))
+                k = ke + int(rng.integers(0, 20))
+        q = qe + int(rng.integers(0, 5))
+    return np.array(slices, np.int32).reshape(-1, 5)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_ffa_fuzz_raw_slices(case):
+    # seeded random shapes, group sizes and slice lists against the oracle
+    rng = np.random.Generator(np.random.PCG64(1000 + case))
+    d, hkv = int(rng.choice([24, 48])), int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 2, 3, 5, 8, 16, 32]))
+    nq, nk = int(rng.integers(1, 260)), int(rng.integers(1, 330))
+    sl = random_slices(rng, nq, nk)
+    note(f"ffa fuzz case {case}: d={d} G={G} hkv={hkv} nq={nq} nk={nk} slices={len(sl)}")
+    ffa_case(rand((nq, G * hkv, d), 2000 + case), rand((nk, hkv, d), 3000 + case), rand((nk, hkv, d), 4000 + case),
+             sl, "bf16")
+
+
+@pytest.mark.parametrize("d", [24, 48])
+def test_ffa_largest_group(d):
+    # 256 query heads over one KV group: one token per work item
+    note(f"ffa G=256 d={d}")
+    sl = ops.build_slices([W.SeqDesc(9, 3, 3, 0, 0, (-1, -1, -1), 1, 1, 9)])
+    ffa_case(rand((27, 256, d), 60), rand((27, 1, d), 61), rand((27, 1, d), 62), sl, "bf16")
+
+
 def to_group_major(t):
     """a copy of a token-major [n, heads, d] tensor stored group-major"""
     g = ops.kv_group_major(t.shape[0], t.shape[1], t.shape[2], t.dtype, t.device)
