@@ -43,7 +43,9 @@ using namespace dev;
 constexpr int kRows = 256;      // query rows per dQ work item (the forward's items)
 constexpr int kKeys = 128;      // keys per dK/dV work item (4 waves x 32)
 constexpr int NT = 512;         // threads per workgroup of the bf16 dQ pass
-constexpr int NTK = 2 * kKeys;  // threads per workgroup of the bf16 dK/dV pass
+// 32-key blocks per wave of the bf16 dK/dV pass (head_dim 24 / 48).  Two blocks per
+// wave at head_dim 24 need 256 VGPRs (2 waves per SIMD) and measured no faster.
+constexpr int KB24 = 1, KB48 = 1;
 constexpr int TK = 64;          // keys per K/V tile (dQ pass)
 constexpr int TQ = 64;          // query rows per Q/dO tile (dK/dV pass)
 constexpr int kThreads32 = 256;  // fp32 kernels
@@ -340,9 +342,13 @@ __device__ __forceinline__ bool find_qrun(const SliceLists& L, int32_t slice_end
   return false;
 }
 
-template <int D, bool PRESCALED>
-__global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
+// KB: 32-key blocks per wave.  The item's kKeys keys are spread over
+// kKeys / (32 KB) waves; KB = 2 lets one wave's Q'/dO' operand reads (and
+// their transposes) serve 64 keys, halving those LDS reads per key.
+template <int D, bool PRESCALED, int KB>
+__global__ __launch_bounds__(2 * kKeys / KB, 2) void bwd_dkdv_bf16(BwdArgs a) {
   using C = BCfg<D>;
+  constexpr int NTK = 2 * kKeys / KB;                // threads per workgroup
   constexpr int NCH = (TQ * C::CH + NTK - 1) / NTK;  // 16-byte chunks per thread per tile (Q and dO each)
   __shared__ __attribute__((aligned(16))) __bf16 Qs[2][TQ * C::PITCH];
   __shared__ __attribute__((aligned(16))) __bf16 Os[2][TQ * C::PITCH];
@@ -368,7 +374,10 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
   const int32_t k1 = k0 + klen;
   const int g = wi.kv_group;
   const float c = a.scale * kLog2e;
+  const float cinv = 1.0f / c;
   const int TQT = TQ / G;  // tokens per tile
+  // floor(row / G) = (row * ginv) >> 16 for row < 64, G <= 64
+  const int32_t ginv = ((1 << 16) + G - 1) / G;
   const int tq_rows = TQT * G;
 
   // zero padding columns D+2.. of both buffers once; columns D, D+1 are
@@ -380,13 +389,16 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
       Os[b][row * C::PITCH + col] = (__bf16)0.0f;
     }
 
-  // this lane's key (column n of the MFMA): K and V rows as B operands with
-  // the two ones columns that meet the augmented slots
-  const int32_t key = k0 + wave * 32 + ln;
-  const bool kvalid = key < k1;
-  bf16x8 kreg[C::KS], vreg[C::KS];
-  {
-    const int32_t kk = kvalid ? key : k0;
+  // this lane's keys (column n of the MFMA, one per key block): K and V
+  // rows as B operands with the two ones columns that meet the augmented slots
+  int32_t key[KB];
+  bool kvalid[KB];
+  bf16x8 kreg[KB][C::KS], vreg[KB][C::KS];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    key[kb] = k0 + (wave * KB + kb) * 32 + ln;
+    kvalid[kb] = key[kb] < k1;
+    const int32_t kk = kvalid[kb] ? key[kb] : k0;
     const __bf16* krow = reinterpret_cast<const __bf16*>(a.k) + (int64_t)kk * a.kv_stride + (int64_t)g * a.kv_hstride;
     const __bf16* vrow = reinterpret_cast<const __bf16*>(a.v) + (int64_t)kk * a.kv_stride + (int64_t)g * a.kv_hstride;
 #pragma unroll
@@ -399,9 +411,9 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
       } else if (d0 == D) {
         x[0] = x[1] = y[0] = y[1] = (__bf16)1.0f;
       }
-      if (!kvalid) x = y = (bf16x8){};
-      kreg[ks] = x;
-      vreg[ks] = y;
+      if (!kvalid[kb]) x = y = (bf16x8){};
+      kreg[kb][ks] = x;
+      vreg[kb][ks] = y;
     }
   }
 
@@ -435,7 +447,7 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
       const int64_t idx = tok * a.hq + g * G + tid % G;
       float l2 = a.lse[idx] * kLog2e;
       if (!(l2 > -INFINITY && l2 < INFINITY)) l2 = 0.f;
-      split_bf16(-l2 / c, aq0, aq1);
+      split_bf16(-l2 * cinv, aq0, aq1);
       split_bf16(-a.delta[idx], ao0, ao1);
     }
   };
@@ -464,9 +476,11 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
                 (int32_t)a.nq, (int32_t)a.nk, r.si + 1, k0, k1, w_lo, w_hi, n);
   };
 
-  f32x16 dk[C::MB], dv[C::MB];
+  f32x16 dk[KB][C::MB], dv[KB][C::MB];
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb) dk[mb] = dv[mb] = (f32x16){};
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) dk[kb][mb] = dv[kb][mb] = (f32x16){};
 
   QRun cur;
   find_qrun(SliceLists{a.slices, a.num_slices, a.k_tile_slices, a.num_k_tile_slices}, wi.slice_end, (int32_t)a.nq,
@@ -494,39 +508,58 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
     const __attribute__((address_space(3))) __bf16* Ot = (const __attribute__((address_space(3))) __bf16*)Os[buf];
 #pragma unroll
     for (int rb = 0; rb < TQ / 32; ++rb) {
-      // S' = Q' . K^T and dP' = dO' . V^T (rows on M, keys on N)
-      f32x16 s = {}, dp = {};
+      // S' = Q' . K^T and dP' = dO' . V^T (rows on M, keys on N); the A
+      // operands are read once for all KB key blocks
+      f32x16 s[KB], dp[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[kb] = dp[kb] = (f32x16){};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qb[(rb * 32 + ln) * C::PITCH + 16 * ks + 8 * h]);
         const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&Ob[(rb * 32 + ln) * C::PITCH + 16 * ks + 8 * h]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vreg[ks], dp, 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[kb][ks], s[kb], 0, 0, 0);
+          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vreg[kb][ks], dp[kb], 0, 0, 0);
+        }
       }
       if (!full) {
-        // element i holds row 8 (i / 4) + 4 h + i % 4 of this 32-row block
+        // Element i holds row 8 (i / 4) + 4 h + i % 4 of this 32-row block,
+        // token tt = row / G of the tile.  The key of block kb is seen by
+        // tokens lo <= tt < hi: hi = ntok (0 if the key is outside the
+        // slice or the item), lo = key - koff - t0 for a causal slice
+        // (bottom-right aligned: token t sees k < koff + t + 1).  The hiding
+        // mask is built by integer arithmetic and applied with a bit select,
+        // so no lane-mask registers are tied up.
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = rb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
-          const int tt = row / G;
-          const int32_t tok = cur.t0 + tt;
-          bool vis = kvalid && row < tq_rows && tt < ntok && key >= cur.ks && key < cur.ke;
-          if (cur.causal) vis = vis && key < cur.koff + tok + 1;
-          if (!vis) s[i] = -INFINITY;
+        for (int kb = 0; kb < KB; ++kb) {
+          const bool kin = kvalid[kb] && key[kb] >= cur.ks && key[kb] < cur.ke;
+          const int32_t hi = kin ? ntok : 0;
+          const int32_t lo = cur.causal ? key[kb] - cur.koff - cur.t0 : -(1 << 30);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = rb * 32 + 8 * (i / 4) + 4 * h + (i % 4);  // < 64
+            const int32_t tt = (row * ginv) >> 16;                    // row / G
+            const uint32_t hide = (uint32_t)(((tt - lo) | (hi - 1 - tt)) >> 31);
+            s[kb][i] = __uint_as_float((__float_as_uint(s[kb][i]) & ~hide) | (0xff800000u & hide));
+          }
         }
       }
       // P and dS = P * dP', rounded to bf16 in the B-operand layout
-      bf16x8 pb[2], dsb[2];
+      bf16x8 pb[KB][2], dsb[KB][2];
 #pragma unroll
-      for (int i2 = 0; i2 < 2; ++i2)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = PRESCALED ? s[8 * i2 + e] : s[8 * i2 + e] * c;
-          const float p = __builtin_amdgcn_exp2f(x);
-          pb[i2][e] = (__bf16)p;
-          dsb[i2][e] = (__bf16)(p * dp[8 * i2 + e]);
-        }
-      // dV^T += dO^T . P and dK^T += Q^T . dS (transposed LDS reads)
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = PRESCALED ? s[kb][8 * i2 + e] : s[kb][8 * i2 + e] * c;
+            const float p = __builtin_amdgcn_exp2f(x);
+            pb[kb][i2][e] = (__bf16)p;
+            dsb[kb][i2][e] = (__bf16)(p * dp[kb][8 * i2 + e]);
+          }
+      // dV^T += dO^T . P and dK^T += Q^T . dS (transposed LDS reads, shared
+      // by the key blocks)
 #pragma unroll
       for (int i2 = 0; i2 < 2; ++i2) {
         const int qrow = rb * 32 + 16 * i2 + 4 * h + li / 4;
@@ -535,8 +568,11 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
           const int dcol = mb * 32 + dgrp + 4 * (li % 4);
           const bf16x8 ot8 = read_tr8(Ot + qrow * C::PITCH + dcol, C::PITCH);
           const bf16x8 qt8 = read_tr8(Qt + qrow * C::PITCH + dcol, C::PITCH);
-          dv[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot8, pb[i2], dv[mb], 0, 0, 0);
-          dk[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt8, dsb[i2], dk[mb], 0, 0, 0);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            dv[kb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot8, pb[kb][i2], dv[kb][mb], 0, 0, 0);
+            dk[kb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt8, dsb[kb][i2], dk[kb][mb], 0, 0, 0);
+          }
         }
       }
     }
@@ -549,40 +585,45 @@ __global__ __launch_bounds__(NTK, 2) void bwd_dkdv_bf16(BwdArgs a) {
   // epilogue: lane (key) holds d = mb 32 + 8 grp + 4 h + r of dK^T / dV^T.
   // One part of a split tile stores its fp32 sums (dK unscaled) in its slot;
   // bwd_reduce adds the parts and writes dK, dV.
-  if (kvalid && slot >= 0 && slot < a.num_slots) {
-    float* pk = a.partial + (int64_t)slot * 2 * kKeys * D + (int64_t)(key - k0) * D;
-    float* pv = pk + kKeys * D;
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
+  for (int kb = 0; kb < KB; ++kb) {
+    if (kvalid[kb] && slot >= 0 && slot < a.num_slots) {
+      float* pk = a.partial + (int64_t)slot * 2 * kKeys * D + (int64_t)(key[kb] - k0) * D;
+      float* pv = pk + kKeys * D;
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int d = mb * 32 + 8 * grp + 4 * h;
-        if (d < D) {
-          *reinterpret_cast<float4*>(pk + d) =
-              make_float4(dk[mb][4 * grp], dk[mb][4 * grp + 1], dk[mb][4 * grp + 2], dk[mb][4 * grp + 3]);
-          *reinterpret_cast<float4*>(pv + d) =
-              make_float4(dv[mb][4 * grp], dv[mb][4 * grp + 1], dv[mb][4 * grp + 2], dv[mb][4 * grp + 3]);
-        }
-      }
-  } else if (kvalid && slot < 0) {
-    __bf16* dkp = reinterpret_cast<__bf16*>(a.dk) + (int64_t)key * a.kv_stride + (int64_t)g * a.kv_hstride;
-    __bf16* dvp = reinterpret_cast<__bf16*>(a.dv) + (int64_t)key * a.kv_stride + (int64_t)g * a.kv_hstride;
+      for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int d = mb * 32 + 8 * grp + 4 * h;
-        if (d < D) {
-          bf16x4 wk, wv;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            wk[r] = (__bf16)(dk[mb][4 * grp + r] * a.scale);
-            wv[r] = (__bf16)dv[mb][4 * grp + r];
+        for (int grp = 0; grp < 4; ++grp) {
+          const int d = mb * 32 + 8 * grp + 4 * h;
+          if (d < D) {
+            const f32x16& K = dk[kb][mb];
+            const f32x16& V = dv[kb][mb];
+            *reinterpret_cast<float4*>(pk + d) = make_float4(K[4 * grp], K[4 * grp + 1], K[4 * grp + 2], K[4 * grp + 3]);
+            *reinterpret_cast<float4*>(pv + d) = make_float4(V[4 * grp], V[4 * grp + 1], V[4 * grp + 2], V[4 * grp + 3]);
           }
-          *reinterpret_cast<bf16x4*>(dkp + d) = wk;
-          *reinterpret_cast<bf16x4*>(dvp + d) = wv;
         }
-      }
+    } else if (kvalid[kb] && slot < 0) {
+      __bf16* dkp =
+          reinterpret_cast<__bf16*>(a.dk) + (int64_t)key[kb] * a.kv_stride + (int64_t)g * a.kv_hstride;
+      __bf16* dvp =
+          reinterpret_cast<__bf16*>(a.dv) + (int64_t)key[kb] * a.kv_stride + (int64_t)g * a.kv_hstride;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          const int d = mb * 32 + 8 * grp + 4 * h;
+          if (d < D) {
+            bf16x4 wk, wv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              wk[r] = (__bf16)(dk[kb][mb][4 * grp + r] * a.scale);
+              wv[r] = (__bf16)dv[kb][mb][4 * grp + r];
+            }
+            *reinterpret_cast<bf16x4*>(dkp + d) = wk;
+            *reinterpret_cast<bf16x4*>(dvp + d) = wv;
+          }
+        }
+    }
   }
 }
 
@@ -769,6 +810,7 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
 
 template <int D>
 hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
+  constexpr int KB = D == 24 ? KB24 : KB48;
   const bool bf = a.dtype == MAGI_DTYPE_BF16;
   const int64_t nvec = a.nq * a.hq;
   if (nvec > 0) {
@@ -793,9 +835,9 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
     if (!bf)
       hipLaunchKernelGGL((bwd_dkdv_f32<D>), grid, dim3(kThreads32), 0, stream, a);
     else if (pre)
-      hipLaunchKernelGGL((bwd_dkdv_bf16<D, true>), grid, dim3(NTK), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_bf16<D, true, KB>), grid, dim3(2 * kKeys / KB), 0, stream, a);
     else
-      hipLaunchKernelGGL((bwd_dkdv_bf16<D, false>), grid, dim3(NTK), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_bf16<D, false, KB>), grid, dim3(2 * kKeys / KB), 0, stream, a);
   }
   if (a.num_reduce > 0) {
     const dim3 grid(a.num_reduce);
