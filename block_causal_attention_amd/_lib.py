@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "MAGI_OK", -1: "MAGI_ERR_INVALID_ARG", -2: "MAGI_ERR_UNSUPPOR
                 -3: "MAGI_ERR_BUFFER_TOO_SMALL", -4: "MAGI_ERR_OVERLAP", -5: "MAGI_ERR_HIP"}
 
 EXPORTS = ("magi_version", "magi_last_error", "magi_slices_build", "magi_default_tile_q",
-           "magi_schedule", "magi_qknorm_rope", "magi_ffa_fwd", "magi_default_tile_k",
+           "magi_schedule", "magi_qknorm_rope", "magi_ffa_fwd", "magi_ffa_fwd_qknorm", "magi_default_tile_k",
            "magi_schedule_kv", "magi_ffa_bwd", "magi_slices_cross", "magi_slices_ring")
 
 
@@ -89,6 +89,8 @@ def lib() -> C.CDLL:
                                        vp, vp]
         L.magi_ffa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i64, i64, i64, i64,
                                    C.c_float, vp, vp, i32, vp, i32, vp, i32, vp]
+        L.magi_ffa_fwd_qknorm.argtypes = L.magi_ffa_fwd.argtypes[:-1] + [vp, i32, C.c_float, vp, vp, C.c_float,
+                                                                         vp, i64, vp]
         L.magi_default_tile_k.argtypes = [i32, i32, i32, i32]
         L.magi_slices_cross.argtypes = [C.POINTER(CrossDesc), i32, C.POINTER(AttnSlice), i32, C.POINTER(i32)]
         L.magi_slices_ring.argtypes = [C.POINTER(RingDesc), C.POINTER(AttnSlice), i32, C.POINTER(i32)]
@@ -98,7 +100,7 @@ def lib() -> C.CDLL:
                                    i64, i64, i64, i64, C.c_float, vp, i32, vp, i32, vp, i32, vp, i32, vp, i32,
                                    vp, vp, i32, i32, vp, i64, vp]
         for name in ("magi_slices_build", "magi_default_tile_q", "magi_schedule", "magi_qknorm_rope",
-                     "magi_ffa_fwd", "magi_default_tile_k", "magi_schedule_kv", "magi_ffa_bwd",
+                     "magi_ffa_fwd", "magi_ffa_fwd_qknorm", "magi_default_tile_k", "magi_schedule_kv", "magi_ffa_bwd",
                      "magi_slices_cross", "magi_slices_ring"):
             getattr(L, name).restype = i32
         _lib = L

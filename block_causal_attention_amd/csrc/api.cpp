@@ -118,14 +118,16 @@ extern "C" int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, i
   return ok();
 }
 
-extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t nq,
+namespace {
+
+int32_t ffa_fwd_args(FfaArgs& a, const void* q, const void* k, const void* v, void* out, float* lse, int64_t nq,
                                 int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
                                 int64_t q_tok_stride, int64_t kv_tok_stride, int64_t kv_head_stride,
                                 int64_t o_tok_stride, float softmax_scale, const float* k_norm_max,
                                 const magi_attn_slice* slices,
                                 int32_t num_slices,
                                 const magi_work_item* work, int32_t num_work, const int32_t* tile_slices,
-                                int32_t num_tile_slices, void* stream) {
+                                int32_t num_tile_slices) {
   int32_t st;
   if ((st = check_common(head_dim, dtype)) != MAGI_OK) return st;
   if (hq < 1 || hkv < 1) return fail(MAGI_ERR_INVALID_ARG, "hq and hkv must be >= 1");
@@ -151,7 +153,7 @@ extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, voi
     return fail(MAGI_ERR_INVALID_ARG, "a non-empty list pointer is NULL");
   if (num_work > 0 && nq == 0) return fail(MAGI_ERR_INVALID_ARG, "work items given for an empty query tensor");
 
-  FfaArgs a{};
+  a = FfaArgs{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -175,9 +177,64 @@ extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, voi
   a.num_work = num_work;
   a.tile_slices = tile_slices;
   a.num_tile_slices = num_tile_slices;
+  return MAGI_OK;
+}
+
+int32_t launch(const FfaArgs& a, void* stream) {
   const hipError_t e = launch_ffa_fwd(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MAGI_ERR_HIP, "ffa_fwd launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t nq,
+                                int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
+                                int64_t q_tok_stride, int64_t kv_tok_stride, int64_t kv_head_stride,
+                                int64_t o_tok_stride, float softmax_scale, const float* k_norm_max,
+                                const magi_attn_slice* slices, int32_t num_slices, const magi_work_item* work,
+                                int32_t num_work, const int32_t* tile_slices, int32_t num_tile_slices,
+                                void* stream) {
+  FfaArgs a;
+  const int32_t st = ffa_fwd_args(a, q, k, v, out, lse, nq, nk, hq, hkv, head_dim, dtype, q_tok_stride,
+                                  kv_tok_stride, kv_head_stride, o_tok_stride, softmax_scale, k_norm_max, slices,
+                                  num_slices, work, num_work, tile_slices, num_tile_slices);
+  if (st != MAGI_OK) return st;
+  return launch(a, stream);
+}
+
+extern "C" int32_t magi_ffa_fwd_qknorm(const void* q_raw, const void* k, const void* v, void* out, float* lse,
+                                       int64_t nq, int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim,
+                                       int32_t dtype, int64_t q_tok_stride, int64_t kv_tok_stride,
+                                       int64_t kv_head_stride, int64_t o_tok_stride, float softmax_scale,
+                                       const float* k_norm_max, const magi_attn_slice* slices, int32_t num_slices,
+                                       const magi_work_item* work, int32_t num_work, const int32_t* tile_slices,
+                                       int32_t num_tile_slices, const float* gain_q, int32_t gain_head_stride,
+                                       float eps, const int32_t* pos_q, const float* rope_base, float q_scale,
+                                       void* q_hat, int64_t q_hat_stride, void* stream) {
+  FfaArgs a;
+  int32_t st = ffa_fwd_args(a, q_raw, k, v, out, lse, nq, nk, hq, hkv, head_dim, dtype, q_tok_stride,
+                            kv_tok_stride, kv_head_stride, o_tok_stride, softmax_scale, k_norm_max, slices,
+                            num_slices, work, num_work, tile_slices, num_tile_slices);
+  if (st != MAGI_OK) return st;
+  if (dtype != MAGI_DTYPE_BF16) return fail(MAGI_ERR_UNSUPPORTED, "the fused Q prologue is bf16 only");
+  if (nq > 0 && (gain_q == nullptr || pos_q == nullptr || rope_base == nullptr))
+    return fail(MAGI_ERR_INVALID_ARG, "gain_q / pos_q / rope_base is NULL");
+  if (gain_head_stride != 0 && gain_head_stride != head_dim)
+    return fail(MAGI_ERR_INVALID_ARG, "gain_head_stride must be 0 or head_dim");
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MAGI_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!std::isfinite(q_scale) || q_scale == 0.f) return fail(MAGI_ERR_INVALID_ARG, "q_scale must be finite, non-zero");
+  if (q_hat != nullptr && (st = check_tensor("q_hat", q_hat, nq, hq, q_hat_stride, head_dim, dtype)) != MAGI_OK)
+    return st;
+  a.qn_gain = gain_q;
+  a.qn_gain_hstride = gain_head_stride;
+  a.qn_eps = eps;
+  a.qn_scale = q_scale;
+  a.qn_pos = pos_q;
+  a.qn_base = rope_base;
+  a.q_hat = q_hat;
+  a.q_hat_stride = q_hat_stride;
+  return launch(a, stream);
 }
 
 extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,

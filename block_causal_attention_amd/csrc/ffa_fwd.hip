@@ -91,7 +91,9 @@ __device__ __forceinline__ __bf16 bf16_floor(float x) {
 // NB: 32-row column blocks per wave.  The 256 rows of a work item are
 // spread over 256 / (32 NB) waves, so NB = 1 doubles the waves per SIMD
 // (more latency hiding) at the price of more LDS reads per score.
-template <int D, bool PRESCALED, int NB>
+// QN: q holds the raw queries; each lane applies QK-Norm and the 3D RoPE to
+// its rows after loading them (as the prologue kernel does for K).
+template <int D, bool PRESCALED, int NB, bool QN>
 __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(FfaArgs a) {
   using C = Cfg<D>;
   constexpr int NT = 2 * kRows / NB;  // threads per workgroup: 32 NB rows per wave
@@ -153,6 +155,61 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
       if (rvalid[nb] && d0 < D)
         x = *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi[nb] * a.q_stride + (int64_t)(g * G + hg[nb]) * D + d0);
       qreg[nb][ks] = x;
+    }
+  }
+  if constexpr (QN) {
+    // Row of 32-row block nb: lane half h holds channels 16 ks + 8 h .. + 7
+    // of each k-step ks, i.e. channel pairs 8 ks + 4 h + e (e < 4).  Pair p
+    // of axis section p / (D/6) turns by pos_axis * base_axis^(-2 j / (D/3)),
+    // j = p mod (D/6).  The RMS needs both lane halves of the row.
+    constexpr int PS = D / 6;
+    float inv[C::KS][4];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pr = 8 * ks + 4 * h + e;
+        inv[ks][e] = 0.f;
+        if (2 * pr < D)
+          inv[ks][e] = exp2f(-(float)(2 * (pr % PS)) / (float)(D / 3) * log2f(a.qn_base[pr / PS]));
+      }
+    constexpr float kInv2Pi = 0.15915494309189535f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float x[C::KS][8];
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[ks][e] = (float)qreg[nb][ks][e];
+          ss = fmaf(x[ks][e], x[ks][e], ss);
+        }
+      ss += pair_other(ss, h);
+      if (!rvalid[nb]) continue;
+      const float r = 1.0f / sqrtf(ss / (float)D + a.qn_eps) * a.qn_scale;
+      const float* gp = a.qn_gain + (int64_t)(g * G + hg[nb]) * a.qn_gain_hstride;
+      const int32_t* pp = a.qn_pos + (int64_t)qi[nb] * 3;
+      const float pos[3] = {(float)pp[0], (float)pp[1], (float)pp[2]};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const int d0 = 16 * ks + 8 * h;
+        if (d0 >= D) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int pr = 8 * ks + 4 * h + e;
+          const float x0 = x[ks][2 * e] * r * gp[d0 + 2 * e];
+          const float x1 = x[ks][2 * e + 1] * r * gp[d0 + 2 * e + 1];
+          // angle in turns, reduced to [0, 1) for the hardware sine and cosine
+          const float turns = __builtin_amdgcn_fractf(pos[pr / PS] * inv[ks][e] * kInv2Pi);
+          const float sn = __builtin_amdgcn_sinf(turns), cs = __builtin_amdgcn_cosf(turns);
+          qreg[nb][ks][2 * e] = (__bf16)(x0 * cs - x1 * sn);
+          qreg[nb][ks][2 * e + 1] = (__bf16)(x0 * sn + x1 * cs);
+        }
+        if (a.q_hat != nullptr)
+          *reinterpret_cast<bf16x8*>(reinterpret_cast<__bf16*>(a.q_hat) + (int64_t)qi[nb] * a.q_hat_stride +
+                                     (int64_t)(g * G + hg[nb]) * D + d0) = qreg[nb][ks];
+      }
     }
   }
 
@@ -541,16 +598,27 @@ hipError_t launch_ffa_fwd(const FfaArgs& a, hipStream_t stream) {
     // head_dim 24: 64 rows per wave halve the LDS operand reads per score
     // (3 waves per SIMD); head_dim 48: 32 rows per wave (4 waves per SIMD)
     constexpr int NB24 = 2, NB48 = 1;
+    const bool qn = a.qn_gain != nullptr;
     if (a.head_dim == 24) {
-      if (pre)
-        hipLaunchKernelGGL((ffa_fwd_bf16<24, true, NB24>), grid, dim3(2 * kRows / NB24), 0, stream, a);
+      const dim3 block(2 * kRows / NB24);
+      if (qn && pre)
+        hipLaunchKernelGGL((ffa_fwd_bf16<24, true, NB24, true>), grid, block, 0, stream, a);
+      else if (qn)
+        hipLaunchKernelGGL((ffa_fwd_bf16<24, false, NB24, true>), grid, block, 0, stream, a);
+      else if (pre)
+        hipLaunchKernelGGL((ffa_fwd_bf16<24, true, NB24, false>), grid, block, 0, stream, a);
       else
-        hipLaunchKernelGGL((ffa_fwd_bf16<24, false, NB24>), grid, dim3(2 * kRows / NB24), 0, stream, a);
+        hipLaunchKernelGGL((ffa_fwd_bf16<24, false, NB24, false>), grid, block, 0, stream, a);
     } else {
-      if (pre)
-        hipLaunchKernelGGL((ffa_fwd_bf16<48, true, NB48>), grid, dim3(2 * kRows / NB48), 0, stream, a);
+      const dim3 block(2 * kRows / NB48);
+      if (qn && pre)
+        hipLaunchKernelGGL((ffa_fwd_bf16<48, true, NB48, true>), grid, block, 0, stream, a);
+      else if (qn)
+        hipLaunchKernelGGL((ffa_fwd_bf16<48, false, NB48, true>), grid, block, 0, stream, a);
+      else if (pre)
+        hipLaunchKernelGGL((ffa_fwd_bf16<48, true, NB48, false>), grid, block, 0, stream, a);
       else
-        hipLaunchKernelGGL((ffa_fwd_bf16<48, false, NB48>), grid, dim3(2 * kRows / NB48), 0, stream, a);
+        hipLaunchKernelGGL((ffa_fwd_bf16<48, false, NB48, false>), grid, block, 0, stream, a);
     }
   } else {
     if (a.head_dim == 24)

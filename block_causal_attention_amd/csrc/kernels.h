@@ -45,6 +45,16 @@ struct FfaArgs {
   int64_t kv_hstride;  // elements between consecutive KV heads of K and V
   float scale;
   const float* k_norm_max;  // device [hkv] upper bounds on key norms, or nullptr
+  // QK-Norm + 3D RoPE of Q done in the kernel (q is then the raw Q): gain
+  // [d] or [hq][d], positions [nq][3], rope base [3]; q_hat (or nullptr)
+  // receives the normalised, rotated Q
+  const float* qn_gain;  // nullptr: q is used as given
+  int32_t qn_gain_hstride;
+  float qn_eps, qn_scale;
+  const int32_t* qn_pos;
+  const float* qn_base;
+  void* q_hat;
+  int64_t q_hat_stride;
   const magi_attn_slice* slices;
   int32_t num_slices;
   const magi_work_item* work;

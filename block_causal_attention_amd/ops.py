@@ -20,7 +20,7 @@ LN2 = 0.6931471805599453
 LOG2E = 1.4426950408889634
 
 __all__ = ["build_slices", "schedule", "Plan", "make_plan", "plan_for_videos", "qknorm_rope",
-           "ffa_fwd", "ffa_bwd", "kv_group_major", "default_tile_q", "dtype_code"]
+           "ffa_fwd", "ffa_bwd", "QNorm", "kv_group_major", "default_tile_q", "dtype_code"]
 
 
 def dtype_code(dt: torch.dtype) -> int:
@@ -312,16 +312,24 @@ def qknorm_rope(q: torch.Tensor, k: Optional[torch.Tensor], gain_q: torch.Tensor
     norm of every output key of each head.  ``k_out`` may be any [nk, hkv, d]
     view with contiguous channels, e.g. kv_group_major(); ``v`` (laid out like
     k) is then copied into ``v_out`` (default: a tensor laid out like k_out)."""
-    d = q.shape[-1]
-    _check_3d("q", q, q.shape[1], d)
-    q_out = torch.empty_like(q) if q_out is None else q_out
-    _check_3d("q_out", q_out, q.shape[1], d)
-    if q_out.stride(0) != q.stride(0):
-        raise ValueError("q and q_out must share the row stride")
+    if q is None:   # K (and V) only: Q is normalised elsewhere (ffa_fwd(..., qknorm=...))
+        if k is None:
+            raise ValueError("nothing to do: q and k are both None")
+        d = k.shape[-1]
+        if q_out is not None:
+            raise ValueError("q_out needs q")
+        gain_q = gain_k if gain_q is None else gain_q
+    else:
+        d = q.shape[-1]
+        _check_3d("q", q, q.shape[1], d)
+        q_out = torch.empty_like(q) if q_out is None else q_out
+        _check_3d("q_out", q_out, q.shape[1], d)
+        if q_out.stride(0) != q.stride(0):
+            raise ValueError("q and q_out must share the row stride")
     ghs = 0 if gain_q.dim() == 1 else d
     if gain_k is not None and gain_k.dim() != gain_q.dim():
         raise ValueError("gain_q and gain_k must both be shared [d] or both per head [heads, d]")
-    nk, hkv, ks = 0, 1, q.shape[1] * d
+    nk, hkv, ks = 0, 1, (q.shape[1] * d if q is not None else d)
     kos, kohs = ks, d
     if k is not None:
         _check_3d("k", k, k.shape[1], d)
@@ -351,23 +359,40 @@ def qknorm_rope(q: torch.Tensor, k: Optional[torch.Tensor], gain_q: torch.Tensor
     for t in (pos_q, pos_k):
         if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
             raise ValueError("positions must be contiguous int32 [n, 3]")
+    nq, hq, qs = (q.shape[0], q.shape[1], q.stride(0)) if q is not None else (0, 1, d)
+    dev_t = q if q is not None else k
     check(lib().magi_qknorm_rope(
-        _ptr(q), _ptr(q_out), q.shape[0], q.shape[1], q.stride(0),
-        _ptr(k), _ptr(k_out), nk, hkv, ks, kos, kohs, _ptr(v), _ptr(v_out), d, dtype_code(q.dtype),
-        _ptr(gain_q), _ptr(gain_k), ghs, float(eps), _ptr(pos_q), _ptr(pos_k), _ptr(rope_base),
-        float(q_scale), float(k_scale), _ptr(k_norm_max), _stream(q)))
+        _ptr(q), _ptr(q_out), nq, hq, qs,
+        _ptr(k), _ptr(k_out), nk, hkv, ks, kos, kohs, _ptr(v), _ptr(v_out), d, dtype_code(dev_t.dtype),
+        _ptr(gain_q) if q is not None else None, _ptr(gain_k), ghs, float(eps),
+        _ptr(pos_q) if q is not None else None, _ptr(pos_k), _ptr(rope_base),
+        float(q_scale), float(k_scale), _ptr(k_norm_max), _stream(dev_t)))
     return (q_out, k_out) if v is None else (q_out, k_out, v_out)
+
+
+@dataclass
+class QNorm:
+    """The QK-Norm + 3D RoPE of Q for ffa_fwd(..., qnorm=...): gain [d] or
+    [hq, d] (float32), positions int32 [nq, 3], rope base float32 [3]; q_hat
+    (optional) receives the normalised, rotated Q."""
+    gain: torch.Tensor
+    pos: torch.Tensor
+    rope_base: torch.Tensor
+    eps: float = 1e-6
+    scale: float = 1.0
+    q_hat: Optional[torch.Tensor] = None
 
 
 def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
             softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
             lse: Optional[torch.Tensor] = None, return_lse: bool = True,
-            k_norm_max: Optional[torch.Tensor] = None):
+            k_norm_max: Optional[torch.Tensor] = None, qnorm: Optional[QNorm] = None):
     """magi_ffa_fwd over ``plan``; returns (out [nq, hq, d], lse [nq, hq] fp32 or None).
     ``k_norm_max`` (float32 [hkv], optional) must bound the norm of every key
     row of each group (qknorm_rope writes one).  k and v are [nk, hkv, d]
     views with contiguous channels and one common layout (token-major, or
-    group-major as from kv_group_major)."""
+    group-major as from kv_group_major).  With ``qnorm`` q is the raw Q and
+    the kernel applies QK-Norm + 3D RoPE to it (magi_ffa_fwd_qknorm)."""
     d = q.shape[-1]
     hq, hkv = q.shape[1], k.shape[1]
     _check_3d("q", q, hq, d)
@@ -384,12 +409,25 @@ def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
         lse = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
     if plan.ready is not None:
         torch.cuda.current_stream(q.device).wait_event(plan.ready)
-    check(lib().magi_ffa_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q.shape[0], k.shape[0], hq, hkv, d,
-        dtype_code(q.dtype), q.stride(0), k.stride(0), k.stride(1), out.stride(0),
-        0.0 if softmax_scale is None else float(softmax_scale), _ptr(k_norm_max),
-        _ptr(plan.slices), int(plan.host["slices"].shape[0]), _ptr(plan.work), plan.num_work,
-        _ptr(plan.tile_slices), int(plan.host["tile_slices"].shape[0]), _stream(q)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q.shape[0], k.shape[0], hq, hkv, d,
+            dtype_code(q.dtype), q.stride(0), k.stride(0), k.stride(1), out.stride(0),
+            0.0 if softmax_scale is None else float(softmax_scale), _ptr(k_norm_max),
+            _ptr(plan.slices), int(plan.host["slices"].shape[0]), _ptr(plan.work), plan.num_work,
+            _ptr(plan.tile_slices), int(plan.host["tile_slices"].shape[0]))
+    if qnorm is None:
+        check(lib().magi_ffa_fwd(*args, _stream(q)))
+        return out, lse
+    g = qnorm
+    for t in (g.gain, g.rope_base):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("qnorm gain and rope_base must be contiguous float32")
+    if g.pos.dtype != torch.int32 or not g.pos.is_contiguous() or g.pos.shape != (q.shape[0], 3):
+        raise ValueError("qnorm positions must be contiguous int32 [nq, 3]")
+    if g.q_hat is not None:
+        _check_3d("q_hat", g.q_hat, hq, d)
+    check(lib().magi_ffa_fwd_qknorm(*args, _ptr(g.gain), 0 if g.gain.dim() == 1 else d, float(g.eps), _ptr(g.pos),
+                                    _ptr(g.rope_base), float(g.scale), _ptr(g.q_hat),
+                                    g.q_hat.stride(0) if g.q_hat is not None else 0, _stream(q)))
     return out, lse
 
 

@@ -300,6 +300,39 @@ int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, void* out, flo
                      void* stream);
 
 /*
+ * magi_ffa_fwd_qknorm -- magi_ffa_fwd with the QK-Norm + 3D RoPE of Q done
+ * inside the attention kernel.                          [device, async]
+ *
+ * The same operation as magi_qknorm_rope on Q followed by magi_ffa_fwd (the
+ * pages' order: QK-Norm, then RoPE, then attention; study notes "自回归去噪
+ * DiT"), with q_raw the un-normalised queries: each work item normalises and
+ * rotates its own query rows in registers, so Q is read once and never
+ * written back (K still goes through magi_qknorm_rope).  Arithmetic as
+ * magi_qknorm_rope (fp32, result rounded to bf16) except that the rotation
+ * angles use the hardware sine and cosine of the angle reduced to one turn
+ * (absolute error ~1e-6, far below the bf16 rounding of the result).
+ *
+ * All arguments of magi_ffa_fwd (q replaced by q_raw), plus:
+ * gain_q, gain_head_stride, eps, pos_q, rope_base, q_scale
+ *              as in magi_qknorm_rope for Q
+ * q_hat        [device] out or NULL: receives the normalised, rotated Q
+ *              (bf16, [nq][hq][head_dim], row stride q_hat_stride), e.g. for
+ *              the backward
+ * Supported: bf16 only (MAGI_ERR_UNSUPPORTED for fp32); otherwise as
+ * magi_ffa_fwd.
+ */
+int32_t magi_ffa_fwd_qknorm(const void* q_raw, const void* k, const void* v, void* out, float* lse,
+                            int64_t nq, int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
+                            int64_t q_tok_stride, int64_t kv_tok_stride, int64_t kv_head_stride,
+                            int64_t o_tok_stride, float softmax_scale, const float* k_norm_max,
+                            const magi_attn_slice* slices, int32_t num_slices,
+                            const magi_work_item* work, int32_t num_work,
+                            const int32_t* tile_slices, int32_t num_tile_slices,
+                            const float* gain_q, int32_t gain_head_stride, float eps,
+                            const int32_t* pos_q, const float* rope_base, float q_scale,
+                            void* q_hat, int64_t q_hat_stride, void* stream);
+
+/*
  * magi_default_tile_k -- keys per key-major work item that magi_ffa_bwd's
  * dK/dV kernel is built for (128).  Returns < 0 on unsupported shapes.
  */

@@ -352,6 +352,70 @@ def test_prologue_group_major_output_and_v_copy(name):
     assert torch.equal(q1, q2) and torch.equal(k1, k2) and torch.equal(v2, d["v"]) and torch.equal(n1, n2)
 
 
+def gpu_forward_fused(wl, d, q_hat=None):
+    """the benchmark's fused configuration: the prologue on K (V moved
+    group-major), QK-Norm + RoPE of Q inside the attention kernel"""
+    knm = torch.empty(wl.hkv, dtype=torch.float32, device=DEV)
+    kg = ops.kv_group_major(wl.nk, wl.hkv, wl.head_dim, d["k"].dtype)
+    _, kh, vh = ops.qknorm_rope(None, d["k"], None, d["gk"], None, d["pk"], d["base"], wl.eps, k_out=kg,
+                                k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm, v=d["v"])
+    plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, d["q"].dtype)
+    qn = ops.QNorm(d["gq"], d["pq"], d["base"], wl.eps, 1.0, q_hat)
+    O, L = ops.ffa_fwd(d["q"], kh, vh, plan, softmax_scale=ops.LN2, k_norm_max=knm, qnorm=qn)
+    torch.cuda.synchronize()
+    return O, L
+
+
+@pytest.mark.parametrize("name,nrows", [("magi4.5b", 384), ("magi24b", 160), ("varlen", 64)])
+def test_fused_q_prologue_end_to_end(name, nrows):
+    # fused path against the oracle on sampled rows, and against the
+    # two-kernel path (prologue on Q, then attention) on every row
+    wl = W.make_workload(name, 0)
+    inp = W.make_inputs(wl, 0)
+    d = dev_inputs(wl, inp)
+    note(f"fused Q prologue {name}")
+    qh_ref = torch.empty_like(d["q"])
+    O, L = gpu_forward_fused(wl, d, q_hat=qh_ref)
+    rows = W.sample_rows(wl, nrows, 0)
+    mask = oracle.video_mask(wl.seqs, wl.nq, wl.nk, rows)
+    Ow, Lw = oracle.forward(np64(inp.q[rows]), np64(inp.k), np64(inp.v), np64(inp.gain_q), np64(inp.gain_k),
+                            inp.pos_q[rows].numpy(), inp.pos_k.numpy(), wl.rope_base, wl.eps, mask,
+                            wl.softmax_scale)
+    compare(np64(O[rows]), Ow, wl.dtype)
+    compare(np64(L[rows]), Lw, wl.dtype, "LSE")
+    qh, _, O2, L2 = gpu_forward(wl, d)
+    # q_hat is the prologue's Q up to the last bf16 bit (the hardware sine and
+    # cosine differ from sincosf by ~1e-6)
+    dq = (qh_ref.float() - qh.float()).abs()
+    assert float(dq.max()) <= 2 ** -7 * float(qh.float().abs().max())
+    assert float((dq > 0).float().mean()) < 0.05
+    compare(np64(O), np64(O2), wl.dtype, "O fused vs two kernels")
+
+
+def test_fused_q_prologue_small_cases():
+    # G = 4 and 1 (several tokens per item), d = 48, per-head gains, a q_scale,
+    # no key-norm bound (online max path), against the oracle on every row
+    for (C_, G, hkv, dd) in ((3, 4, 2, 48), (2, 1, 3, 24)):
+        wl = W.custom_block_causal(C_, 2, 3, 4, G * hkv, hkv, dd)
+        inp = W.make_inputs(wl, 11)
+        d = dev_inputs(wl, inp)
+        rng = np.random.Generator(np.random.PCG64(11))
+        gq = torch.from_numpy(rng.uniform(0.5, 1.5, (G * hkv, dd)).astype(np.float32)).to(DEV)
+        plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, dd, torch.bfloat16)
+        _, kh = ops.qknorm_rope(None, d["k"], None, d["gk"], None, d["pk"], d["base"], wl.eps)
+        O, L = ops.ffa_fwd(d["q"], kh, d["v"], plan, qnorm=ops.QNorm(gq, d["pq"], d["base"], wl.eps, 0.7))
+        torch.cuda.synchronize()
+        mask = oracle.video_mask(wl.seqs, wl.nq, wl.nk)
+        qhat = oracle.rope_3d(oracle.qk_norm(np64(inp.q), gq.cpu().numpy().astype(np.float64), wl.eps) * 0.7,
+                              inp.pos_q.numpy(), oracle.rope_inv_freq(wl.rope_base, dd))
+        khat = oracle.rope_3d(oracle.qk_norm(np64(inp.k), np64(inp.gain_k), wl.eps), inp.pos_k.numpy(),
+                              oracle.rope_inv_freq(wl.rope_base, dd))
+        Ow, Lw = oracle.attention(qhat, khat, np64(inp.v), mask, dd ** -0.5)
+        note(f"fused small case G={G} hkv={hkv} d={dd}")
+        compare(np64(O), Ow, "bf16")
+        compare(np64(L), Lw, "bf16", "LSE")
+
+
 def test_end_to_end_magi45b_token_major():
     # the full 4.5B layer with K and V left token-major
     wl = W.make_workload("magi4.5b", 0)

@@ -23,7 +23,7 @@ def header_functions():
 def test_library_exports_every_header_symbol():
     L = _lib.lib()
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -437,6 +437,26 @@ def test_device_entry_points_validate_before_any_hip_call():
     assert ffa(nq=-2) == _lib.MAGI_ERR_INVALID_ARG
     assert ffa(nq=0, q=None, out=None) == _lib.MAGI_ERR_INVALID_ARG  # work for no rows
     assert b"work" in L.magi_last_error()
+
+
+def test_fused_forward_entry_validates_q_prologue():
+    L = _lib.lib()
+    p = C.c_void_p(4096)  # never dereferenced: every call below fails validation
+
+    def fq(**kw):
+        a = dict(dt=0, gq=p, ghs=0, eps=1e-6, pq=p, base=p, qsc=1.0, qhat=None, qhs=0)
+        a.update(kw)
+        return L.magi_ffa_fwd_qknorm(p, p, p, p, None, 16, 16, 16, 1, 24, a["dt"], 384, 24, 24, 384, 0.0, None, p, 1,
+                                     p, 1, p, 1, a["gq"], a["ghs"], a["eps"], a["pq"], a["base"], a["qsc"], a["qhat"],
+                                     a["qhs"], None)
+    assert fq(dt=1) == _lib.MAGI_ERR_UNSUPPORTED          # bf16 only
+    assert fq(gq=None) == _lib.MAGI_ERR_INVALID_ARG
+    assert fq(pq=None) == _lib.MAGI_ERR_INVALID_ARG
+    assert fq(base=None) == _lib.MAGI_ERR_INVALID_ARG
+    assert fq(ghs=5) == _lib.MAGI_ERR_INVALID_ARG
+    assert fq(eps=-1.0) == _lib.MAGI_ERR_INVALID_ARG
+    assert fq(qsc=0.0) == _lib.MAGI_ERR_INVALID_ARG
+    assert fq(qhat=p, qhs=100) == _lib.MAGI_ERR_INVALID_ARG   # q_hat row stride < heads * d
 
 
 def test_backward_entry_validates_split_workspace():
