@@ -4,6 +4,7 @@ invariants that fix what the oracle computes independently of its own code.
 Each test names the plausible mistake it would catch.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -442,3 +443,29 @@ def test_attention_backward_sum_invariants():
     for g in range(hkv):
         np.testing.assert_allclose(dV[:, g].sum(0), dO[live][:, g * G:(g + 1) * G].sum((0, 1)), rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(dK[:, g].sum(0), 0.0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- hand-written fixtures
+
+def _golden(name):
+    rows = [ln.strip() for ln in open(os.path.join(os.path.dirname(__file__), "golden", name))
+            if ln.strip() and not ln.startswith("#")]
+    return np.array([[c == "1" for c in r] for r in rows], bool)
+
+
+def test_golden_block_causal_mask():
+    # [notes] "自回归去噪 DiT": full inside a chunk, causal across chunks
+    seqs = [SeqDesc(2, 3, 3, 0, 0, (-1, -1, -1), 1, 1, 2)]
+    np.testing.assert_array_equal(oracle.video_mask(seqs, 6, 6), _golden("block_causal_3x2.txt"))
+
+
+def test_golden_kv_range_mask():
+    # [notes] "推理技巧", KV Cache: a chunk with range r sees itself and r earlier chunks
+    seqs = [SeqDesc(2, 4, 4, 0, 0, (-1, -1, 1, 1), 1, 1, 2)]
+    np.testing.assert_array_equal(oracle.video_mask(seqs, 8, 8), _golden("kv_range_4x2_r1.txt"))
+
+
+def test_golden_packed_videos_mask():
+    # [interview]: packed videos never see each other
+    seqs = [SeqDesc(2, 2, 2, 0, 0, (-1, -1), 1, 1, 2), SeqDesc(1, 2, 2, 4, 4, (-1, -1), 1, 1, 1)]
+    np.testing.assert_array_equal(oracle.video_mask(seqs, 6, 6), _golden("packed_two_videos.txt"))
