@@ -284,7 +284,7 @@ def committed_traffic(wl_name: str):
     return float(rec["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(wl, target_s=15.0, seed=0):
+def cpu_baseline(wl, target_s=30.0, seed=0):
     """Time the float64 oracle on a seeded row sample (all heads) of the workload."""
     import oracle
     import workloads as W
