@@ -530,11 +530,13 @@ def test_packing_equals_separate_videos_gpu():
 
 # --------------------------------------------------------------------------- cross-attention
 
-def test_cross_attention_packed_samples():
+@pytest.mark.parametrize("group_major", [False, True])
+def test_cross_attention_packed_samples(group_major):
     # the parallel block's cross-attention: each sample's video tokens see its
     # own condition tokens (FULL slices from magi_slices_cross); QK-Norm on
-    # both sides and no rotation (zero positions), GQA 32/2, d = 24
-    note("cross-attention packed samples")
+    # both sides and no rotation (zero positions), GQA 32/2, d = 24; K and V
+    # token-major or group-major (as the benchmark runs it)
+    note(f"cross-attention packed samples group_major={group_major}")
     d, hq, hkv = 24, 32, 2
     samples = [(0, 300, 0, 77), (300, 240, 77, 50)]
     nq, nk = 540, 127
@@ -545,10 +547,16 @@ def test_cross_attention_packed_samples():
     zq = torch.zeros((nq, 3), dtype=torch.int32, device=DEV)
     zk = torch.zeros((nk, 3), dtype=torch.int32, device=DEV)
     base = torch.tensor((1e4, 1e4, 1e4), dtype=torch.float32, device=DEV)
-    qh, kh = ops.qknorm_rope(qd, kd, torch.from_numpy(gq).to(DEV), torch.from_numpy(gk).to(DEV), zq, zk, base, 1e-6)
+    if group_major:
+        qh, kh, vh = ops.qknorm_rope(qd, kd, torch.from_numpy(gq).to(DEV), torch.from_numpy(gk).to(DEV), zq, zk, base,
+                                     1e-6, k_out=ops.kv_group_major(nk, hkv, d, torch.bfloat16), v=vd)
+    else:
+        qh, kh = ops.qknorm_rope(qd, kd, torch.from_numpy(gq).to(DEV), torch.from_numpy(gk).to(DEV), zq, zk, base,
+                                 1e-6)
+        vh = vd
     sl = ops.build_cross_slices(samples)
     plan = ops.make_plan(sl, nq, nk, hq, hkv, d, torch.bfloat16)
-    O, L = ops.ffa_fwd(qh, kh, vd, plan)
+    O, L = ops.ffa_fwd(qh, kh, vh, plan)
     torch.cuda.synchronize()
     mask = oracle.slices_mask([tuple(int(x) for x in s) for s in sl], nq, nk)
     Ow, Lw = oracle.forward(np64(qd), np64(kd), np64(vd), gq, gk, np.zeros((nq, 3)), np.zeros((nk, 3)),
@@ -559,13 +567,14 @@ def test_cross_attention_packed_samples():
 
 # --------------------------------------------------------------------------- streaming ring KV cache
 
-def test_streaming_step_over_ring_cache():
+@pytest.mark.parametrize("group_major", [False, True])
+def test_streaming_step_over_ring_cache(group_major):
     # ring of 6 chunk slots holding global chunks 4..9, chunks 7..9 in flight
     # (slots 1..3 after wrapping) with per-chunk KV ranges 2, unlimited, 1.
     # The prologue writes every chunk's keys straight into its slot (cached
     # chunks in "earlier steps"); the oracle runs the same chunks laid out
     # linearly, so the ring order of the keys must not matter
-    note("streaming step over a ring KV cache")
+    note(f"streaming step over a ring KV cache group_major={group_major}")
     C, S, first, count, n = 48, 6, 4, 6, 3
     d, hq, hkv = 24, 32, 2
     kvr = [2, -1, 1]
@@ -584,8 +593,12 @@ def test_streaming_step_over_ring_cache():
     base = torch.tensor((1e4, 1e4, 1e4), dtype=torch.float32, device=DEV)
     gqd, gkd = dv_(gq), dv_(gk)
     scale = d ** -0.5
-    ring_k = torch.zeros((S * C, hkv, d), dtype=torch.bfloat16, device=DEV)
-    ring_v = torch.zeros_like(ring_k)
+    if group_major:   # the ring stored [hkv][slots x C][d], as the benchmark keeps it
+        ring_k = ops.kv_group_major(S * C, hkv, d, torch.bfloat16).zero_()
+        ring_v = ops.kv_group_major(S * C, hkv, d, torch.bfloat16).zero_()
+    else:
+        ring_k = torch.zeros((S * C, hkv, d), dtype=torch.bfloat16, device=DEV)
+        ring_v = torch.zeros_like(ring_k)
     for c in range(first, nchunks):
         s = c % S
         kc = dv_(kraw[c * C:(c + 1) * C]).to(torch.bfloat16)
