@@ -18,6 +18,8 @@ MAGI_ERR_OVERLAP = -4
 MAGI_ERR_HIP = -5
 MASK_FULL = 0
 MASK_CAUSAL = 1
+MASK_INVCAUSAL = 2
+MASK_BICAUSAL = 3
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 
@@ -26,7 +28,7 @@ STATUS_NAMES = {0: "MAGI_OK", -1: "MAGI_ERR_INVALID_ARG", -2: "MAGI_ERR_UNSUPPOR
 
 EXPORTS = ("magi_version", "magi_last_error", "magi_slices_build", "magi_default_tile_q",
            "magi_schedule", "magi_qknorm_rope", "magi_ffa_fwd", "magi_ffa_fwd_qknorm", "magi_default_tile_k",
-           "magi_schedule_kv", "magi_ffa_bwd", "magi_slices_cross", "magi_slices_ring")
+           "magi_schedule_kv", "magi_ffa_bwd", "magi_slices_cross", "magi_slices_ring", "magi_slices_window")
 
 
 class AttnSlice(C.Structure):
@@ -52,6 +54,10 @@ class KvReduce(C.Structure):
 
 class CrossDesc(C.Structure):
     _fields_ = [("q_offset", C.c_int32), ("q_len", C.c_int32), ("k_offset", C.c_int32), ("k_len", C.c_int32)]
+
+
+class WindowDesc(C.Structure):
+    _fields_ = [("len", C.c_int32), ("window", C.c_int32), ("q_offset", C.c_int32), ("k_offset", C.c_int32)]
 
 
 class SeqDesc(C.Structure):
@@ -94,6 +100,7 @@ def lib() -> C.CDLL:
         L.magi_default_tile_k.argtypes = [i32, i32, i32, i32]
         L.magi_slices_cross.argtypes = [C.POINTER(CrossDesc), i32, C.POINTER(AttnSlice), i32, C.POINTER(i32)]
         L.magi_slices_ring.argtypes = [C.POINTER(RingDesc), C.POINTER(AttnSlice), i32, C.POINTER(i32)]
+        L.magi_slices_window.argtypes = [C.POINTER(WindowDesc), i32, C.POINTER(AttnSlice), i32, C.POINTER(i32)]
         L.magi_schedule_kv.argtypes = L.magi_schedule.argtypes + [C.POINTER(i32), C.POINTER(KvReduce), i32,
                                                                    C.POINTER(i32), C.POINTER(i32)]
         L.magi_ffa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32,
@@ -101,7 +108,7 @@ def lib() -> C.CDLL:
                                    vp, vp, i32, i32, vp, i64, vp]
         for name in ("magi_slices_build", "magi_default_tile_q", "magi_schedule", "magi_qknorm_rope",
                      "magi_ffa_fwd", "magi_ffa_fwd_qknorm", "magi_default_tile_k", "magi_schedule_kv", "magi_ffa_bwd",
-                     "magi_slices_cross", "magi_slices_ring"):
+                     "magi_slices_cross", "magi_slices_ring", "magi_slices_window"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib

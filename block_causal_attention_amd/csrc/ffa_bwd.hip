@@ -219,7 +219,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
       nkt = ng.ks;
     }
     if (have_next) load_tile(nkt, ng.khi);  // in flight while this tile is computed
-    const bool masked = kt + TK > cg.kfull;
+    const bool masked = kt < cg.klo || kt + TK > cg.kfull;
     const __bf16* Kb = Ks[buf];
     const __bf16* Vb = Vs[buf];
     const __attribute__((address_space(3))) __bf16* Kt = (const __attribute__((address_space(3))) __bf16*)Ks[buf];
@@ -235,15 +235,13 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dreg[ks], dp, 0, 0, 0);
       }
       if (masked) {
-        int32_t re = cg.ke;
-        if (cg.causal) {
-          const int32_t ce = cg.koff + qi + 1;
-          re = ce < re ? ce : re;
-        }
-        const int32_t lim = re - kt - kb * 32 - 4 * h;
+        // keys at block offset >= lim or < lim_lo are hidden from the row
+        const int32_t kb0 = kt + kb * 32 + 4 * h;
+        const int32_t lim = geo_row_end(cg, qi) - kb0;
+        const int32_t lim_lo = (cg.type & MAGI_MASK_INVCAUSAL) ? cg.loff + qi - kb0 : -TK;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (key_of0(i) >= lim) s[i] = -INFINITY;
+          if (key_of0(i) >= lim || key_of0(i) < lim_lo) s[i] = -INFINITY;
       }
       // dS^T = P^T * dP'^T, rounded to bf16 in the B-operand layout
       bf16x8 dsb[2];
@@ -301,8 +299,9 @@ struct QRun {
   int32_t t0;      // first token of the current tile
   int32_t t_end;   // one past the last token of the run
   int32_t ks, ke;  // slice key range (ke clamped to nk)
-  int32_t koff;    // k_end - q_end
-  int32_t causal;
+  int32_t koff;    // k_end - q_end: under the upper bound token t sees keys below koff + t + 1
+  int32_t loff;    // k_start - q_start: under the lower bound token t sees keys from loff + t
+  int32_t type;    // mask type bits: 1 = upper bound, 2 = lower bound
   int32_t valid;
 };
 
@@ -320,13 +319,18 @@ __device__ __forceinline__ bool find_qrun(const SliceLists& L, int32_t slice_end
     int32_t qe = s.q_end < nq ? s.q_end : nq;
     if (qe > w_hi) qe = w_hi;  // the item's token window
     if (ks >= ke || s.q_start >= qe || ke <= k0 || ks >= k1) continue;
-    const int32_t causal = s.mask_type == MAGI_MASK_CAUSAL;
+    const int32_t type = s.mask_type & (MAGI_MASK_CAUSAL | MAGI_MASK_INVCAUSAL);
     const int32_t koff = s.k_end - s.q_end;
-    // rows that see a key >= max(k0, ks): causal row r sees k iff k < koff + r + 1
+    const int32_t loff = s.k_start - s.q_start;
+    // rows that see a key of [max(k0, ks), min(k1, ke)): under the upper
+    // bound row r sees k iff k < koff + r + 1, under the lower bound iff
+    // k >= loff + r
     const int32_t kmin = k0 > ks ? k0 : ks;
+    const int32_t kmax = (k1 < ke ? k1 : ke) - 1;
     int32_t t0 = s.q_start;
-    if (causal && kmin - koff > t0) t0 = kmin - koff;
+    if ((type & MAGI_MASK_CAUSAL) && kmin - koff > t0) t0 = kmin - koff;
     if (t0 < w_lo) t0 = w_lo;
+    if ((type & MAGI_MASK_INVCAUSAL) && kmax - loff + 1 < qe) qe = kmax - loff + 1;
     if (t0 >= qe) continue;
     r.si = si;
     r.t0 = t0;
@@ -334,7 +338,8 @@ __device__ __forceinline__ bool find_qrun(const SliceLists& L, int32_t slice_end
     r.ks = ks;
     r.ke = ke;
     r.koff = koff;
-    r.causal = causal;
+    r.loff = loff;
+    r.type = type;
     r.valid = 1;
     return true;
   }
@@ -498,10 +503,12 @@ __global__ __launch_bounds__(2 * kKeys / KB, 2) void bwd_dkdv_bf16(BwdArgs a) {
     if (nxt.valid) load_tile(nxt);  // in flight while this tile is computed
     const int32_t ntok = cur.t_end - cur.t0 < TQT ? cur.t_end - cur.t0 : TQT;
     // every element visible: the item's keys inside the slice's key range,
-    // a whole tile of rows, and (causal) the tile's first token already
-    // seeing the item's last key
+    // a whole tile of rows, the tile's first token already seeing the item's
+    // last key (upper bound) and its last token still seeing the item's
+    // first key (lower bound)
     const bool full = cur.ks <= k0 && k1 <= cur.ke && ntok == TQT && tq_rows == TQ &&
-                      (!cur.causal || k1 - 1 < cur.koff + cur.t0 + 1);
+                      (!(cur.type & MAGI_MASK_CAUSAL) || k1 - 1 < cur.koff + cur.t0 + 1) &&
+                      (!(cur.type & MAGI_MASK_INVCAUSAL) || k0 >= cur.loff + cur.t0 + TQT - 1);
     const __bf16* Qb = Qs[buf];
     const __bf16* Ob = Os[buf];
     const __attribute__((address_space(3))) __bf16* Qt = (const __attribute__((address_space(3))) __bf16*)Qs[buf];
@@ -527,15 +534,21 @@ __global__ __launch_bounds__(2 * kKeys / KB, 2) void bwd_dkdv_bf16(BwdArgs a) {
         // Element i holds row 8 (i / 4) + 4 h + i % 4 of this 32-row block,
         // token tt = row / G of the tile.  The key of block kb is seen by
         // tokens lo <= tt < hi: hi = ntok (0 if the key is outside the
-        // slice or the item), lo = key - koff - t0 for a causal slice
-        // (bottom-right aligned: token t sees k < koff + t + 1).  The hiding
-        // mask is built by integer arithmetic and applied with a bit select,
-        // so no lane-mask registers are tied up.
+        // slice or the item), lowered to key - loff - t0 + 1 under the
+        // lower bound (top-left aligned: token t sees k >= loff + t); lo =
+        // key - koff - t0 under the upper bound (bottom-right aligned: token
+        // t sees k < koff + t + 1).  The hiding mask is built by integer
+        // arithmetic and applied with a bit select, so no lane-mask
+        // registers are tied up.
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const bool kin = kvalid[kb] && key[kb] >= cur.ks && key[kb] < cur.ke;
-          const int32_t hi = kin ? ntok : 0;
-          const int32_t lo = cur.causal ? key[kb] - cur.koff - cur.t0 : -(1 << 30);
+          int32_t hi = kin ? ntok : 0;
+          if (cur.type & MAGI_MASK_INVCAUSAL) {
+            const int32_t e = key[kb] - cur.loff - cur.t0 + 1;
+            hi = e < hi ? e : hi;
+          }
+          const int32_t lo = (cur.type & MAGI_MASK_CAUSAL) ? key[kb] - cur.koff - cur.t0 : -(1 << 30);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int row = rb * 32 + 8 * (i / 4) + 4 * h + (i % 4);  // < 64
@@ -663,8 +676,8 @@ __global__ __launch_bounds__(kThreads32) void bwd_dq_f32(BwdArgs a) {
       if (qi < sl.q_start || qi >= sl.q_end) continue;
       const int64_t ks = sl.k_start > 0 ? sl.k_start : 0;
       const int64_t ke = sl.k_end < a.nk ? sl.k_end : a.nk;
-      const int64_t re = sl.mask_type == MAGI_MASK_CAUSAL ? causal_end(sl, ke, qi) : ke;
-      for (int64_t kk = ks; kk < re; ++kk) {
+      const int64_t re = row_key_end(sl, ke, qi);
+      for (int64_t kk = row_key_begin(sl, ks, qi); kk < re; ++kk) {
         const float* kr = kp + kk * a.kv_stride + (int64_t)g * a.kv_hstride;
         const float* vr = vp + kk * a.kv_stride + (int64_t)g * a.kv_hstride;
         float s = 0.f, dpv = 0.f;
@@ -719,12 +732,16 @@ __global__ __launch_bounds__(kThreads32) void bwd_dkdv_f32(BwdArgs a) {
     const int64_t ke = sl.k_end < a.nk ? sl.k_end : a.nk;
     if (key < sl.k_start || key >= ke) continue;
     int64_t r0 = sl.q_start;
-    if (sl.mask_type == MAGI_MASK_CAUSAL) {
+    if (sl.mask_type & MAGI_MASK_CAUSAL) {
       const int64_t f = key - ((int64_t)sl.k_end - sl.q_end);  // first row that sees the key
       r0 = f > r0 ? f : r0;
     }
     if (r0 < w_lo) r0 = w_lo;
     int64_t qe = sl.q_end < a.nq ? sl.q_end : a.nq;
+    if (sl.mask_type & MAGI_MASK_INVCAUSAL) {
+      const int64_t e = key - ((int64_t)sl.k_start - sl.q_start) + 1;  // one past the last row that sees it
+      qe = e < qe ? e : qe;
+    }
     if (qe > w_hi) qe = w_hi;
     for (int64_t r = r0; r < qe; ++r)
       for (int hh = 0; hh < G; ++hh) {

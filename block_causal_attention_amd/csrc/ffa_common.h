@@ -56,10 +56,19 @@ __device__ __forceinline__ magi_attn_slice load_slice(const magi_attn_slice* sli
   return s;
 }
 
-// bottom-right aligned causal: row r sees key k iff k - k_end <= r - q_end
-__device__ inline int64_t causal_end(const magi_attn_slice& s, int64_t ke, int64_t row) {
+// Keys [row_key_begin, row_key_end) of row `row` (q_start <= row < q_end)
+// under slice s, within [ks, ke).  Bottom-right (causal) bound, type bit 0:
+// k - k_end <= row - q_end.  Top-left (inverse causal) bound, type bit 1:
+// k - k_start >= row - q_start.
+__device__ inline int64_t row_key_end(const magi_attn_slice& s, int64_t ke, int64_t row) {
+  if (!(s.mask_type & MAGI_MASK_CAUSAL)) return ke;
   const int64_t e = (int64_t)s.k_end - (int64_t)s.q_end + row + 1;
   return e < ke ? e : ke;
+}
+__device__ inline int64_t row_key_begin(const magi_attn_slice& s, int64_t ks, int64_t row) {
+  if (!(s.mask_type & MAGI_MASK_INVCAUSAL)) return ks;
+  const int64_t b = (int64_t)s.k_start - (int64_t)s.q_start + row;
+  return b > ks ? b : ks;
 }
 
 // The slice lists a kernel walks (device copies of a schedule).
@@ -75,14 +84,23 @@ struct SliceLists {
 // fit in 32 bits (the entry points reject nq or nk >= 2^31), so all of it is
 // 32-bit scalar arithmetic.
 struct SliceGeo {
-  int32_t ks;     // first key
+  int32_t ks;     // first key that any row of the item sees
   int32_t khi;    // one past the last key that any row of the item sees
-  int32_t kfull;  // keys below this are visible to every row of the item
-  int32_t ke;     // slice key end, clamped to nk
-  int32_t koff;   // k_end - q_end: a causal row r sees keys below koff + r + 1
-  int32_t causal;
+  int32_t kfull;  // keys below this pass the upper bound of every row of the item
+  int32_t klo;    // keys from this on pass the lower bound of every row of the item
+  int32_t koff;   // k_end - q_end: under the upper bound row r sees keys below koff + r + 1
+  int32_t loff;   // k_start - q_start: under the lower bound row r sees keys from loff + r
+  int32_t type;   // mask type: bit 0 = upper (causal) bound, bit 1 = lower bound
   int32_t si;     // position in the tile-slice list
 };
+
+// One past the last key row `row` of the item sees: with the upper bound
+// min(koff + row + 1, khi), which equals min(koff + row + 1, k_end) for the
+// item's rows because khi = min(koff + last row + 1, k_end).
+__device__ __forceinline__ int32_t geo_row_end(const SliceGeo& g, int32_t row) {
+  const int32_t e = g.koff + row + 1;
+  return (g.type & MAGI_MASK_CAUSAL) && e < g.khi ? e : g.khi;
+}
 
 // First slice at or after list position si (of the item's [.., slice_end))
 // that shows the item's query tokens [first_tok, last_tok] a key.  Returns
@@ -94,22 +112,26 @@ __device__ __forceinline__ bool find_slice(const SliceLists& L, int32_t slice_en
     const int sidx = const_ld(L.tile_slices + si);
     if (sidx < 0 || sidx >= L.num_slices) continue;
     const magi_attn_slice s = load_slice(L.slices, sidx);
-    const int32_t causal = s.mask_type == MAGI_MASK_CAUSAL;
+    const int32_t upper = s.mask_type & MAGI_MASK_CAUSAL, lower = s.mask_type & MAGI_MASK_INVCAUSAL;
     const int32_t ks = s.k_start > 0 ? s.k_start : 0;
     const int32_t ke = s.k_end < nk ? s.k_end : nk;
     // a well-formed schedule only lists slices that cover every row of the
-    // item (so qe > last_tok >= first_tok >= qs >= 0 and no sum below
+    // item (so qe > last_tok >= first_tok >= qs >= 0, and the host keeps
+    // k_start + (q_end - q_start) below 2^31 for a lower bound: no sum below
     // leaves 32 bits)
     if (ks >= ke || first_tok < s.q_start || last_tok >= s.q_end) continue;
     const int32_t koff = s.k_end - s.q_end;
-    const int32_t khi = causal ? (koff + last_tok + 1 < ke ? koff + last_tok + 1 : ke) : ke;
-    if (khi <= ks) continue;
-    g.ks = ks;
+    const int32_t loff = s.k_start - s.q_start;
+    const int32_t khi = upper ? (koff + last_tok + 1 < ke ? koff + last_tok + 1 : ke) : ke;
+    const int32_t kbeg = lower && loff + first_tok > ks ? loff + first_tok : ks;
+    if (khi <= kbeg) continue;
+    g.ks = kbeg;
     g.khi = khi;
-    g.kfull = causal ? (koff + first_tok + 1 < ke ? koff + first_tok + 1 : ke) : ke;
-    g.ke = ke;
+    g.kfull = upper ? (koff + first_tok + 1 < ke ? koff + first_tok + 1 : ke) : ke;
+    g.klo = lower && loff + last_tok > ks ? loff + last_tok : ks;
     g.koff = koff;
-    g.causal = causal;
+    g.loff = loff;
+    g.type = s.mask_type & (MAGI_MASK_CAUSAL | MAGI_MASK_INVCAUSAL);
     g.si = si;
     return true;
   }

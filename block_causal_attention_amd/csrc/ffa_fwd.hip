@@ -371,7 +371,7 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
     constexpr bool BOUNDED = decltype(bounded_tag)::value;
     while (T0.valid) {
       const int b1 = b0 == 2 ? 0 : b0 + 1;
-      const bool masked = T0.kt + TK > T0.geo.kfull;
+      const bool masked = T0.kt < T0.geo.klo || T0.kt + TK > T0.geo.kfull;
       const __bf16* Kb = Ks[b0];
       __attribute__((address_space(3))) __bf16* Vb = (__attribute__((address_space(3))) __bf16*)Vs[b0];
       TileRef T2;
@@ -402,16 +402,13 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
         if (masked) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
-            // keys at block offset >= lim are hidden from the row
-            int32_t re = T0.geo.ke;
-            if (T0.geo.causal) {
-              const int32_t ce = T0.geo.koff + qi[nb] + 1;
-              re = ce < re ? ce : re;
-            }
-            const int32_t lim = re - T0.kt - kb * 32 - 4 * h;
+            // keys at block offset >= lim or < lim_lo are hidden from the row
+            const int32_t kb0 = T0.kt + kb * 32 + 4 * h;
+            const int32_t lim = geo_row_end(T0.geo, qi[nb]) - kb0;
+            const int32_t lim_lo = (T0.geo.type & MAGI_MASK_INVCAUSAL) ? T0.geo.loff + qi[nb] - kb0 : -TK;
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-              if (key_of0(i) >= lim) sc[nb][i] = -INFINITY;
+              if (key_of0(i) >= lim || key_of0(i) < lim_lo) sc[nb][i] = -INFINITY;
           }
         }
         // row maxima of the shifted scores; move m only where needed (the
@@ -563,8 +560,8 @@ __global__ __launch_bounds__(kThreads) void ffa_fwd_f32(FfaArgs a) {
     if (qi < sl.q_start || qi >= sl.q_end) continue;
     const int64_t ks = sl.k_start > 0 ? sl.k_start : 0;
     const int64_t ke = sl.k_end < a.nk ? sl.k_end : a.nk;
-    const int64_t re = sl.mask_type == MAGI_MASK_CAUSAL ? causal_end(sl, ke, qi) : ke;
-    for (int64_t key = ks; key < re; ++key) {
+    const int64_t re = row_key_end(sl, ke, qi);
+    for (int64_t key = row_key_begin(sl, ks, qi); key < re; ++key) {
       const float* kr = kp + key * a.kv_stride + (int64_t)g * a.kv_hstride;
       const float* vr = vp + key * a.kv_stride + (int64_t)g * a.kv_hstride;
       float sdot = 0.f;

@@ -27,15 +27,52 @@ namespace {
 
 constexpr int kRowsPerTile = 256;  // query rows (tokens x heads of a group) per work item
 
-// Visible keys of row r under slice s: [s.k_start, row_end).
+// Bit 0 of the mask type: the bottom-right (causal) bound; bit 1: the
+// top-left (inverse causal) bound.
+inline bool has_upper(const magi_attn_slice& s) { return (s.mask_type & MAGI_MASK_CAUSAL) != 0; }
+inline bool has_lower(const magi_attn_slice& s) { return (s.mask_type & MAGI_MASK_INVCAUSAL) != 0; }
+
+// Visible keys of row r (q_start <= r < q_end) under slice s:
+// [row_begin, row_end).
 inline int64_t row_end(const magi_attn_slice& s, int64_t r) {
-  if (s.mask_type == MAGI_MASK_FULL) return s.k_end;
+  if (!has_upper(s)) return s.k_end;
   int64_t e = (int64_t)s.k_end - (int64_t)s.q_end + r + 1;
   return std::min<int64_t>(s.k_end, e);
 }
+inline int64_t row_begin(const magi_attn_slice& s, int64_t r) {
+  if (!has_lower(s)) return s.k_start;
+  return std::max<int64_t>(s.k_start, (int64_t)s.k_start + r - (int64_t)s.q_start);
+}
 
 inline int64_t row_count(const magi_attn_slice& s, int64_t r) {
-  return std::max<int64_t>(0, row_end(s, r) - s.k_start);
+  return std::max<int64_t>(0, row_end(s, r) - row_begin(s, r));
+}
+
+// First row of [r0, r1) (rows both slices cover) on which slices a and b
+// show a common key, or -1.  Inside a slice's rows each bound is linear in
+// the row (slope 1 on a diagonal, 0 otherwise), so the width of the shared
+// key range, min(ends) - max(begins), is concave and piecewise linear: its
+// maximum lies on an end row or where a diagonal bound crosses the other
+// slice's flat one.
+int64_t shared_row(const magi_attn_slice& a, const magi_attn_slice& b, int64_t r0, int64_t r1) {
+  std::vector<int64_t> cand = {r0, r1 - 1};
+  auto add = [&](int64_t r) {
+    for (int64_t x = r - 1; x <= r + 1; ++x)
+      if (x >= r0 && x < r1) cand.push_back(x);
+  };
+  if (has_upper(a) != has_upper(b)) {  // k_end - q_end + r + 1 of one meets k_end of the other
+    const magi_attn_slice& d = has_upper(a) ? a : b;
+    const magi_attn_slice& f = has_upper(a) ? b : a;
+    add((int64_t)f.k_end - d.k_end + d.q_end - 1);
+  }
+  if (has_lower(a) != has_lower(b)) {  // k_start - q_start + r of one meets k_start of the other
+    const magi_attn_slice& d = has_lower(a) ? a : b;
+    const magi_attn_slice& f = has_lower(a) ? b : a;
+    add((int64_t)f.k_start - d.k_start + d.q_start);
+  }
+  for (int64_t r : cand)
+    if (std::max(row_begin(a, r), row_begin(b, r)) < std::min(row_end(a, r), row_end(b, r))) return r;
+  return -1;
 }
 
 }  // namespace
@@ -151,12 +188,15 @@ extern "C" int32_t magi_schedule(const magi_attn_slice* slices, int32_t num_slic
   // validate slices
   for (int i = 0; i < num_slices; ++i) {
     const magi_attn_slice& s = slices[i];
-    if (s.mask_type != MAGI_MASK_FULL && s.mask_type != MAGI_MASK_CAUSAL)
+    if (s.mask_type < MAGI_MASK_FULL || s.mask_type > MAGI_MASK_BICAUSAL)
       return fail(MAGI_ERR_INVALID_ARG, "slice %d: unknown mask type %d", i, s.mask_type);
     if (s.q_start < 0 || s.q_start > s.q_end || s.q_end > nq || s.k_start < 0 || s.k_start > s.k_end ||
         s.k_end > nk)
       return fail(MAGI_ERR_INVALID_ARG, "slice %d: range q[%d,%d) k[%d,%d) outside [0,%lld)x[0,%lld)", i,
                   s.q_start, s.q_end, s.k_start, s.k_end, (long long)nq, (long long)nk);
+    // the kernels form k_start + (r - q_start) in 32 bits
+    if (has_lower(s) && (int64_t)s.k_start + (s.q_end - s.q_start) > INT32_MAX)
+      return fail(MAGI_ERR_INVALID_ARG, "slice %d: k_start + (q_end - q_start) exceeds int32", i);
   }
 
   // cut the query axis at every slice boundary
@@ -177,14 +217,28 @@ extern "C" int32_t magi_schedule(const magi_attn_slice* slices, int32_t num_slic
     for (size_t g = a; g < nseg && cuts[g] < s.q_end; ++g) cover[g].push_back(i);
   }
 
-  // overlap check: key ranges only grow with the row, so two slices that
-  // share a (q, k) pair anywhere in a segment share one on its last row
+  // overlap check.  Without a lower bound a slice's key range only grows
+  // with the row, so two such slices that share a (q, k) pair anywhere in a
+  // segment share one on its last row; a slice with a lower bound is checked
+  // against every other slice of the segment (shared_row).
   for (size_t g = 0; g < nseg; ++g) {
     if (cover[g].size() < 2) continue;
     const int64_t r = cuts[g + 1] - 1;
+    for (size_t x = 0; x < cover[g].size(); ++x) {
+      const magi_attn_slice& a = slices[cover[g][x]];
+      if (!has_lower(a)) continue;
+      for (size_t y = 0; y < cover[g].size(); ++y) {
+        const magi_attn_slice& b = slices[cover[g][y]];
+        if (y == x || (has_lower(b) && y < x)) continue;
+        const int64_t row = shared_row(a, b, cuts[g], cuts[g + 1]);
+        if (row >= 0)
+          return fail(MAGI_ERR_OVERLAP, "slices %d and %d overlap at query row %lld", cover[g][x], cover[g][y],
+                      (long long)row);
+      }
+    }
     std::vector<std::pair<int64_t, int64_t>> iv;
-    std::vector<int32_t> who;
     for (int32_t i : cover[g]) {
+      if (has_lower(slices[i])) continue;
       int64_t e = row_end(slices[i], r);
       if (e > slices[i].k_start) iv.push_back({slices[i].k_start, e});
     }
@@ -244,11 +298,34 @@ namespace magi {
 namespace {
 constexpr int kKeysPerTile = 128;  // keys of one KV group per backward work item
 
-// Rows of slice s that see key k: [first, s.q_end).
+// Rows of slice s that see key k (k_start <= k < k_end): [col_first, col_end).
 inline int64_t col_first(const magi_attn_slice& s, int64_t k) {
-  if (s.mask_type == MAGI_MASK_FULL) return s.q_start;
-  // causal, bottom-right aligned: row r sees k iff k < k_end - q_end + r + 1
+  if (!has_upper(s)) return s.q_start;
+  // bottom-right aligned: row r sees k iff k < k_end - q_end + r + 1
   return std::max<int64_t>(s.q_start, k - ((int64_t)s.k_end - (int64_t)s.q_end));
+}
+inline int64_t col_end(const magi_attn_slice& s, int64_t k) {
+  if (!has_lower(s)) return s.q_end;
+  // top-left aligned: row r sees k iff k >= k_start + r - q_start
+  return std::min<int64_t>(s.q_end, k - (int64_t)s.k_start + (int64_t)s.q_start + 1);
+}
+inline int64_t col_count(const magi_attn_slice& s, int64_t k) {
+  return std::max<int64_t>(0, col_end(s, k) - col_first(s, k));
+}
+// Whether some row of s sees a key of [k0, k1) (inside s's key range).  The
+// row count is concave and piecewise linear in the key, with breaks where a
+// diagonal bound reaches the first or last row.
+inline bool any_col(const magi_attn_slice& s, int64_t k0, int64_t k1) {
+  std::vector<int64_t> cand = {k0, k1 - 1};
+  auto add = [&](int64_t k) {
+    for (int64_t x = k - 1; x <= k + 1; ++x)
+      if (x >= k0 && x < k1) cand.push_back(x);
+  };
+  if (has_upper(s)) add((int64_t)s.q_start + s.k_end - s.q_end);
+  if (has_lower(s)) add((int64_t)s.q_end + s.k_start - s.q_start - 1);
+  for (int64_t k : cand)
+    if (col_count(s, k) > 0) return true;
+  return false;
 }
 }  // namespace
 }  // namespace magi
@@ -298,7 +375,7 @@ extern "C" int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_s
     if (s.q_start >= s.q_end || s.k_start >= s.k_end) continue;
     size_t a = std::lower_bound(cuts.begin(), cuts.end(), (int64_t)s.k_start) - cuts.begin();
     for (size_t g = a; g < nseg && cuts[g] < s.k_end; ++g)
-      if (col_first(s, cuts[g]) < s.q_end) cover[g].push_back(i);
+      if (any_col(s, cuts[g], cuts[g + 1])) cover[g].push_back(i);
   }
   for (auto& c : cover)
     std::sort(c.begin(), c.end(), [&](int32_t x, int32_t y) {
@@ -314,7 +391,7 @@ extern "C" int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_s
       Tile t{t0, std::min<int64_t>(tile_k, cuts[g + 1] - t0), g, {}};
       for (int32_t i : cover[g]) {
         int64_t c = 0;
-        for (int64_t k = t0; k < t0 + t.len; ++k) c += std::max<int64_t>(0, slices[i].q_end - col_first(slices[i], k));
+        for (int64_t k = t0; k < t0 + t.len; ++k) c += col_count(slices[i], k);
         t.pairs.push_back(c);
         total += c;
         largest = std::max(largest, c);
@@ -355,31 +432,28 @@ extern "C" int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_s
         const int64_t nw = (c + T - 1) / T;
         int64_t run = 0, cut = 1;
         const size_t wfirst = units.size();
-        int32_t lo = (int32_t)col_first(sl, t.k0);
         const int32_t k_hi = (int32_t)std::min<int64_t>(t.k0 + t.len, sl.k_end);
         const int32_t k_lo = (int32_t)std::max<int64_t>(t.k0, sl.k_start);
-        for (int32_t r = lo; r < sl.q_end; ++r) {
-          // keys of the tile row r sees
-          int64_t kend = k_hi;
-          if (sl.mask_type == MAGI_MASK_CAUSAL)
-            kend = std::min<int64_t>(kend, (int64_t)sl.k_end - sl.q_end + r + 1);
-          run += std::max<int64_t>(0, kend - k_lo);
+        // rows that see a key of the tile, and the keys of the tile row r sees
+        int32_t lo = (int32_t)col_first(sl, k_lo);
+        const int32_t r_end = (int32_t)col_end(sl, k_hi - 1);
+        auto tile_keys = [&](int64_t r) {
+          return std::max<int64_t>(0, std::min<int64_t>(k_hi, row_end(sl, r)) -
+                                          std::max<int64_t>(k_lo, row_begin(sl, r)));
+        };
+        for (int32_t r = lo; r < r_end; ++r) {
+          run += tile_keys(r);
           if (cut < nw && run * nw >= c * cut) {
             units.push_back({ti, j, j + 1, 0, 0, 0, lo, r + 1});
             lo = r + 1;
             ++cut;
           }
         }
-        if (lo < sl.q_end) units.push_back({ti, j, j + 1, 0, 0, 0, lo, sl.q_end});
+        if (lo < r_end) units.push_back({ti, j, j + 1, 0, 0, 0, lo, r_end});
         // pairs of each window
         for (size_t u = wfirst; u < units.size(); ++u) {
           int64_t pc = 0;
-          for (int32_t r = units[u].lo; r < units[u].hi; ++r) {
-            int64_t kend = k_hi;
-            if (sl.mask_type == MAGI_MASK_CAUSAL)
-              kend = std::min<int64_t>(kend, (int64_t)sl.k_end - sl.q_end + r + 1);
-            pc += std::max<int64_t>(0, kend - k_lo);
-          }
+          for (int32_t r = units[u].lo; r < units[u].hi; ++r) pc += tile_keys(r);
           units[u].cost = pc;
         }
         a = j + 1;
@@ -525,5 +599,56 @@ extern "C" int32_t magi_slices_ring(const magi_ring_desc* d, magi_attn_slice* sl
   if (slice_cap < (int32_t)out.size())
     return fail(MAGI_ERR_BUFFER_TOO_SMALL, "slice_cap %d < %d", slice_cap, (int32_t)out.size());
   for (size_t i = 0; i < out.size(); ++i) slices[i] = {out[i].q0, out[i].q1, out[i].k0, out[i].k1, MAGI_MASK_FULL};
+  return ok();
+}
+
+extern "C" int32_t magi_slices_window(const magi_window_desc* descs, int32_t num_descs, magi_attn_slice* slices,
+                                      int32_t slice_cap, int32_t* num_slices) {
+  if (num_slices == nullptr) return fail(MAGI_ERR_INVALID_ARG, "num_slices is NULL");
+  if (num_descs < 0) return fail(MAGI_ERR_INVALID_ARG, "num_descs < 0");
+  if (num_descs > 0 && descs == nullptr) return fail(MAGI_ERR_INVALID_ARG, "descs is NULL");
+  if (slice_cap < 0) return fail(MAGI_ERR_INVALID_ARG, "slice_cap < 0");
+  if (slices == nullptr && slice_cap != 0) return fail(MAGI_ERR_INVALID_ARG, "slices is NULL but slice_cap > 0");
+  struct Span { int64_t a, b; int idx; };
+  std::vector<Span> qs, ks;
+  int64_t need = 0;
+  for (int i = 0; i < num_descs; ++i) {
+    const magi_window_desc& d = descs[i];
+    if (d.len < 0 || d.q_offset < 0 || d.k_offset < 0)
+      return fail(MAGI_ERR_INVALID_ARG, "sequence %d: negative length or offset", i);
+    if (d.window < 1) return fail(MAGI_ERR_INVALID_ARG, "sequence %d: window %d < 1", i, d.window);
+    if ((int64_t)d.q_offset + d.len > INT32_MAX || (int64_t)d.k_offset + d.len > INT32_MAX)
+      return fail(MAGI_ERR_INVALID_ARG, "sequence %d: ranges exceed int32", i);
+    if (d.len == 0) continue;
+    qs.push_back({d.q_offset, (int64_t)d.q_offset + d.len, i});
+    ks.push_back({d.k_offset, (int64_t)d.k_offset + d.len, i});
+    need += d.window >= d.len ? 1 : (d.window > 1 ? 2 : 1);
+  }
+  for (auto* v : {&qs, &ks}) {
+    std::sort(v->begin(), v->end(), [](const Span& x, const Span& y) { return x.a < y.a; });
+    for (size_t j = 1; j < v->size(); ++j)
+      if ((*v)[j].a < (*v)[j - 1].b)
+        return fail(MAGI_ERR_OVERLAP, "sequences %d and %d overlap in the %s index space", (*v)[j - 1].idx,
+                    (*v)[j].idx, v == &qs ? "query" : "key");
+  }
+  if (need > INT32_MAX) return fail(MAGI_ERR_INVALID_ARG, "too many slices");
+  *num_slices = (int32_t)need;
+  if (slices == nullptr && slice_cap == 0) return ok();
+  if (slice_cap < need) return fail(MAGI_ERR_BUFFER_TOO_SMALL, "slice_cap %d < %lld", slice_cap, (long long)need);
+  int32_t n = 0;
+  for (int i = 0; i < num_descs; ++i) {
+    const magi_window_desc& d = descs[i];
+    if (d.len == 0) continue;
+    const int32_t q0 = d.q_offset, k0 = d.k_offset, L = d.len, w = d.window;
+    if (w >= L) {
+      // the window reaches back to the sequence start for every row
+      slices[n++] = {q0, q0 + L, k0, k0 + L, MAGI_MASK_CAUSAL};
+      continue;
+    }
+    // rows 0 .. w-2 see the sequence start: a causal square; the rest see a
+    // band of w keys ending at themselves
+    if (w > 1) slices[n++] = {q0, q0 + w - 1, k0, k0 + w - 1, MAGI_MASK_CAUSAL};
+    slices[n++] = {q0 + w - 1, q0 + L, k0, k0 + L, MAGI_MASK_BICAUSAL};
+  }
   return ok();
 }

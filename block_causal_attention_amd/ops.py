@@ -14,7 +14,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import AttnSlice, CrossDesc, KvReduce, RingDesc, SeqDesc, WorkItem, check, lib
+from ._lib import AttnSlice, CrossDesc, KvReduce, RingDesc, SeqDesc, WindowDesc, WorkItem, check, lib
 
 LN2 = 0.6931471805599453
 LOG2E = 1.4426950408889634
@@ -78,6 +78,20 @@ def build_cross_slices(samples: Sequence) -> np.ndarray:
     cnt = C.c_int32(0)
     out = np.empty((max(n, 1), 5), np.int32)
     check(lib().magi_slices_cross(descs, n, out.ctypes.data_as(C.POINTER(AttnSlice)), out.shape[0], C.byref(cnt)))
+    return out[:cnt.value]
+
+
+def build_window_slices(seqs: Sequence) -> np.ndarray:
+    """magi_slices_window: packed causal sliding-window sequences (len,
+    window, q_offset, k_offset) -> int32 [n, 5] slices (CAUSAL for the rows
+    whose window reaches the sequence start, BICAUSAL bands for the rest)."""
+    n = len(seqs)
+    descs = (WindowDesc * max(n, 1))()
+    for i, (ln, w, qo, ko) in enumerate(seqs):
+        descs[i] = WindowDesc(int(ln), int(w), int(qo), int(ko))
+    cnt = C.c_int32(0)
+    out = np.empty((2 * max(n, 1), 5), np.int32)
+    check(lib().magi_slices_window(descs, n, out.ctypes.data_as(C.POINTER(AttnSlice)), out.shape[0], C.byref(cnt)))
     return out[:cnt.value]
 
 

@@ -45,11 +45,23 @@ typedef enum {
   MAGI_ERR_HIP = -5               /* a HIP call failed (message has the HIP error) */
 } magi_status;
 
+/* Mask type of a slice.  The pages build every mask from full and causal
+ * pieces and name sliding-window attention as the next mask form (interview
+ * with Zhang Zheng, answer on FFA's mask types).  A token-level sliding
+ * window needs a lower bound on the keys that moves with the row, which no
+ * union of full and bottom-right causal rectangles gives; the two types
+ * after CAUSAL add it (bit 0 of the type = the upper, bottom-right bound,
+ * bit 1 = the lower, top-left bound). */
 typedef enum {
-  MAGI_MASK_FULL = 0,   /* every (q, k) pair of the rectangle is visible */
-  MAGI_MASK_CAUSAL = 1  /* lower triangle aligned at the bottom-right corner:
-                           row r of [q_start, q_end) sees k in [k_start, k_end)
-                           with k - k_end <= r - q_end */
+  MAGI_MASK_FULL = 0,      /* every (q, k) pair of the rectangle is visible */
+  MAGI_MASK_CAUSAL = 1,    /* lower triangle aligned at the bottom-right corner:
+                              row r of [q_start, q_end) sees k in [k_start, k_end)
+                              with k - k_end <= r - q_end */
+  MAGI_MASK_INVCAUSAL = 2, /* upper triangle aligned at the top-left corner:
+                              row r sees k in [k_start, k_end) with
+                              k - k_start >= r - q_start */
+  MAGI_MASK_BICAUSAL = 3   /* both bounds: a band of k_end - k_start - (q_end - q_start) + 1
+                              keys per row, e.g. a sliding window */
 } magi_mask_type;
 
 typedef enum { MAGI_DTYPE_BF16 = 0, MAGI_DTYPE_FP32 = 1 } magi_dtype;
@@ -104,6 +116,15 @@ typedef struct {
   int32_t q_offset, q_len;  /* video tokens of the sample in the packed Q index space */
   int32_t k_offset, k_len;  /* its condition tokens in the packed K index space */
 } magi_cross_desc;
+
+/* One packed sequence under causal sliding-window attention: every token
+ * sees itself and the window - 1 tokens before it in its own sequence. */
+typedef struct {
+  int32_t len;       /* tokens of the sequence (its queries and keys alike), >= 0 */
+  int32_t window;    /* keys per row, >= 1 (window >= len is plain causal attention) */
+  int32_t q_offset;  /* first row of the sequence in the packed Q index space */
+  int32_t k_offset;  /* first row of the sequence in the packed K index space */
+} magi_window_desc;
 
 /* Library version string (static storage). */
 const char* magi_version(void);
@@ -169,6 +190,24 @@ int32_t magi_slices_cross(const magi_cross_desc* descs, int32_t num_descs,
                           magi_attn_slice* slices, int32_t slice_cap, int32_t* num_slices);
 
 /*
+ * magi_slices_window -- packed causal sliding-window mask -> AttnSlices.
+ *                                                                [host only]
+ *
+ * Sliding-window attention is the mask form the pages name as the next one
+ * for FFA (interview with Zhang Zheng, answer on FFA's mask types); the
+ * window here is counted in tokens, row r of a sequence starting at s seeing
+ * keys [max(s, r - window + 1), r].  Per sequence of len tokens and window
+ * w: one CAUSAL slice when w >= len; otherwise a CAUSAL slice over the first
+ * w - 1 rows and keys (when w > 1) and a BICAUSAL slice
+ * q = [q_offset + w - 1, q_offset + len), k = [k_offset, k_offset + len),
+ * whose band is exactly w keys wide.  Sequences must not overlap each other
+ * in either index space (MAGI_ERR_OVERLAP).  Output, size query and errors
+ * as magi_slices_build.
+ */
+int32_t magi_slices_window(const magi_window_desc* descs, int32_t num_descs,
+                           magi_attn_slice* slices, int32_t slice_cap, int32_t* num_slices);
+
+/*
  * magi_default_tile_q -- query tokens per work item that magi_ffa_fwd's
  * kernel is built for at this shape (the kernel covers 256 query rows =
  * tile_q tokens x (hq/hkv) heads).  Returns < 0 on unsupported shapes.
@@ -179,7 +218,8 @@ int32_t magi_default_tile_q(int32_t hq, int32_t hkv, int32_t head_dim, int32_t d
  * magi_schedule -- AttnSlices -> atomic-free work list.          [host only]
  *
  * Validates the slices (ranges inside [0,nq) x [0,nk), known mask type, no
- * (q, k) pair listed twice), cuts the query axis at every slice boundary,
+ * (q, k) pair listed twice, k_start + (q_end - q_start) < 2^31 for a type
+ * with the top-left bound), cuts the query axis at every slice boundary,
  * tiles each piece into tiles of at most tile_q tokens (tile_q = 0 picks
  * magi_default_tile_q), and emits one work item per (tile, KV group),
  * including tiles no slice covers (their rows get O = 0, LSE = -inf).

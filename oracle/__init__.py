@@ -14,6 +14,7 @@ Functions (each cites the passage it follows in its docstring):
   rope_3d          rotary embedding over (t, h, w) coordinates
   video_mask       dense block-causal / KV-range / packed-video mask rows
   slices_mask      dense mask rows denoted by a list of AttnSlices
+  window_mask      dense packed causal sliding-window mask rows
   attention        masked softmax attention with grouped K/V heads
   attention_backward  its gradients with respect to q, k and v
   forward          qk_norm -> rope_3d -> attention, end to end
@@ -26,6 +27,6 @@ do not state them, so those readings are "parity unpinned" with respect to the
 model, while the oracle-vs-kernel parity is fully pinned.
 """
 from .reference import (  # noqa: F401
-    qk_norm, rope_inv_freq, rope_3d, video_mask, slices_mask, attention, attention_backward, forward,
-    MASK_FULL, MASK_CAUSAL,
+    qk_norm, rope_inv_freq, rope_3d, video_mask, slices_mask, window_mask, attention, attention_backward,
+    forward, MASK_FULL, MASK_CAUSAL, MASK_INVCAUSAL, MASK_BICAUSAL,
 )

@@ -12,6 +12,8 @@ import numpy as np
 
 MASK_FULL = 0
 MASK_CAUSAL = 1
+MASK_INVCAUSAL = 2
+MASK_BICAUSAL = 3
 
 
 def qk_norm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
@@ -125,6 +127,13 @@ def slices_mask(slices, nq: int, nk: int, q_rows=None) -> np.ndarray:
     slice is aligned at its bottom-right corner: row r of [qs, qe) sees keys
     k in [ks, ke) with k - ke <= r - qe, which for a square slice is the
     ordinary lower triangle.  A pair listed by two slices is an error.
+
+    Sliding-window attention, which the interview names as the next mask
+    form for FFA, needs a lower key bound that moves with the row; two more
+    types give it (the reading taken here): an inverse causal slice is
+    aligned at its top-left corner, row r seeing k with k - ks >= r - qs
+    (for a square slice the upper triangle with the diagonal), and a
+    bicausal slice applies both bounds (a band).
     """
     q_rows = np.arange(nq) if q_rows is None else np.asarray(q_rows)
     m = np.zeros((len(q_rows), nk), bool)
@@ -134,13 +143,40 @@ def slices_mask(slices, nq: int, nk: int, q_rows=None) -> np.ndarray:
         if not (0 <= qs <= qe <= nq and 0 <= ks <= ke <= nk):
             raise ValueError(f"slice out of range: {(qs, qe, ks, ke)}")
         cell = (r >= qs) & (r < qe) & (kk >= ks) & (kk < ke)
-        if t == MASK_CAUSAL:
-            cell &= (kk - ke) <= (r - qe)
-        elif t != MASK_FULL:
+        if t not in (MASK_FULL, MASK_CAUSAL, MASK_INVCAUSAL, MASK_BICAUSAL):
             raise ValueError(f"unknown mask type {t}")
+        if t in (MASK_CAUSAL, MASK_BICAUSAL):
+            cell &= (kk - ke) <= (r - qe)
+        if t in (MASK_INVCAUSAL, MASK_BICAUSAL):
+            cell &= (kk - ks) >= (r - qs)
         if np.any(m & cell):
             raise ValueError("slices overlap")
         m |= cell
+    return m
+
+
+def window_mask(seqs, nq: int, nk: int, q_rows=None) -> np.ndarray:
+    """Dense boolean mask rows [len(q_rows), nk] of packed causal
+    sliding-window attention.
+
+    ``seqs`` holds (length, window, q_offset, k_offset) per sequence: query
+    token i of a sequence sees key token j of the same sequence iff
+    i - window < j <= i (positions counted from the sequence start).  The
+    interview names sliding-window attention as the mask form FFA is to
+    support next ([interview], answer on FFA's mask types) without defining
+    it; this is the usual causal reading, the window counted in tokens and
+    including the token itself.  Packed sequences never see each other
+    ([interview] packed videos must not see each other).
+    """
+    q_rows = np.arange(nq) if q_rows is None else np.asarray(q_rows)
+    m = np.zeros((len(q_rows), nk), bool)
+    kk = np.arange(nk)[None, :]
+    r = q_rows[:, None]
+    for length, window, qo, ko in seqs:
+        pos_q = r - qo
+        pos_k = kk - ko
+        inside = (pos_q >= 0) & (pos_q < length) & (pos_k >= 0) & (pos_k < length)
+        m |= inside & (pos_k <= pos_q) & (pos_k > pos_q - window)
     return m
 
 

@@ -202,3 +202,32 @@ def test_bwd_fuzz_raw_slices(case):
     note(f"bwd fuzz case {case}: d={d} G={G} hkv={hkv} nq={nq} nk={nk} slices={len(sl)}")
     bwd_case(rand((nq, G * hkv, d), 6000 + case), rand((nk, hkv, d), 7000 + case), rand((nk, hkv, d), 8000 + case),
              rand((nq, G * hkv, d), 9000 + case), sl, "bf16")
+
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_bwd_fuzz_all_slice_types(case):
+    # random slices of all four types, lower key bounds included
+    from test_gpu_parity import random_slices
+    rng = np.random.Generator(np.random.PCG64(5100 + case))
+    d, hkv = int(rng.choice([24, 48])), int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 3, 8, 16]))
+    nq, nk = int(rng.integers(1, 200)), int(rng.integers(1, 260))
+    sl = random_slices(rng, nq, nk, all_types=True)
+    note(f"bwd all-types fuzz case {case}: d={d} G={G} hkv={hkv} nq={nq} nk={nk} slices={len(sl)}")
+    args = (rand((nq, G * hkv, d), 6100 + case), rand((nk, hkv, d), 7100 + case), rand((nk, hkv, d), 8100 + case),
+            rand((nq, G * hkv, d), 9100 + case), sl)
+    bwd_case(*args, "bf16")
+    bwd_case(*args, "fp32")
+
+
+@pytest.mark.parametrize("d", [24, 48])
+@pytest.mark.parametrize("window", [5, 160])
+def test_bwd_sliding_window(d, window):
+    # gradients of causal sliding-window attention over two packed
+    # sequences, long enough that key tiles are split into parts
+    note(f"bwd sliding window d={d} w={window}")
+    spec = [(600, window, 0, 0), (300, window, 600, 600)]
+    sl = ops.build_window_slices(spec)
+    n = 900
+    bwd_case(rand((n, 32, d), 71), rand((n, 2, d), 72), rand((n, 2, d), 73), rand((n, 32, d), 74), sl, "bf16")

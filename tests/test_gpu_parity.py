@@ -255,9 +255,10 @@ def test_ffa_no_keys_and_scale():
     ffa_case(rand((30, 16, 24), 11, 3.0), rand((50, 1, 24), 12, 3.0), rand((50, 1, 24), 13), sl, "bf16", scale=0.05)
 
 
-def random_slices(rng, nq, nk):
+def random_slices(rng, nq, nk, all_types=False):
     """Disjoint AttnSlices: query bands, each with a few disjoint key ranges,
-    FULL or CAUSAL (bottom-right aligned), some bands and gaps left empty."""
+    FULL or CAUSAL (bottom-right aligned; with all_types also INVCAUSAL and
+    BICAUSAL), some bands and gaps left empty."""
     slices = []
     q = 0
     while q < nq:
@@ -266,7 +267,8 @@ def random_slices(rng, nq, nk):
             k = int(rng.integers(0, 8))
             while k < nk:
                 ke = min(nk, k + int(rng.integers(1, 90)))
-                slices.append((q, qe, k, ke, int(rng.random() < 0.4)))
+                t = int(rng.integers(0, 4)) if all_types else int(rng.random() < 0.4)
+                slices.append((q, qe, k, ke, t))
                 k = ke + int(rng.integers(0, 20))
         q = qe + int(rng.integers(0, 5))
     return np.array(slices, np.int32).reshape(-1, 5)
@@ -283,6 +285,91 @@ def test_ffa_fuzz_raw_slices(case):
     note(f"ffa fuzz case {case}: d={d} G={G} hkv={hkv} nq={nq} nk={nk} slices={len(sl)}")
     ffa_case(rand((nq, G * hkv, d), 2000 + case), rand((nk, hkv, d), 3000 + case), rand((nk, hkv, d), 4000 + case),
              sl, "bf16")
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_ffa_fuzz_all_slice_types(case):
+    # random slices of all four types (lower key bounds included), bf16 with
+    # and without the key-norm bound, and the fp32 kernel
+    rng = np.random.Generator(np.random.PCG64(1100 + case))
+    d, hkv = int(rng.choice([24, 48])), int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 3, 8, 16]))
+    nq, nk = int(rng.integers(1, 260)), int(rng.integers(1, 330))
+    sl = random_slices(rng, nq, nk, all_types=True)
+    note(f"ffa all-types fuzz case {case}: d={d} G={G} hkv={hkv} nq={nq} nk={nk} slices={len(sl)}")
+    q, k, v = rand((nq, G * hkv, d), 2100 + case), rand((nk, hkv, d), 3100 + case), rand((nk, hkv, d), 4100 + case)
+    ffa_case(q, k, v, sl, "bf16")
+    kb = np.linalg.norm(k.astype(np.float64), axis=-1).max(axis=0) * 1.01
+    ffa_case(q, k, v, sl, "bf16", knm=kb)
+    ffa_case(q, k, v, sl, "fp32")
+
+
+def window_forward(wl, inp, spec, d):
+    """prologue + FFA over sliding-window slices, in the benchmark's
+    configuration (scale folded into K, K/V group-major, key-norm bound)"""
+    knm = torch.empty(wl.hkv, dtype=torch.float32, device=DEV)
+    kg = ops.kv_group_major(wl.nk, wl.hkv, wl.head_dim, d["k"].dtype)
+    qh, kh, vh = ops.qknorm_rope(d["q"], d["k"], d["gq"], d["gk"], d["pq"], d["pk"], d["base"], wl.eps,
+                                 k_out=kg, k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm, v=d["v"])
+    plan = ops.make_plan(ops.build_window_slices(spec), wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, d["q"].dtype)
+    O, L = ops.ffa_fwd(qh, kh, vh, plan, softmax_scale=ops.LN2, k_norm_max=knm)
+    torch.cuda.synchronize()
+    return O, L
+
+
+@pytest.mark.parametrize("d", [24, 48])
+@pytest.mark.parametrize("window", [1, 37, 300, 720])
+def test_sliding_window_end_to_end(d, window):
+    # causal sliding-window attention over the tokens of a packed video
+    # (3 chunks x 240 tokens) and a second, shorter sequence, QK-Norm and 3D
+    # RoPE applied by the prologue, against the oracle's window mask
+    note(f"sliding window d={d} w={window}")
+    wl = W.custom_packed([(3, 2, 10, 12, None), (1, 2, 7, 9, None)], 32, 2, d)
+    inp = W.make_inputs(wl, 0)
+    dd = dev_inputs(wl, inp)
+    spec = [(720, window, 0, 0), (wl.nq - 720, window, 720, 720)]
+    O, L = window_forward(wl, inp, spec, dd)
+    mask = oracle.window_mask(spec, wl.nq, wl.nk)
+    Ow, Lw = oracle.forward(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.gain_q), np64(inp.gain_k),
+                            inp.pos_q.numpy(), inp.pos_k.numpy(), wl.rope_base, wl.eps, mask, wl.softmax_scale)
+    compare(np64(O), Ow, "bf16")
+    # LSE: with a handful of visible keys the rounding is not averaged out.
+    # q_hat and scale * log2(e) * k_hat are stored in bf16 (unit roundoff
+    # u = 2^-8), so a logit moves by up to 2u * scale * |q_hat| * |k_hat|;
+    # the denominator sums P after its own bf16 rounding, which moves
+    # ln(sum P) by up to u.  Per row the bound is that sum, at least the
+    # usual 1e-2.
+    inv = oracle.rope_inv_freq(wl.rope_base, wl.head_dim)
+    qn = np.linalg.norm(oracle.rope_3d(oracle.qk_norm(np64(inp.q), np64(inp.gain_q), wl.eps),
+                                       inp.pos_q.numpy(), inv), axis=-1)
+    kn = np.linalg.norm(oracle.rope_3d(oracle.qk_norm(np64(inp.k), np64(inp.gain_k), wl.eps),
+                                       inp.pos_k.numpy(), inv), axis=-1).max(axis=0)
+    u = 2.0 ** -8
+    bound = np.maximum(1e-2, 2 * u * wl.softmax_scale * qn * np.repeat(kn, wl.hq // wl.hkv)[None, :] * 1.05 + u)
+    Lg = np64(L)
+    assert np.array_equal(np.isfinite(Lg), np.isfinite(Lw))
+    err = np.abs(Lg - Lw)
+    note(f"LSE: max-abs {err.max():.3e}, worst err/bound {(err / bound).max():.3f}")
+    assert (err <= bound).all()
+
+
+def test_sliding_window_large_sampled():
+    # the 24B-shaped layer (8 chunks x 3600 tokens, 128/8 heads, d = 48) under
+    # a 3600-token window: sampled rows against the oracle
+    note("sliding window magi24b w=3600 sampled")
+    wl = W.make_workload("magi24b")
+    inp = W.make_inputs(wl, 0)
+    dd = dev_inputs(wl, inp)
+    spec = [(wl.nq, 3600, 0, 0)]
+    O, L = window_forward(wl, inp, spec, dd)
+    rows = W.sample_rows(wl, 192)
+    mask = oracle.window_mask(spec, wl.nq, wl.nk, rows)
+    keys = np.flatnonzero(mask.any(axis=0))
+    Ow, Lw = oracle.forward(np64(inp.q[rows]), np64(inp.k[keys]), np64(inp.v[keys]), np64(inp.gain_q),
+                            np64(inp.gain_k), inp.pos_q[rows].numpy(), inp.pos_k[keys].numpy(), wl.rope_base,
+                            wl.eps, mask[:, keys], wl.softmax_scale)
+    compare(np64(O)[rows], Ow, "bf16")
+    compare(np64(L)[rows], Lw, "bf16", "LSE")
 
 
 @pytest.mark.parametrize("d", [24, 48])

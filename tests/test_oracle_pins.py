@@ -12,8 +12,8 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from oracle import (MASK_CAUSAL, MASK_FULL, attention, qk_norm, rope_3d,
-                    rope_inv_freq, slices_mask, video_mask)
+from oracle import (MASK_BICAUSAL, MASK_CAUSAL, MASK_FULL, MASK_INVCAUSAL, attention, qk_norm, rope_3d,
+                    rope_inv_freq, slices_mask, video_mask, window_mask)
 from workloads import SeqDesc
 
 RNG = np.random.Generator(np.random.PCG64(1234))
@@ -469,3 +469,68 @@ def test_golden_packed_videos_mask():
     # [interview]: packed videos never see each other
     seqs = [SeqDesc(2, 2, 2, 0, 0, (-1, -1), 1, 1, 2), SeqDesc(1, 2, 2, 4, 4, (-1, -1), 1, 1, 1)]
     np.testing.assert_array_equal(oracle.video_mask(seqs, 6, 6), _golden("packed_two_videos.txt"))
+
+
+def test_golden_slice_types():
+    # the four slice types over one 4 x 6 rectangle, written out by hand
+    g = _golden("slice_types_4x6.txt")
+    for i, t in enumerate((MASK_FULL, MASK_CAUSAL, MASK_INVCAUSAL, MASK_BICAUSAL)):
+        np.testing.assert_array_equal(slices_mask([(0, 4, 0, 6, t)], 4, 6), g[4 * i:4 * i + 4])
+
+
+def test_golden_sliding_window_mask():
+    g = _golden("sliding_window_two_seqs.txt")
+    np.testing.assert_array_equal(window_mask([(6, 3, 0, 0), (4, 3, 6, 6)], 10, 10), g)
+
+
+def test_inverse_causal_is_causal_turned_half_round():
+    # turning both axes around maps a top-left aligned triangle onto a
+    # bottom-right aligned one, for any rectangle shape
+    rng = np.random.default_rng(5)
+    nq, nk = 9, 11
+    for _ in range(40):
+        qs, qe = sorted(rng.integers(0, nq + 1, 2))
+        ks, ke = sorted(rng.integers(0, nk + 1, 2))
+        inv = slices_mask([(qs, qe, ks, ke, MASK_INVCAUSAL)], nq, nk)
+        cau = slices_mask([(nq - qe, nq - qs, nk - ke, nk - ks, MASK_CAUSAL)], nq, nk)
+        np.testing.assert_array_equal(inv, cau[::-1, ::-1])
+        both = slices_mask([(qs, qe, ks, ke, MASK_BICAUSAL)], nq, nk)
+        np.testing.assert_array_equal(both, inv & slices_mask([(qs, qe, ks, ke, MASK_CAUSAL)], nq, nk))
+
+
+def test_square_slice_types_are_textbook_triangles():
+    n = 7
+    one = np.ones((n, n), bool)
+    np.testing.assert_array_equal(slices_mask([(0, n, 0, n, MASK_INVCAUSAL)], n, n), np.triu(one))
+    np.testing.assert_array_equal(slices_mask([(0, n, 0, n, MASK_BICAUSAL)], n, n), np.eye(n, dtype=bool))
+
+
+def test_window_mask_special_cases_and_counts():
+    n = 13
+    # a window as long as the sequence is plain causal attention, a window
+    # of one token sees only itself
+    np.testing.assert_array_equal(window_mask([(n, n, 0, 0)], n, n), np.tril(np.ones((n, n), bool)))
+    np.testing.assert_array_equal(window_mask([(n, 40, 0, 0)], n, n), np.tril(np.ones((n, n), bool)))
+    np.testing.assert_array_equal(window_mask([(n, 1, 0, 0)], n, n), np.eye(n, dtype=bool))
+    # brute force: row i of a sequence sees exactly min(w, i + 1) keys, the
+    # newest being itself
+    for w in (2, 3, 5):
+        m = window_mask([(n, w, 2, 1)], n + 2, n + 1)
+        for i in range(n):
+            row = m[2 + i]
+            assert row.sum() == min(w, i + 1)
+            assert row[1 + i] and not row[2 + i:].any()
+
+
+def test_window_mask_equals_attention_over_the_window_alone():
+    # the output of a row under the window equals plain softmax attention
+    # over exactly the keys of its window
+    rng = np.random.default_rng(8)
+    n, w, d = 10, 4, 6
+    q, k, v = (rng.standard_normal((n, 1, d)) for _ in range(3))
+    O, L = attention(q, k, v, window_mask([(n, w, 0, 0)], n, n), 0.5)
+    for i in range(n):
+        lo = max(0, i - w + 1)
+        s = 0.5 * k[lo:i + 1, 0] @ q[i, 0]
+        p = np.exp(s - s.max())
+        np.testing.assert_allclose(O[i, 0], p @ v[lo:i + 1, 0] / p.sum(), rtol=1e-12, atol=1e-12)

@@ -23,7 +23,7 @@ def header_functions():
 def test_library_exports_every_header_symbol():
     L = _lib.lib()
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -178,7 +178,7 @@ def test_schedule_fuzz_raw_slices(trial):
             k = int(rng.integers(0, 5))
             while k < nk:
                 ke = min(nk, k + int(rng.integers(1, 40)))
-                slices.append((q, qe, k, ke, int(rng.random() < 0.4)))
+                slices.append((q, qe, k, ke, int(rng.choice(4, p=[0.5, 0.2, 0.15, 0.15]))))
                 k = ke + int(rng.integers(0, 10))
         q = qe + int(rng.integers(0, 4))
     arr = np.array(slices, np.int32).reshape(-1, 5)
@@ -297,7 +297,7 @@ def test_schedule_kv_fuzz_raw_slices(trial):
             k = int(rng.integers(0, 5))
             while k < nk:
                 ke = min(nk, k + int(rng.integers(1, 40)))
-                slices.append((q, qe, k, ke, int(rng.random() < 0.4)))
+                slices.append((q, qe, k, ke, int(rng.choice(4, p=[0.5, 0.2, 0.15, 0.15]))))
                 k = ke + int(rng.integers(0, 10))
         q = qe + int(rng.integers(0, 4))
     arr = np.array(slices, np.int32).reshape(-1, 5)
@@ -325,6 +325,55 @@ def test_schedule_causal_overlap_detection():
     assert len(ok[0]) == 1
     # a tall causal slice whose early rows see nothing is not an overlap
     ops.schedule(np.array([(0, 8, 0, 2, 1), (0, 8, 2, 4, 0)]), 8, 4, 16, 1, 24, 0)
+
+
+def test_schedule_lower_bound_overlap_detection():
+    n = 8
+    cau = (0, n, 0, n, _lib.MASK_CAUSAL)
+    # the two triangles of one square share its diagonal
+    with pytest.raises(_lib.MagiError) as e:
+        ops.schedule(np.array([cau, (0, n, 0, n, _lib.MASK_INVCAUSAL)]), n, n + 1, 16, 1, 24, 0)
+    assert e.value.status == _lib.MAGI_ERR_OVERLAP
+    # shifted one key to the right they tile the rectangle [0, n) x [0, n + 1)
+    sl = np.array([cau, (0, n, 1, n + 1, _lib.MASK_INVCAUSAL)])
+    work, _ = check_schedule(sl, n, n + 1, 16, 1, 24)
+    np.testing.assert_array_equal(expand(sl, n, n + 1), np.ones((n, n + 1), bool))
+    # a band and a full rectangle that meet only where the band ends
+    band = (0, n, 0, n + 2, _lib.MASK_BICAUSAL)   # row r sees [r, r + 3)
+    ops.schedule(np.array([band, (0, n, n + 2, n + 5, 0)]), n, n + 5, 16, 1, 24, 0)
+    with pytest.raises(_lib.MagiError) as e:
+        ops.schedule(np.array([band, (0, n, n + 1, n + 5, 0)]), n, n + 5, 16, 1, 24, 0)
+    assert e.value.status == _lib.MAGI_ERR_OVERLAP
+    # k_start + (q_end - q_start) must stay inside int32 for a lower bound
+    with pytest.raises(_lib.MagiError) as e:
+        ops.schedule(np.array([(0, 4, 2 ** 31 - 3, 2 ** 31 - 1, _lib.MASK_INVCAUSAL)]), 4, 2 ** 31 - 1, 16, 1,
+                     24, 0)
+    assert e.value.status == _lib.MAGI_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("trial", range(12))
+def test_schedule_overlap_verdict_matches_brute_force(trial):
+    # random slices of every type in a small space, overlapping or not: the
+    # scheduler reports an overlap exactly when the dense masks share a pair
+    rng = np.random.Generator(np.random.PCG64(1300 + trial))
+    nq, nk = 12, 14
+    for _ in range(60):
+        sl = []
+        for _ in range(int(rng.integers(2, 4))):
+            qs, qe = sorted(int(x) for x in rng.integers(0, nq + 1, 2))
+            ks, ke = sorted(int(x) for x in rng.integers(0, nk + 1, 2))
+            sl.append((qs, qe, ks, ke, int(rng.integers(0, 4))))
+        try:
+            oracle.slices_mask(sl, nq, nk)
+            want = 0
+        except ValueError:
+            want = _lib.MAGI_ERR_OVERLAP
+        try:
+            ops.schedule(np.array(sl, np.int32), nq, nk, 16, 1, 24, 0)
+            got = 0
+        except _lib.MagiError as e:
+            got = e.status
+        assert got == want, sl
 
 
 def test_schedule_rejects_bad_arguments():
@@ -526,3 +575,60 @@ def test_ring_slices_match_chunk_windows():
     with pytest.raises(_lib.MagiError):
         ops.build_ring_slices(4, 3, 0, 3, 4)          # more in flight than present
     assert ops.ring_slot_runs(6, 4, 6) == [(4, 2), (0, 4)]
+
+
+# --------------------------------------------------------------------------- sliding window
+
+@pytest.mark.parametrize("trial", range(15))
+def test_window_builder_round_trip(trial):
+    rng = np.random.Generator(np.random.PCG64(1500 + trial))
+    spec, qo, ko = [], 0, 0
+    for _ in range(int(rng.integers(1, 5))):
+        ln = int(rng.integers(0, 30))
+        w = int(rng.integers(1, 35))
+        qo += int(rng.integers(0, 3))
+        ko += int(rng.integers(0, 3))
+        spec.append((ln, w, qo, ko))
+        qo += ln
+        ko += ln
+    sl = ops.build_window_slices(spec)
+    assert set(sl[:, 4]) <= {_lib.MASK_CAUSAL, _lib.MASK_BICAUSAL}
+    np.testing.assert_array_equal(expand(sl, qo, ko), oracle.window_mask(spec, qo, ko))
+    check_schedule(sl, qo, ko, 16, 2, 24)
+    check_schedule_kv(sl, qo, ko, 16, 2, 24, tile_k=int(rng.choice([0, 7])))
+
+
+def test_window_builder_slices_and_errors():
+    np.testing.assert_array_equal(ops.build_window_slices([(10, 4, 0, 0)]),
+                                  [[0, 3, 0, 3, _lib.MASK_CAUSAL], [3, 10, 0, 10, _lib.MASK_BICAUSAL]])
+    np.testing.assert_array_equal(ops.build_window_slices([(10, 1, 5, 2)]), [[5, 15, 2, 12, _lib.MASK_BICAUSAL]])
+    np.testing.assert_array_equal(ops.build_window_slices([(10, 10, 0, 0), (0, 3, 10, 10)]),
+                                  [[0, 10, 0, 10, _lib.MASK_CAUSAL]])
+    for bad, code in [([(10, 0, 0, 0)], _lib.MAGI_ERR_INVALID_ARG), ([(-1, 2, 0, 0)], _lib.MAGI_ERR_INVALID_ARG),
+                      ([(10, 2, -1, 0)], _lib.MAGI_ERR_INVALID_ARG),
+                      ([(10, 2, 2 ** 31 - 5, 0)], _lib.MAGI_ERR_INVALID_ARG),
+                      ([(10, 2, 0, 0), (10, 2, 5, 20)], _lib.MAGI_ERR_OVERLAP),
+                      ([(10, 2, 0, 0), (10, 2, 20, 9)], _lib.MAGI_ERR_OVERLAP)]:
+        with pytest.raises(_lib.MagiError) as e:
+            ops.build_window_slices(bad)
+        assert e.value.status == code
+    L = _lib.lib()
+    n = C.c_int32()
+    assert L.magi_slices_window(None, 1, None, 0, C.byref(n)) == _lib.MAGI_ERR_INVALID_ARG
+    assert L.magi_slices_window(None, 0, None, 0, None) == _lib.MAGI_ERR_INVALID_ARG
+    descs = (_lib.WindowDesc * 1)(_lib.WindowDesc(10, 4, 0, 0))
+    buf = (_lib.AttnSlice * 1)()
+    assert L.magi_slices_window(descs, 1, buf, 1, C.byref(n)) == _lib.MAGI_ERR_BUFFER_TOO_SMALL and n.value == 2
+    assert L.magi_slices_window(descs, 1, None, 0, C.byref(n)) == 0 and n.value == 2
+
+
+def test_window_schedule_costs_large():
+    # one 28,800-token sequence with a 3,600-token window: the area is
+    # closed form, sum over rows of min(w, i + 1)
+    n, w = 28800, 3600
+    sl = ops.build_window_slices([(n, w, 0, 0)])
+    work, _ = ops.schedule(sl, n, n, 128, 8, 48, _lib.DTYPE_BF16)
+    area = w * (w + 1) // 2 + (n - w) * w
+    assert work[:, 5].astype(np.int64).sum() == area * 8
+    work, _, ext, red, nslots = ops.schedule_kv(sl, n, n, 128, 8, 48, _lib.DTYPE_BF16)
+    assert work[:, 5].astype(np.int64).sum() == area * 8
