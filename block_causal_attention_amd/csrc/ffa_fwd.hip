@@ -365,13 +365,27 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
   lds_barrier();
   read_k(0, 0, kcur);  // unused if the item sees no key
   int b0 = 0;  // buffer of T0
-  // the tile loop, compiled once for bounded waves and once for waves with
-  // an online max
-  auto tile_loop = [&](auto bounded_tag) {
+  // Whether a slice of the item bounds its keys from below (inverse causal
+  // or band): only then do tiles below the diagonal need the second test.
+  // The head_dim 24 loop has one instance without that test (it saves 2 %
+  // there); head_dim 48 keeps a single instance, which is as fast as the
+  // test-free one while a second copy of its loop spills scalar registers.
+  bool lower = D == 48;
+  if constexpr (D != 48) {
+    const int end = wi.slice_end < a.num_tile_slices ? wi.slice_end : a.num_tile_slices;
+    for (int si = wi.slice_begin < 0 ? 0 : wi.slice_begin; si < end; ++si) {
+      const int sidx = const_ld(a.tile_slices + si);
+      if (sidx >= 0 && sidx < a.num_slices) lower |= (const_ld(&a.slices[sidx].mask_type) & MAGI_MASK_INVCAUSAL) != 0;
+    }
+  }
+  // the tile loop, compiled for bounded waves and for waves with an online
+  // max, each with and without lower key bounds
+  auto tile_loop = [&](auto bounded_tag, auto lower_tag) {
     constexpr bool BOUNDED = decltype(bounded_tag)::value;
+    constexpr bool LOWER = decltype(lower_tag)::value;
     while (T0.valid) {
       const int b1 = b0 == 2 ? 0 : b0 + 1;
-      const bool masked = T0.kt < T0.geo.klo || T0.kt + TK > T0.geo.kfull;
+      const bool masked = (LOWER && T0.kt < T0.geo.klo) || T0.kt + TK > T0.geo.kfull;
       const __bf16* Kb = Ks[b0];
       __attribute__((address_space(3))) __bf16* Vb = (__attribute__((address_space(3))) __bf16*)Vs[b0];
       TileRef T2;
@@ -405,10 +419,10 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
             // keys at block offset >= lim or < lim_lo are hidden from the row
             const int32_t kb0 = T0.kt + kb * 32 + 4 * h;
             const int32_t lim = geo_row_end(T0.geo, qi[nb]) - kb0;
-            const int32_t lim_lo = (T0.geo.type & MAGI_MASK_INVCAUSAL) ? T0.geo.loff + qi[nb] - kb0 : -TK;
+            const int32_t lim_lo = (LOWER && (T0.geo.type & MAGI_MASK_INVCAUSAL)) ? T0.geo.loff + qi[nb] - kb0 : -TK;
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-              if (key_of0(i) >= lim || key_of0(i) < lim_lo) sc[nb][i] = -INFINITY;
+              if (key_of0(i) >= lim || (LOWER && key_of0(i) < lim_lo)) sc[nb][i] = -INFINITY;
           }
         }
         // row maxima of the shifted scores; move m only where needed (the
@@ -494,10 +508,17 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
       b0 = b1;
     }
   };
-  if (bounded)
-    tile_loop(std::true_type{});
-  else
-    tile_loop(std::false_type{});
+  if (bounded) {
+    if (lower)
+      tile_loop(std::true_type{}, std::true_type{});
+    else if constexpr (D != 48)
+      tile_loop(std::true_type{}, std::false_type{});
+  } else {
+    if (lower)
+      tile_loop(std::false_type{}, std::true_type{});
+    else if constexpr (D != 48)
+      tile_loop(std::false_type{}, std::false_type{});
+  }
 
   // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
   __bf16* __restrict__ op = reinterpret_cast<__bf16*>(a.out);
