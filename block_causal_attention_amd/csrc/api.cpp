@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 
 #include "kernels.h"
 #include "status.h"
@@ -12,6 +13,14 @@
 using namespace magi;
 
 namespace {
+
+// Finite test on the bit pattern: no floating-point compile option (the
+// device pass of this file assumes no NaN) can fold it away.
+inline bool finite_bits(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, sizeof u);
+  return (u & 0x7f800000u) != 0x7f800000u;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -92,9 +101,9 @@ extern "C" int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, i
   if (nq > 0 && (gain_q == nullptr || pos_q == nullptr)) return fail(MAGI_ERR_INVALID_ARG, "gain_q / pos_q is NULL");
   if (gain_head_stride != 0 && gain_head_stride != head_dim)
     return fail(MAGI_ERR_INVALID_ARG, "gain_head_stride must be 0 or head_dim");
-  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MAGI_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!(eps >= 0.f) || !finite_bits(eps)) return fail(MAGI_ERR_INVALID_ARG, "eps must be finite and >= 0");
   if (rope_base == nullptr) return fail(MAGI_ERR_INVALID_ARG, "rope_base is NULL");
-  if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || q_scale == 0.f || k_scale == 0.f)
+  if (!finite_bits(q_scale) || !finite_bits(k_scale) || q_scale == 0.f || k_scale == 0.f)
     return fail(MAGI_ERR_INVALID_ARG, "q_scale and k_scale must be finite and non-zero");
 
   QkArgs a{};
@@ -142,7 +151,7 @@ int32_t ffa_fwd_args(FfaArgs& a, const void* q, const void* k, const void* v, vo
     return fail(MAGI_ERR_UNSUPPORTED, "kv row stride %lld >= 2^23 elements", (long long)kv_tok_stride);
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(MAGI_ERR_INVALID_ARG, "lse is not 4-byte aligned");
-  if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
+  if (!finite_bits(softmax_scale))
     return fail(MAGI_ERR_INVALID_ARG, "softmax_scale must be finite");
   if (k_norm_max != nullptr && (reinterpret_cast<uintptr_t>(k_norm_max) & 3u))
     return fail(MAGI_ERR_INVALID_ARG, "k_norm_max is not 4-byte aligned");
@@ -222,8 +231,8 @@ extern "C" int32_t magi_ffa_fwd_qknorm(const void* q_raw, const void* k, const v
     return fail(MAGI_ERR_INVALID_ARG, "gain_q / pos_q / rope_base is NULL");
   if (gain_head_stride != 0 && gain_head_stride != head_dim)
     return fail(MAGI_ERR_INVALID_ARG, "gain_head_stride must be 0 or head_dim");
-  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MAGI_ERR_INVALID_ARG, "eps must be finite and >= 0");
-  if (!std::isfinite(q_scale) || q_scale == 0.f) return fail(MAGI_ERR_INVALID_ARG, "q_scale must be finite, non-zero");
+  if (!(eps >= 0.f) || !finite_bits(eps)) return fail(MAGI_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!finite_bits(q_scale) || q_scale == 0.f) return fail(MAGI_ERR_INVALID_ARG, "q_scale must be finite, non-zero");
   if (q_hat != nullptr && (st = check_tensor("q_hat", q_hat, nq, hq, q_hat_stride, head_dim, dtype)) != MAGI_OK)
     return st;
   a.qn_gain = gain_q;
@@ -266,7 +275,7 @@ extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, con
   if (nq > 0 && (lse == nullptr || delta == nullptr)) return fail(MAGI_ERR_INVALID_ARG, "lse and delta are required");
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(delta) & 3u))
     return fail(MAGI_ERR_INVALID_ARG, "lse / delta not 4-byte aligned");
-  if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
+  if (!finite_bits(softmax_scale))
     return fail(MAGI_ERR_INVALID_ARG, "softmax_scale must be finite");
   if (num_slices < 0 || num_qwork < 0 || num_q_tile_slices < 0 || num_kwork < 0 || num_k_tile_slices < 0)
     return fail(MAGI_ERR_INVALID_ARG, "negative list length");
