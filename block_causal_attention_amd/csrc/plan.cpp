@@ -297,6 +297,7 @@ extern "C" int32_t magi_schedule(const magi_attn_slice* slices, int32_t num_slic
 namespace magi {
 namespace {
 constexpr int kKeysPerTile = 128;  // keys of one KV group per backward work item
+constexpr int kRowsPerQTile = 64;  // query rows (tokens x heads) per Q/dO tile of the dK/dV pass
 
 // Rows of slice s that see key k (k_start <= k < k_end): [col_first, col_end).
 inline int64_t col_first(const magi_attn_slice& s, int64_t k) {
@@ -441,9 +442,13 @@ extern "C" int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_s
           return std::max<int64_t>(0, std::min<int64_t>(k_hi, row_end(sl, r)) -
                                           std::max<int64_t>(k_lo, row_begin(sl, r)));
         };
+        // the dK/dV pass walks a window in row tiles of `step` tokens from
+        // its first row: windows of whole tiles leave a partial (masked)
+        // tile only at the end of the slice's rows
+        const int32_t step = std::max<int32_t>(1, kRowsPerQTile / (hq / hkv));
         for (int32_t r = lo; r < r_end; ++r) {
           run += tile_keys(r);
-          if (cut < nw && run * nw >= c * cut) {
+          if (cut < nw && run * nw >= c * cut && (r + 1 - lo) % step == 0) {
             units.push_back({ti, j, j + 1, 0, 0, 0, lo, r + 1});
             lo = r + 1;
             ++cut;

@@ -249,9 +249,13 @@ def check_schedule_kv(slices, nq, nk, hq, hkv, d, dtype=_lib.DTYPE_BF16, tile_k=
         for i in items:
             assert tuple(work[i, [0, 1, 4]]) == (k0, kl, g)
         # parts follow the tile list in order: a run of slices, or windows of one slice
+        step = max(1, 64 // (hq // hkv))   # tokens per row tile of the dK/dV pass
         for a_, b_ in zip(items, items[1:]):
             assert work[a_, 3] == work[b_, 2] or (work[a_, 2] == work[b_, 2] and work[a_, 3] == work[b_, 3]
                                                   and whi[a_] <= wlo[b_])
+            if work[a_, 2] == work[b_, 2] and work[a_, 3] == work[b_, 3]:
+                # a window that another window of the slice follows holds whole row tiles
+                assert (whi[a_] - wlo[a_]) % step == 0
         assert (owner[k0:k0 + kl, g] == -1).all(), "key owned twice"
         owner[k0:k0 + kl, g] = len(work) + r
         check_cols(k0, kl, items)
