@@ -289,17 +289,24 @@ def run_ring(steps, warmup, seed=0):
     return (t1 - t0) * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev])), 4.0 * d * hq * visible
 
 
+def kernel_sources_sha256() -> str:
+    """sha256 over the sources the forward kernel is compiled from"""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("ffa_fwd.hip", "ffa_common.h", "kernels.h"):
+        h.update(open(os.path.join(ROOT, "block_causal_attention_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def committed_traffic(wl_name: str):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary (profiles/traffic_<workload>.json), or None when the kernel
     source changed since those counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{wl_name}.json")
-    src = os.path.join(ROOT, "block_causal_attention_amd", "csrc", "ffa_fwd.hip")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("ffa_fwd_hip_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    if rec.get("kernel_sources_sha256") != kernel_sources_sha256():
         return None
     return float(rec["traffic_bytes_per_launch"])
 
