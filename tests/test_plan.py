@@ -636,3 +636,24 @@ def test_window_schedule_costs_large():
     assert work[:, 5].astype(np.int64).sum() == area * 8
     work, _, ext, red, nslots = ops.schedule_kv(sl, n, n, 128, 8, 48, _lib.DTYPE_BF16)
     assert work[:, 5].astype(np.int64).sum() == area * 8
+
+
+def test_product_path_has_no_fallback(tmp_path):
+    # without the built library every entry point raises; nothing computes
+    # the attention elsewhere (the package never imports the oracle)
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from block_causal_attention_amd import _lib, ops\n"
+            "_lib.LIB_PATH = %r\n"
+            "try:\n"
+            "    ops.build_slices([])\n"
+            "except ImportError as e:\n"
+            "    print('raised', e)\n") % (ROOT, str(tmp_path / "missing.so"))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0 and "raised" in out.stdout and "missing.so is missing" in out.stdout, out
+    pkg = os.path.join(ROOT, "block_causal_attention_amd")
+    for f in os.listdir(pkg):
+        if f.endswith(".py"):
+            src = open(os.path.join(pkg, f)).read()
+            assert not re.search(r"^\s*(import|from)\s+oracle", src, re.M), f
