@@ -255,6 +255,28 @@ def test_ffa_no_keys_and_scale():
     ffa_case(rand((30, 16, 24), 11, 3.0), rand((50, 1, 24), 12, 3.0), rand((50, 1, 24), 13), sl, "bf16", scale=0.05)
 
 
+def test_empty_query_and_key_sets():
+    # no query tokens at all (nothing to launch), and window / band slices
+    # whose rows see no key (an empty band, a window slice over no keys)
+    note("empty query set, empty bands")
+    q0 = torch.zeros(0, 16, 24, device=DEV, dtype=torch.bfloat16)
+    k = torch.randn(7, 1, 24, device=DEV).to(torch.bfloat16)
+    plan = ops.make_plan(np.zeros((0, 5), np.int32), 0, 7, 16, 1, 24, torch.bfloat16)
+    O, L = ops.ffa_fwd(q0, k, k, plan)
+    qh, kh = ops.qknorm_rope(q0, k[:0], torch.ones(24, device=DEV), torch.ones(24, device=DEV),
+                             torch.zeros(0, 3, dtype=torch.int32, device=DEV),
+                             torch.zeros(0, 3, dtype=torch.int32, device=DEV),
+                             torch.full((3,), 1e4, device=DEV), 1e-6)
+    torch.cuda.synchronize()
+    assert O.shape == (0, 16, 24) and L.shape == (0, 16) and qh.shape == (0, 16, 24) and kh.shape == (0, 1, 24)
+    # a band narrower than its query range shows no row a key (width
+    # 5 - 9 + 1 < 1), next to a band that does; rows of the empty band get
+    # O = 0 and LSE = -inf
+    sl = np.array([(0, 9, 0, 5, 3), (9, 20, 5, 20, 3)])
+    ffa_case(rand((20, 16, 24), 21), rand((20, 1, 24), 22), rand((20, 1, 24), 23), sl, "bf16")
+    ffa_case(rand((20, 16, 48), 24), rand((20, 1, 48), 25), rand((20, 1, 48), 26), sl, "fp32")
+
+
 def random_slices(rng, nq, nk, all_types=False):
     """Disjoint AttnSlices: query bands, each with a few disjoint key ranges,
     FULL or CAUSAL (bottom-right aligned; with all_types also INVCAUSAL and
