@@ -63,6 +63,9 @@ def window_pairs(wl, window) -> int:
     return tot
 
 
+LAST_LAUNCHES_MS = []  # per-launch attention times of the last run_gpu call
+
+
 def run_gpu(wl, steps, warmup, seed=0, window=None):
     """One step = plan build and upload, prologue, forward.  With ``window``
     the mask is causal sliding-window attention of that many tokens over
@@ -132,6 +135,7 @@ def run_gpu(wl, steps, warmup, seed=0, window=None):
     finally:
         gc.enable()
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    LAST_LAUNCHES_MS[:] = kernel_ms
     return (t1 - t0) * 1e3 / steps, float(np.mean(kernel_ms)), plan.num_work
 
 
@@ -374,6 +378,7 @@ def main():
     wl = W.make_workload(args.workload)
     flops = masked_flops(wl)
     ms_step, ms_kernel, nwork = run_gpu(wl, args.steps, args.warmup)
+    launches = sorted(LAST_LAUNCHES_MS)
     achieved = flops / (ms_kernel * 1e-3) / 1e12
     rec = {
         "metric": METRIC,
@@ -396,7 +401,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": committed_traffic(wl.name),
-                     "kernel": "ffa_fwd_bf16", "avg_launch_ms": round(ms_kernel, 5)},
+                     "kernel": "ffa_fwd_bf16", "avg_launch_ms": round(ms_kernel, 5),
+                     "median_launch_ms": round(launches[len(launches) // 2], 5),
+                     "min_launch_ms": round(launches[0], 5)},
     }
     if not args.no_secondary and wl.name == "magi4.5b":
         wl2 = W.make_workload("magi24b")
