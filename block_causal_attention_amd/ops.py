@@ -207,6 +207,17 @@ class Plan:
     def num_work(self) -> int:
         return int(self.host["work"].shape[0])
 
+    def settle(self) -> "Plan":
+        """Wait on the host for the plan's upload and drop its event, so that
+        the plan can be used inside HIP graph capture (a captured stream
+        cannot wait on an event recorded outside the capture).  A settled
+        plan's device lists stay fixed, so a captured graph may replay it any
+        number of times.  Returns the plan."""
+        if self.ready is not None:
+            self.ready.synchronize()
+            self.ready = None
+        return self
+
 
 def make_plan(slices: np.ndarray, nq: int, nk: int, hq: int, hkv: int, head_dim: int, dtype,
               device="cuda", tile_q: int = 0, backward: bool = False) -> Plan:
