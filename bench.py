@@ -237,6 +237,46 @@ def run_cross(wl, steps, warmup, seed=0):
     return (t1 - t0) * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
+def run_prologue(wl, steps=200, warmup=50, seed=0):
+    """The prologue alone (QK-Norm + 3D RoPE of Q and K, V moved group-major,
+    as in the step), timed with HIP events on its stream: (mean ms, median
+    ms, algorithmic HBM bytes = every Q/K/V element read and written once
+    plus the positions)."""
+    import torch
+    import workloads as W
+    from block_causal_attention_amd import ops
+
+    dev = "cuda"
+    inp = W.make_inputs(wl, seed)
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    gq, gk, pq, pk = (t.to(dev) for t in (inp.gain_q, inp.gain_k, inp.pos_q, inp.pos_k))
+    base = torch.tensor(wl.rope_base, dtype=torch.float32, device=dev)
+    qh = torch.empty_like(q)
+    kh = ops.kv_group_major(wl.nk, wl.hkv, wl.head_dim, q.dtype, dev)
+    vh = ops.kv_group_major(wl.nk, wl.hkv, wl.head_dim, q.dtype, dev)
+    knm = torch.empty(wl.hkv, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def f():
+        ops.qknorm_rope(q, k, gq, gk, pq, pk, base, wl.eps, q_out=qh, k_out=kh,
+                        k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm, v=v, v_out=vh)
+
+    for _ in range(warmup):
+        f()
+    ev = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        f()
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    el = q.element_size()
+    nbytes = 2 * el * (q.numel() + 2 * k.numel()) + 2 * 4 * 3 * (wl.nq + wl.nk)
+    return float(np.mean(ms)), ms[len(ms) // 2], nbytes
+
+
 def run_first_chunk(steps=300, warmup=30, d=24):
     """A streaming generation's first chunk (2 latent frames x 12 x 16 = 384
     tokens, 128/8 heads): prologue + attention, launch-bound.  Wall time per
@@ -506,6 +546,14 @@ def main():
                          "kernel_tflops": round(fw / (ms_k * 1e-3) / 1e12, 2),
                          "pct_of_bf16_peak": round(100.0 * fw / (ms_k * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
         rec["sliding_window"] = win
+        pro = {}
+        for name in ("magi4.5b", "magi24b"):
+            w = W.make_workload(name)
+            mean_ms, med_ms, nbytes = run_prologue(w)
+            pro[name] = {"avg_launch_ms": round(mean_ms, 5), "median_launch_ms": round(med_ms, 5),
+                         "algorithmic_bytes": nbytes, "GB/s": round(nbytes / (mean_ms * 1e-3) / 1e9, 1),
+                         "frac_of_hbm_peak": round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        rec["prologue"] = pro
         rec["first_chunk"] = run_first_chunk()
         ms_s, ms_k, fr = run_ring(5, 2)
         rec["streaming_ring"] = {"shape": "4 in-flight x 3600 queries over a 24-slot ring (86400 keys), 128/8, d=48",
