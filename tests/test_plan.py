@@ -356,7 +356,7 @@ def test_schedule_lower_bound_overlap_detection():
 
 
 @pytest.mark.parametrize("trial", range(12))
-def test_schedule_overlap_verdict_matches_brute_force(trial):
+def test_schedule_overlap_decision_matches_brute_force(trial):
     # random slices of every type in a small space, overlapping or not: the
     # scheduler reports an overlap exactly when the dense masks share a pair
     rng = np.random.Generator(np.random.PCG64(1300 + trial))
