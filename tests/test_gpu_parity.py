@@ -640,6 +640,23 @@ def test_packing_equals_separate_videos_gpu():
         assert torch.equal(Os, O[a:b]) and torch.equal(Ls, L[a:b])
 
 
+def test_window_packing_equals_separate_sequences_gpu():
+    # causal sliding windows over packed sequences: each sequence's rows are
+    # bit for bit those of the sequence run alone
+    note("window packing == separate sequences")
+    spec = [(300, 64, 0, 0), (130, 200, 300, 300), (250, 1, 430, 430)]
+    n = 680
+    q, k, v = (torch.from_numpy(rand((n, h, 48), 80 + i)).to(torch.bfloat16).to(DEV)
+               for i, h in enumerate((16, 2, 2)))
+    O, L = ops.ffa_fwd(q, k, v, ops.make_plan(ops.build_window_slices(spec), n, n, 16, 2, 48, torch.bfloat16))
+    torch.cuda.synchronize()
+    for ln, w, a, _ in spec:
+        Os, Ls = ops.ffa_fwd(q[a:a + ln].contiguous(), k[a:a + ln].contiguous(), v[a:a + ln].contiguous(),
+                             ops.make_plan(ops.build_window_slices([(ln, w, 0, 0)]), ln, ln, 16, 2, 48, torch.bfloat16))
+        torch.cuda.synchronize()
+        assert torch.equal(Os, O[a:a + ln]) and torch.equal(Ls, L[a:a + ln])
+
+
 # --------------------------------------------------------------------------- cross-attention
 
 @pytest.mark.parametrize("group_major", [False, True])

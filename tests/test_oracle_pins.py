@@ -534,3 +534,14 @@ def test_window_mask_equals_attention_over_the_window_alone():
         s = 0.5 * k[lo:i + 1, 0] @ q[i, 0]
         p = np.exp(s - s.max())
         np.testing.assert_allclose(O[i, 0], p @ v[lo:i + 1, 0] / p.sum(), rtol=1e-12, atol=1e-12)
+
+
+def test_window_mask_packing_is_block_diagonal():
+    # packed sequences never see each other: the packed mask is the
+    # block-diagonal assembly of the masks of the sequences alone
+    spec = [(7, 3, 0, 0), (5, 9, 7, 7), (6, 1, 12, 12)]
+    m = window_mask(spec, 18, 18)
+    want = np.zeros((18, 18), bool)
+    for ln, w, a, _ in spec:
+        want[a:a + ln, a:a + ln] = window_mask([(ln, w, 0, 0)], ln, ln)
+    np.testing.assert_array_equal(m, want)
