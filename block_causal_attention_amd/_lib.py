@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "MAGI_OK", -1: "MAGI_ERR_INVALID_ARG", -2: "MAGI_ERR_UNSUPPOR
 
 EXPORTS = ("magi_version", "magi_last_error", "magi_slices_build", "magi_default_tile_q",
            "magi_schedule", "magi_qknorm_rope", "magi_ffa_fwd", "magi_ffa_fwd_qknorm", "magi_default_tile_k",
-           "magi_schedule_kv", "magi_ffa_bwd", "magi_slices_cross", "magi_slices_ring", "magi_slices_window")
+           "magi_schedule_kv", "magi_ffa_bwd", "magi_ffa_bwd_noalloc", "magi_slices_cross", "magi_slices_ring",
+           "magi_slices_window")
 
 
 class AttnSlice(C.Structure):
@@ -106,8 +107,12 @@ def lib() -> C.CDLL:
         L.magi_ffa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32,
                                    i64, i64, i64, i64, C.c_float, vp, i32, vp, i32, vp, i32, vp, i32, vp, i32,
                                    vp, vp, i32, i32, vp, i64, vp]
+        # magi_ffa_bwd without delta (after dv) and without partial, partial_floats
+        bw = L.magi_ffa_bwd.argtypes
+        L.magi_ffa_bwd_noalloc.argtypes = bw[:9] + bw[10:-3] + bw[-1:]
         for name in ("magi_slices_build", "magi_default_tile_q", "magi_schedule", "magi_qknorm_rope",
                      "magi_ffa_fwd", "magi_ffa_fwd_qknorm", "magi_default_tile_k", "magi_schedule_kv", "magi_ffa_bwd",
+                     "magi_ffa_bwd_noalloc",
                      "magi_slices_cross", "magi_slices_ring", "magi_slices_window"):
             getattr(L, name).restype = i32
         _lib = L

@@ -246,17 +246,18 @@ extern "C" int32_t magi_ffa_fwd_qknorm(const void* q_raw, const void* k, const v
   return launch(a, stream);
 }
 
-extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                                const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t nq,
-                                int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
-                                int64_t q_tok_stride, int64_t kv_tok_stride, int64_t kv_head_stride,
-                                int64_t o_tok_stride, float softmax_scale, const magi_attn_slice* slices,
-                                int32_t num_slices, const magi_work_item* qwork, int32_t num_qwork,
-                                const int32_t* q_tile_slices, int32_t num_q_tile_slices,
-                                const magi_work_item* kwork, int32_t num_kwork, const int32_t* k_tile_slices,
-                                int32_t num_k_tile_slices, const int32_t* kitem_ext,
-                                const magi_kv_reduce* reduce, int32_t num_reduce, int32_t num_slots,
-                                float* partial, int64_t partial_floats, void* stream) {
+namespace {
+
+// Every check of the backward's arguments except its workspace (delta and
+// the partial sums of split key tiles), then the kernel arguments.
+int32_t bwd_args(BwdArgs& a, const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int64_t nq, int64_t nk, int32_t hq, int32_t hkv,
+                 int32_t head_dim, int32_t dtype, int64_t q_tok_stride, int64_t kv_tok_stride,
+                 int64_t kv_head_stride, int64_t o_tok_stride, float softmax_scale, const magi_attn_slice* slices,
+                 int32_t num_slices, const magi_work_item* qwork, int32_t num_qwork, const int32_t* q_tile_slices,
+                 int32_t num_q_tile_slices, const magi_work_item* kwork, int32_t num_kwork,
+                 const int32_t* k_tile_slices, int32_t num_k_tile_slices, const int32_t* kitem_ext,
+                 const magi_kv_reduce* reduce, int32_t num_reduce, int32_t num_slots) {
   int32_t st;
   if ((st = check_common(head_dim, dtype)) != MAGI_OK) return st;
   if (hq < 1 || hkv < 1) return fail(MAGI_ERR_INVALID_ARG, "hq and hkv must be >= 1");
@@ -272,9 +273,8 @@ extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, con
     if ((st = check_layout(t.name, t.p, nk, hkv, kv_tok_stride, kv_head_stride, head_dim, dtype)) != MAGI_OK) return st;
   if (kv_tok_stride >= (int64_t)1 << 23)
     return fail(MAGI_ERR_UNSUPPORTED, "kv row stride %lld >= 2^23 elements", (long long)kv_tok_stride);
-  if (nq > 0 && (lse == nullptr || delta == nullptr)) return fail(MAGI_ERR_INVALID_ARG, "lse and delta are required");
-  if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(delta) & 3u))
-    return fail(MAGI_ERR_INVALID_ARG, "lse / delta not 4-byte aligned");
+  if (nq > 0 && lse == nullptr) return fail(MAGI_ERR_INVALID_ARG, "lse is required");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(MAGI_ERR_INVALID_ARG, "lse not 4-byte aligned");
   if (!finite_bits(softmax_scale))
     return fail(MAGI_ERR_INVALID_ARG, "softmax_scale must be finite");
   if (num_slices < 0 || num_qwork < 0 || num_q_tile_slices < 0 || num_kwork < 0 || num_k_tile_slices < 0)
@@ -285,18 +285,11 @@ extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, con
     return fail(MAGI_ERR_INVALID_ARG, "a non-empty list pointer is NULL");
   if (num_qwork > 0 && nq == 0) return fail(MAGI_ERR_INVALID_ARG, "query work items for an empty query tensor");
   if (num_reduce < 0 || num_slots < 0) return fail(MAGI_ERR_INVALID_ARG, "negative reduce or slot count");
-  if (num_reduce > 0 || num_slots > 0) {
-    if (reduce == nullptr || kitem_ext == nullptr || partial == nullptr)
-      return fail(MAGI_ERR_INVALID_ARG, "a split schedule needs kitem_ext, reduce and partial");
-    // slot layout fixed by the dK/dV kernel: 2 x 128 keys x head_dim fp32
-    if (partial_floats < (int64_t)num_slots * 2 * 128 * head_dim)
-      return fail(MAGI_ERR_INVALID_ARG, "partial holds %lld floats, %d slots need %lld", (long long)partial_floats,
-                  num_slots, (long long)num_slots * 2 * 128 * head_dim);
-    if (!aligned16(partial)) return fail(MAGI_ERR_INVALID_ARG, "partial is not 16-byte aligned");
-  }
+  if ((num_reduce > 0 || num_slots > 0) && (reduce == nullptr || kitem_ext == nullptr))
+    return fail(MAGI_ERR_INVALID_ARG, "a split schedule needs kitem_ext and reduce");
   if (num_kwork > 0 && nk == 0) return fail(MAGI_ERR_INVALID_ARG, "key work items for an empty key tensor");
 
-  BwdArgs a{};
+  a = BwdArgs{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -306,7 +299,6 @@ extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, con
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.delta = delta;
   a.nq = nq;
   a.nk = nk;
   a.hq = hq;
@@ -332,8 +324,81 @@ extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, con
   a.reduce = reduce;
   a.num_reduce = num_reduce;
   a.num_slots = num_slots;
-  a.partial = partial;
+  return MAGI_OK;
+}
+
+// fp32 values of the partial-sum workspace a schedule with num_slots slots
+// needs: 2 (dK, dV) x 128 keys x head_dim per slot, the dK/dV kernel's layout
+int64_t partial_need(int32_t num_slots, int32_t head_dim) { return (int64_t)num_slots * 2 * 128 * head_dim; }
+
+int32_t bwd_launch(const BwdArgs& a, void* stream) {
   const hipError_t e = launch_ffa_bwd(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MAGI_ERR_HIP, "ffa_bwd launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t nq,
+                                int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
+                                int64_t q_tok_stride, int64_t kv_tok_stride, int64_t kv_head_stride,
+                                int64_t o_tok_stride, float softmax_scale, const magi_attn_slice* slices,
+                                int32_t num_slices, const magi_work_item* qwork, int32_t num_qwork,
+                                const int32_t* q_tile_slices, int32_t num_q_tile_slices,
+                                const magi_work_item* kwork, int32_t num_kwork, const int32_t* k_tile_slices,
+                                int32_t num_k_tile_slices, const int32_t* kitem_ext,
+                                const magi_kv_reduce* reduce, int32_t num_reduce, int32_t num_slots,
+                                float* partial, int64_t partial_floats, void* stream) {
+  BwdArgs a;
+  int32_t st = bwd_args(a, q, k, v, out, dout, lse, dq, dk, dv, nq, nk, hq, hkv, head_dim, dtype, q_tok_stride,
+                        kv_tok_stride, kv_head_stride, o_tok_stride, softmax_scale, slices, num_slices, qwork,
+                        num_qwork, q_tile_slices, num_q_tile_slices, kwork, num_kwork, k_tile_slices,
+                        num_k_tile_slices, kitem_ext, reduce, num_reduce, num_slots);
+  if (st != MAGI_OK) return st;
+  if (nq > 0 && delta == nullptr) return fail(MAGI_ERR_INVALID_ARG, "delta is required");
+  if (reinterpret_cast<uintptr_t>(delta) & 3u) return fail(MAGI_ERR_INVALID_ARG, "delta not 4-byte aligned");
+  if (num_reduce > 0 || num_slots > 0) {
+    if (partial == nullptr) return fail(MAGI_ERR_INVALID_ARG, "a split schedule needs partial");
+    if (partial_floats < partial_need(num_slots, head_dim))
+      return fail(MAGI_ERR_INVALID_ARG, "partial holds %lld floats, %d slots need %lld", (long long)partial_floats,
+                  num_slots, (long long)partial_need(num_slots, head_dim));
+    if (!aligned16(partial)) return fail(MAGI_ERR_INVALID_ARG, "partial is not 16-byte aligned");
+  }
+  a.delta = delta;
+  a.partial = partial;
+  return bwd_launch(a, stream);
+}
+
+extern "C" int32_t magi_ffa_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
+                                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                        int64_t nq, int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim,
+                                        int32_t dtype, int64_t q_tok_stride, int64_t kv_tok_stride,
+                                        int64_t kv_head_stride, int64_t o_tok_stride, float softmax_scale,
+                                        const magi_attn_slice* slices, int32_t num_slices,
+                                        const magi_work_item* qwork, int32_t num_qwork,
+                                        const int32_t* q_tile_slices, int32_t num_q_tile_slices,
+                                        const magi_work_item* kwork, int32_t num_kwork,
+                                        const int32_t* k_tile_slices, int32_t num_k_tile_slices,
+                                        const int32_t* kitem_ext, const magi_kv_reduce* reduce,
+                                        int32_t num_reduce, int32_t num_slots, void* stream) {
+  BwdArgs a;
+  int32_t st = bwd_args(a, q, k, v, out, dout, lse, dq, dk, dv, nq, nk, hq, hkv, head_dim, dtype, q_tok_stride,
+                        kv_tok_stride, kv_head_stride, o_tok_stride, softmax_scale, slices, num_slices, qwork,
+                        num_qwork, q_tile_slices, num_q_tile_slices, kwork, num_kwork, k_tile_slices,
+                        num_k_tile_slices, kitem_ext, reduce, num_reduce, num_slots);
+  if (st != MAGI_OK) return st;
+  // delta first, then the partial sums from a 256-byte boundary
+  const int64_t delta_floats = (nq * hq + 63) / 64 * 64;
+  const int64_t need = delta_floats + partial_need(num_slots, head_dim);
+  if (need > kScratchFloats)
+    return fail(MAGI_ERR_UNSUPPORTED,
+                "workspace of %lld floats (delta %lld + %d partial slots) exceeds the static %lld-float scratch",
+                (long long)need, (long long)(nq * hq), num_slots, (long long)kScratchFloats);
+  float* base = nullptr;
+  const hipError_t e = scratch_for_stream(stream, &base);
+  if (e != hipSuccess) return fail(MAGI_ERR_HIP, "scratch lookup: %s", hipGetErrorString(e));
+  a.delta = base;
+  a.partial = base + delta_floats;
+  return bwd_launch(a, stream);
 }

@@ -100,4 +100,12 @@ struct BwdArgs {
 
 hipError_t launch_ffa_bwd(const BwdArgs& a, hipStream_t stream);
 
+// The static device workspace of the entry points that allocate nothing:
+// kScratchFloats fp32 values (64 MiB) per GPU, held until the process ends.
+constexpr int64_t kScratchFloats = (int64_t)16 << 20;
+
+// Device address of the workspace on the device of `stream` (a hipStream_t;
+// NULL = the current device), looked up once per device.
+hipError_t scratch_for_stream(void* stream, float** out);
+
 }  // namespace magi

@@ -456,13 +456,7 @@ def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
     return out, lse
 
 
-def ffa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
-            lse: torch.Tensor, plan: Plan, softmax_scale: Optional[float] = None,
-            dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-            dv: Optional[torch.Tensor] = None):
-    """magi_ffa_bwd over a backward ``plan`` (make_plan(..., backward=True));
-    returns (dq, dk, dv).  q, k, v, out, lse and softmax_scale are the
-    forward's; dout has the layout of out."""
+def _bwd_common(q, k, v, out, dout, lse, plan, dq, dk, dv):
     d = q.shape[-1]
     hq, hkv = q.shape[1], k.shape[1]
     for name, t, heads in (("q", q, hq), ("k", k, hkv), ("v", v, hkv), ("out", out, hq), ("dout", dout, hq)):
@@ -476,26 +470,58 @@ def ffa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor
         raise ValueError("plan was made for a different shape or dtype")
     if lse.dtype != torch.float32 or lse.shape != (q.shape[0], hq) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous float32 [nq, hq]")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype:
             raise ValueError(f"{name} must match {name[1:]} in shape, strides and dtype")
+
+
+def _bwd_list_args(plan):
+    H = plan.host
+    return (_ptr(plan.slices), int(H["slices"].shape[0]), _ptr(plan.work), plan.num_work,
+            _ptr(plan.tile_slices), int(H["tile_slices"].shape[0]),
+            _ptr(plan.kwork), int(H["kwork"].shape[0]), _ptr(plan.k_tile_slices), int(H["k_tile_slices"].shape[0]),
+            _ptr(plan.kitem_ext), _ptr(plan.kreduce), int(H["kreduce"].shape[0]), plan.num_slots)
+
+
+def ffa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+            lse: torch.Tensor, plan: Plan, softmax_scale: Optional[float] = None,
+            dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+            dv: Optional[torch.Tensor] = None):
+    """magi_ffa_bwd over a backward ``plan`` (make_plan(..., backward=True));
+    returns (dq, dk, dv).  q, k, v, out, lse and softmax_scale are the
+    forward's; dout has the layout of out."""
+    d = q.shape[-1]
+    hq = q.shape[1]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _bwd_common(q, k, v, out, dout, lse, plan, dq, dk, dv)
     delta = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
     # partial sums of split key tiles: 2 x 128 keys x d fp32 per slot
     nfl = plan.num_slots * 2 * 128 * d
     partial = torch.empty(max(nfl, 4), dtype=torch.float32, device=q.device)
     if plan.ready is not None:
         torch.cuda.current_stream(q.device).wait_event(plan.ready)
-    H = plan.host
     check(lib().magi_ffa_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
-        q.shape[0], k.shape[0], hq, hkv, d, dtype_code(q.dtype), q.stride(0), k.stride(0), k.stride(1), out.stride(0),
-        0.0 if softmax_scale is None else float(softmax_scale),
-        _ptr(plan.slices), int(H["slices"].shape[0]), _ptr(plan.work), plan.num_work,
-        _ptr(plan.tile_slices), int(H["tile_slices"].shape[0]),
-        _ptr(plan.kwork), int(H["kwork"].shape[0]), _ptr(plan.k_tile_slices), int(H["k_tile_slices"].shape[0]),
-        _ptr(plan.kitem_ext), _ptr(plan.kreduce), int(H["kreduce"].shape[0]), plan.num_slots, _ptr(partial), nfl,
-        _stream(q)))
+        q.shape[0], k.shape[0], hq, k.shape[1], d, dtype_code(q.dtype), q.stride(0), k.stride(0), k.stride(1),
+        out.stride(0), 0.0 if softmax_scale is None else float(softmax_scale),
+        *_bwd_list_args(plan), _ptr(partial), nfl, _stream(q)))
+    return dq, dk, dv
+
+
+def ffa_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+                    lse: torch.Tensor, plan: Plan, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor,
+                    softmax_scale: Optional[float] = None):
+    """magi_ffa_bwd_noalloc: ffa_bwd with its workspace in the library's
+    static device scratch; the gradients go into the caller's dq, dk, dv and
+    nothing is allocated (the plan must already be on the device)."""
+    _bwd_common(q, k, v, out, dout, lse, plan, dq, dk, dv)
+    if plan.ready is not None:
+        torch.cuda.current_stream(q.device).wait_event(plan.ready)
+    check(lib().magi_ffa_bwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+        q.shape[0], k.shape[0], q.shape[1], k.shape[1], q.shape[-1], dtype_code(q.dtype), q.stride(0), k.stride(0),
+        k.stride(1), out.stride(0), 0.0 if softmax_scale is None else float(softmax_scale),
+        *_bwd_list_args(plan), _stream(q)))
     return dq, dk, dv

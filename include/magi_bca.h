@@ -476,6 +476,39 @@ int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, const void* ou
                      int32_t num_slots, float* partial, int64_t partial_floats,
                      void* stream);
 
+/*
+ * magi_ffa_bwd_noalloc -- magi_ffa_bwd with its workspace taken from the
+ * library's static device scratch instead of caller buffers.  [device, async]
+ *
+ * For callers that cannot allocate device memory or be handed a workspace:
+ * code under HIP graph capture, tight serving or training loops, harnesses
+ * that forbid hipMalloc.  The call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine); the caller still passes every
+ * input and output.
+ *
+ * Arguments, results and errors as magi_ffa_bwd without delta, partial and
+ * partial_floats.  The workspace -- delta (nq x hq fp32, rounded up to 64)
+ * followed by the partial sums of split key tiles (num_slots x 2 x 128 x
+ * head_dim fp32) -- lives in a file-scope device array of 16 Mi fp32 values
+ * (64 MiB) that every GPU the library runs on holds until the process ends;
+ * a call needing more returns MAGI_ERR_UNSUPPORTED before any HIP call.
+ * Nothing in it needs to start at zero (every value is written before it is
+ * read within the call).  Every call on one GPU uses that GPU's single copy:
+ * calls that overlap on one GPU (other streams, other host threads) race and
+ * give wrong results; calls serialised on one stream are safe.
+ */
+int32_t magi_ffa_bwd_noalloc(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                             const float* lse, void* dq, void* dk, void* dv,
+                             int64_t nq, int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
+                             int64_t q_tok_stride, int64_t kv_tok_stride, int64_t kv_head_stride,
+                             int64_t o_tok_stride, float softmax_scale, const magi_attn_slice* slices,
+                             int32_t num_slices, const magi_work_item* qwork, int32_t num_qwork,
+                             const int32_t* q_tile_slices, int32_t num_q_tile_slices,
+                             const magi_work_item* kwork, int32_t num_kwork,
+                             const int32_t* k_tile_slices, int32_t num_k_tile_slices,
+                             const int32_t* kitem_ext, const magi_kv_reduce* reduce, int32_t num_reduce,
+                             int32_t num_slots, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ def header_functions():
 def test_library_exports_every_header_symbol():
     L = _lib.lib()
     names = header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -531,6 +531,32 @@ def test_backward_entry_validates_split_workspace():
     assert bwd(delta=None) == _lib.MAGI_ERR_INVALID_ARG
     assert bwd(kvhs=20) == _lib.MAGI_ERR_INVALID_ARG                    # K/V layout overlaps
     assert b"K/V" in L.magi_last_error() or b"overlap" in L.magi_last_error()
+
+
+def test_noalloc_backward_entry_validates_and_bounds_its_scratch():
+    # the same checks as magi_ffa_bwd, then the static-scratch bound; every
+    # call below fails on the host, before any HIP call
+    L = _lib.lib()
+    p = C.c_void_p(4096)  # never dereferenced
+
+    def bwd(**kw):
+        a = dict(nq=16, nk=16, hq=16, hkv=1, d=24, qs=384, kvs=24, kvhs=24, os_=384, slot=p, red=p, nred=1,
+                 nslots=2, lse=p)
+        a.update(kw)
+        return L.magi_ffa_bwd_noalloc(p, p, p, p, p, a["lse"], p, p, p, a["nq"], a["nk"], a["hq"], a["hkv"],
+                                      a["d"], 0, a["qs"], a["kvs"], a["kvhs"], a["os_"], 0.0, p, 1, p, 1, p, 1, p,
+                                      1, p, 1, a["slot"], a["red"], a["nred"], a["nslots"], None)
+    assert bwd(slot=None) == _lib.MAGI_ERR_INVALID_ARG
+    assert bwd(lse=None) == _lib.MAGI_ERR_INVALID_ARG
+    assert bwd(kvhs=20) == _lib.MAGI_ERR_INVALID_ARG
+    assert bwd(d=32) == _lib.MAGI_ERR_UNSUPPORTED
+    # 64 MiB = 16 Mi floats: 2731 slots x 2 x 128 x 24 floats leave no room for delta
+    assert bwd(nslots=2731) == _lib.MAGI_ERR_UNSUPPORTED
+    assert b"scratch" in L.magi_last_error()
+    # delta alone: nq x hq floats past the bound (rows of 48 heads x 24)
+    big = (16 << 20) // 48 + 1
+    assert bwd(nq=big, hq=48, qs=48 * 24, os_=48 * 24, nk=16, nslots=0, nred=0, slot=None, red=None) == \
+        _lib.MAGI_ERR_UNSUPPORTED
 
 
 def test_cross_slices():
