@@ -49,7 +49,71 @@ def masked_flops(wl) -> float:
     return 4.0 * wl.head_dim * wl.hq * visible_pairs(wl)
 
 
+CLOCK_GHZ = 2.4   # the clock the published peaks assume (256 CUs, 1024 SIMDs)
+
+
+def ceilings(d: int) -> dict:
+    """The two ceilings of the bf16 forward at head_dim d, in masked TFLOP/s.
+
+    Per 32-key x 32-row score block of one wave (4 d 1024 useful FLOPs):
+    * VALU: 16 v_exp_f32 at half rate (8 issue cycles each; 31 of 64 lanes
+      per clock per CU measured) + 8 v_cvt_pk_bf16_f32 (4 cycles each) =
+      160 issue cycles of one SIMD, the softmax work that cannot leave it;
+    * MFMA: the padded products, ceil(d/16) Q.K steps and 2 x ceil((d+1)/32)
+      P.V steps of v_mfma_f32_32x32x16_bf16 (32768 FLOPs each), of which
+      d / 8 carry the counted work (d = 24: 3 of 4; d = 48: 6 of 7).
+    """
+    valu = 1024 * CLOCK_GHZ * 1e9 * 4.0 * d * 1024 / 160 / 1e12
+    issued = -(-d // 16) + 2 * -(-(d + 1) // 32)
+    mfma = PEAK_BF16_TFLOPS * (d / 8.0) / issued
+    return {"valu_tflops": round(valu, 1), "mfma_padded_tflops": round(mfma, 1)}
+
+
+def with_ceilings(rec: dict, tflops: float, d: int) -> dict:
+    """add the fractions of the VALU and padded-MFMA ceilings beside the
+    fraction of the bf16 peak"""
+    c = ceilings(d)
+    rec["frac_of_valu_ceiling"] = round(tflops / c["valu_tflops"], 4)
+    rec["frac_of_mfma_padded_ceiling"] = round(tflops / c["mfma_padded_tflops"], 4)
+    return rec
+
+
 MIN_WARM_S = 0.5
+SYNC_EVERY = 32  # warm-up steps between synchronisations (bounds the host's run-ahead)
+
+
+class steady_timing:
+    """No garbage-collection pass inside the warm-up or the timed region (as
+    timeit does; a full pass over large heaps stalls the host for ms)."""
+
+    def __enter__(self):
+        gc.collect()
+        gc.disable()
+
+    def __exit__(self, *exc):
+        gc.enable()
+
+
+def warm_up(step, warmup):
+    """At least ``warmup`` untimed steps and MIN_WARM_S seconds of them,
+    synchronising every SYNC_EVERY steps, then a synchronisation.
+
+    The shader clock of an idle GPU takes a few hundred ms of load to settle.
+    The periodic synchronisation keeps the host at most SYNC_EVERY steps
+    ahead: after an unbounded burst of thousands of queued launches the HIP
+    runtime spends many later calls retiring it, the host then falls behind
+    the GPU at the start of the timed region, and the kernels that follow
+    idle gaps run up to 20 % slower (measured on the 4.5B-shaped layer:
+    0.330 ms per attention launch with this warm-up against 0.355-0.40 ms
+    after an unbounded one)."""
+    import torch
+    t_w, i = time.perf_counter(), 0
+    while i < warmup or time.perf_counter() - t_w < MIN_WARM_S:
+        step(False)
+        i += 1
+        if i % SYNC_EVERY == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
 
 def window_pairs(wl, window) -> int:
@@ -93,14 +157,22 @@ def run_gpu(wl, steps, warmup, seed=0, window=None):
     spec = None if window is None else [(s.num_q_chunks * s.chunk_len, window, s.q_offset, s.k_offset)
                                          for s in wl.seqs]
 
+    # A streaming step's cached keys and values were processed by earlier
+    # steps: they are written once here, and a step's prologue covers the
+    # in-flight rows only.
+    kf = wl.k_fresh_start
+    if kf:
+        ops.qknorm_rope(q[:1], k[:kf], gq, gk, pq[:1], pk[:kf], base, wl.eps, q_out=qh[:1], k_out=kh[:kf],
+                        k_scale=wl.softmax_scale * ops.LOG2E, v=v[:kf], v_out=vh[:kf])
+
     def step(record):
         if spec is None:
             plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, tdt, dev)
         else:
             plan = ops.make_plan(ops.build_window_slices(spec), wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, tdt, dev)
         # the softmax scale (times log2 e) is folded into K by the prologue
-        ops.qknorm_rope(q, k, gq, gk, pq, pk, base, wl.eps, q_out=qh, k_out=kh,
-                        k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm, v=v, v_out=vh)
+        ops.qknorm_rope(q, k[kf:], gq, gk, pq, pk[kf:], base, wl.eps, q_out=qh, k_out=kh[kf:],
+                        k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm, v=v[kf:], v_out=vh[kf:])
         if record:
             # the wait for the plan upload (a side stream) goes before the
             # start event, so that the events bracket the attention kernel
@@ -114,30 +186,13 @@ def run_gpu(wl, steps, warmup, seed=0, window=None):
             ev.append((a, b))
         return plan
 
-    # W untimed steps, and at least MIN_WARM_S of them: the shader clock of
-    # an idle GPU takes a few hundred ms of load to settle
-    t_w, i = time.perf_counter(), 0
-    while i < warmup or time.perf_counter() - t_w < MIN_WARM_S:
-        step(False)
-        i += 1
-    torch.cuda.synchronize()
-    # the first call after a long burst of launches pays the runtime's
-    # deferred clean-up of that burst (a few ms of host time); one more
-    # untimed step takes it, so the timed region starts in steady state
-    step(False)
-    torch.cuda.synchronize()
-    # as timeit does: no garbage-collection pass inside the timed region (a
-    # full pass over the warm-up's garbage can stall the host for ms)
-    gc.collect()
-    gc.disable()
-    try:
+    with steady_timing():
+        warm_up(step, warmup)
         t0 = time.perf_counter()
         for _ in range(steps):
             plan = step(True)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-    finally:
-        gc.enable()
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
     LAST_LAUNCHES_MS[:] = kernel_ms
     return (t1 - t0) * 1e3 / steps, float(np.mean(kernel_ms)), plan.num_work
@@ -167,8 +222,8 @@ def run_backward(wl, steps, warmup, seed=0):
     dq, dk, dv = torch.empty_like(qh), torch.empty_like(kh), torch.empty_like(vh)
     stream = torch.cuda.current_stream()
     ev = []
-    for i in range(warmup + steps):
-        rec = i >= warmup
+
+    def step(rec):
         if rec:
             stream.wait_event(plan.ready)  # the upload wait stays outside the kernels' events
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -177,7 +232,12 @@ def run_backward(wl, steps, warmup, seed=0):
         if rec:
             b.record(stream)
             ev.append((a, b))
-    torch.cuda.synchronize()
+
+    with steady_timing():
+        warm_up(step, warmup)
+        for _ in range(steps):
+            step(True)
+        torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
@@ -226,14 +286,13 @@ def run_cross(wl, steps, warmup, seed=0):
             b.record(stream)
             ev.append((a, b))
 
-    for _ in range(warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step(True)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with steady_timing():
+        warm_up(step, warmup)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step(True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     return (t1 - t0) * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
@@ -261,16 +320,16 @@ def run_prologue(wl, steps=200, warmup=50, seed=0):
         ops.qknorm_rope(q, k, gq, gk, pq, pk, base, wl.eps, q_out=qh, k_out=kh,
                         k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm, v=v, v_out=vh)
 
-    for _ in range(warmup):
-        f()
     ev = []
-    for _ in range(steps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        f()
-        b.record(stream)
-        ev.append((a, b))
-    torch.cuda.synchronize()
+    with steady_timing():
+        warm_up(lambda rec: f(), warmup)
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
     el = q.element_size()
     nbytes = 2 * el * (q.numel() + 2 * k.numel()) + 2 * 4 * 3 * (wl.nq + wl.nk)
@@ -353,7 +412,7 @@ def run_ring(steps, warmup, seed=0):
         ops.kv_group_major(S * C, hkv, d, torch.bfloat16, dev)
     ring_k.copy_(mk(S * C, hkv, d))
     ring_v.copy_(mk(S * C, hkv, d))
-    q, knew = mk(n * C, hq, d), mk(n * C, hkv, d)
+    q, knew, vnew = mk(n * C, hq, d), mk(n * C, hkv, d), mk(n * C, hkv, d)
     gq = (0.8 + 0.4 * torch.rand(d, generator=g)).to(dev)
     gk = (0.8 + 0.4 * torch.rand(d, generator=g)).to(dev)
     pos = torch.randint(0, 24, (n * C, 3), generator=g, dtype=torch.int32).to(dev)
@@ -373,11 +432,12 @@ def run_ring(steps, warmup, seed=0):
         visible = int(((sl[:, 1] - sl[:, 0]).astype(np.int64) * (sl[:, 3] - sl[:, 2])).sum())
         plan = ops.make_plan(sl, n * C, S * C, hq, hkv, d, q.dtype, dev)
         done = 0
-        for s0, m in runs:   # in-flight keys into their slots (the ring wraps at most once)
+        for s0, m in runs:   # in-flight keys and values into their slots (the ring wraps at most once)
             ops.qknorm_rope(q[:1] if done else q, knew[done * C:(done + m) * C], gq, gk,
                             pos[:1] if done else pos, pos[done * C:(done + m) * C], base, 1e-6,
                             q_out=qh[:1] if done else qh, k_out=ring_k[s0 * C:(s0 + m) * C],
-                            k_scale=scale * ops.LOG2E)
+                            k_scale=scale * ops.LOG2E, v=vnew[done * C:(done + m) * C],
+                            v_out=ring_v[s0 * C:(s0 + m) * C])
             done += m
         if record:
             stream.wait_event(plan.ready)  # the upload wait stays outside the kernel's events
@@ -388,14 +448,13 @@ def run_ring(steps, warmup, seed=0):
             b.record(stream)
             ev.append((a, b))
 
-    for _ in range(warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step(True)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with steady_timing():
+        warm_up(step, warmup)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step(True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     return (t1 - t0) * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev])), 4.0 * d * hq * visible
 
 
@@ -425,7 +484,7 @@ def cpu_baseline(wl, target_s=30.0, seed=0):
     """Time the float64 oracle on a seeded row sample (all heads) of the workload."""
     import oracle
     import workloads as W
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     inp = W.make_inputs(wl, seed)
     f64 = lambda t: t.float().numpy().astype(np.float64)
@@ -439,17 +498,83 @@ def cpu_baseline(wl, target_s=30.0, seed=0):
                        wl.rope_base, wl.eps, mask, wl.softmax_scale)
         return time.perf_counter() - t, int(mask.sum())
 
-    rng = np.random.Generator(np.random.PCG64(seed))
-    probe = np.sort(rng.choice(wl.nq, 16, replace=False))
-    dt, _ = run(probe)
-    n = int(np.clip(16 * target_s / max(dt, 1e-3), 16, wl.nq))
-    rows = np.sort(rng.choice(wl.nq, n, replace=False))
-    dt, pairs = run(rows)
+    # the oracle's BLAS runs on every core this process may use
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores, user_api="blas"):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] + [1])
+        rng = np.random.Generator(np.random.PCG64(seed))
+        probe = np.sort(rng.choice(wl.nq, 16, replace=False))
+        dt, _ = run(probe)
+        n = int(np.clip(16 * target_s / max(dt, 1e-3), 16, wl.nq))
+        rows = np.sort(rng.choice(wl.nq, n, replace=False))
+        dt, pairs = run(rows)
     flops = 4.0 * wl.head_dim * wl.hq * pairs
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(min(threads, cores)), "kind": "oracle",
             "sample": f"{n} random query rows x {wl.hq} heads of {wl.name} (float64 numpy, "
                       f"{dt:.1f} s, incl. QK-Norm+RoPE of all {wl.nk} keys)"}
+
+
+def summarize_trace(path, steps):
+    """The headline run's launches in a rocprofv3 kernel trace (CSV) of this
+    script's default command: the attention and prologue dispatches of the
+    4.5B-shaped layer's main run (the ones before the first 24B-shaped
+    attention launch, at the layer's full grid), the last ``steps`` of which
+    are the timed ones.  Prints a markdown table (durations in microseconds)."""
+    import csv
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    end = min([int(r["Start_Timestamp"]) for r in rows if "ffa_fwd_bf16<48" in r["Kernel_Name"]] +
+              [int(rows[-1]["End_Timestamp"]) + 1])
+    grid = max(int(r["Grid_Size_X"]) for r in rows
+               if "ffa_fwd_bf16<24" in r["Kernel_Name"] and int(r["Start_Timestamp"]) < end)
+    att = [r for r in rows if "ffa_fwd_bf16<24" in r["Kernel_Name"] and int(r["Grid_Size_X"]) == grid
+           and int(r["Start_Timestamp"]) < end]
+    t0 = int(att[-steps]["Start_Timestamp"])
+    prev_end = int(att[-steps - 1]["End_Timestamp"]) if len(att) > steps else t0
+    pro = [r for r in rows if "qknorm_rope_kernelILi24" in r["Kernel_Name"] and prev_end <= int(r["Start_Timestamp"]) < end]
+    print("| launches | count | avg us | median us | min us | max us |")
+    print("|---|---|---|---|---|---|")
+    for name, sel in (("attention, timed steps", att[-steps:]), ("attention, warm-up steps", att[:-steps]),
+                      ("prologue, timed steps", pro)):
+        d = np.array([dur(r) for r in sel]) if sel else np.zeros(1)
+        print(f"| {name} | {len(sel)} | {d.mean():.1f} | {np.median(d):.1f} | {d.min():.1f} | {d.max():.1f} |")
+    gaps = [(int(att[i]["Start_Timestamp"]) - int(att[i - 1]["End_Timestamp"])) / 1e3
+            for i in range(len(att) - steps + 1, len(att))]
+    print(f"\nkernel: `{att[-1]['Kernel_Name'][:80]}`; grid {grid}; idle before the first timed launch "
+          f"{(t0 - prev_end) / 1e3:.1f} us; mean gap between timed attention launches {np.mean(gaps):.1f} us "
+          "(the prologue and the event packets)")
+
+
+def counter_means(path, name_part):
+    """Mean per dispatch of each counter in a rocprofv3 --pmc CSV, over the
+    dispatches whose kernel name contains ``name_part`` (rows of one
+    dispatch and counter are summed first)."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if name_part not in r["Kernel_Name"]:
+            continue
+        key = (r["Dispatch_Id"], r["Counter_Name"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (_, cname), v in per.items():
+        out.setdefault(cname, []).append(v)
+    return {k: float(np.mean(v)) for k, v in out.items()}
+
+
+def traffic_record(wl_name, kernel, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes):
+    """HBM bytes per launch of ``kernel`` from FETCH_SIZE and WRITE_SIZE (KiB
+    per dispatch), each scaled by what the same counter reads for a plain
+    device copy of ``copy_bytes`` bytes; the record committed_traffic()
+    reads back (tied to the kernel sources' sha256)."""
+    f = counter_means(fetch_csv, kernel)["FETCH_SIZE"]
+    w = counter_means(write_csv, kernel)["WRITE_SIZE"]
+    cf = counter_means(copy_fetch_csv, "copyBuffer")["FETCH_SIZE"]
+    cw = counter_means(copy_write_csv, "copyBuffer")["WRITE_SIZE"]
+    ff, wf = copy_bytes / 1024.0 / cf, copy_bytes / 1024.0 / cw
+    return {"workload": wl_name, "kernel": kernel, "fetch_kib": f, "write_kib": w, "fetch_factor": ff,
+            "write_factor": wf, "traffic_bytes_per_launch": 1024.0 * (f * ff + w * wf),
+            "kernel_sources_sha256": kernel_sources_sha256()}
 
 
 def main():
@@ -465,7 +590,22 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (a known-size "
                          "reference for calibrating the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="print the headline run's timed launches from a rocprofv3 kernel trace of this script "
+                         "(no GPU needed) and exit")
+    ap.add_argument("--traffic-record", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="print the HBM-traffic record of the workload's attention kernel from four rocprofv3 "
+                         "--pmc CSVs (FETCH_SIZE, WRITE_SIZE of this script; the same of --copy-bytes 1 GiB) "
+                         "and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.traffic_record:
+        d = 24 if args.workload == "magi4.5b" else 48
+        print(json.dumps(traffic_record(args.workload, f"ffa_fwd_bf16<{d}", *args.traffic_record, 1 << 30),
+                         indent=1))
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.steps)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the attention path has no "
               "multi-GPU mode", file=sys.stderr)
@@ -521,13 +661,17 @@ def main():
                    "query_heads": wl.hq, "kv_groups": wl.hkv, "head_dim": wl.head_dim,
                    "masked_flops_per_step": flops, "work_items": nwork, "parallelism": "single GPU",
                    "kv_layout": "group-major [hkv][nk][d], written by the prologue"},
-        "pct_of_bf16_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": committed_traffic(wl.name),
-                     "kernel": "ffa_fwd_bf16", "avg_launch_ms": round(ms_kernel, 5),
-                     "median_launch_ms": round(launches[len(launches) // 2], 5),
-                     "min_launch_ms": round(launches[0], 5)},
+        # whole step (plan, upload, prologue, attention) against the bf16 peak;
+        # the attention kernel alone is in roofline.frac
+        "step_pct_of_bf16_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "roofline": with_ceilings(
+            {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+             "traffic": committed_traffic(wl.name),
+             "kernel": "ffa_fwd_bf16", "avg_launch_ms": round(ms_kernel, 5),
+             "median_launch_ms": round(launches[len(launches) // 2], 5),
+             "min_launch_ms": round(launches[0], 5), "ceilings": ceilings(wl.head_dim)},
+            achieved, wl.head_dim),
     }
     if first_chunk is not None:
         rec["first_chunk"] = first_chunk
@@ -535,9 +679,26 @@ def main():
         wl2 = W.make_workload("magi24b")
         f2 = masked_flops(wl2)
         s2, k2, _ = run_gpu(wl2, max(3, args.steps // 2), 2)
-        rec["secondary"] = {"workload": wl2.name, "ms_per_step": round(s2, 4),
-                            "value": round(f2 / (s2 * 1e-3) / 1e12, 2), "kernel_tflops": round(f2 / (k2 * 1e-3) / 1e12, 2),
-                            "pct_of_bf16_peak": round(100.0 * f2 / (k2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        kt2 = f2 / (k2 * 1e-3) / 1e12
+        rec["secondary"] = with_ceilings(
+            {"workload": wl2.name, "ms_per_step": round(s2, 4), "value": round(f2 / (s2 * 1e-3) / 1e12, 2),
+             "avg_launch_ms": round(k2, 4), "kernel_tflops": round(kt2, 2),
+             "pct_of_bf16_peak": round(100.0 * kt2 / PEAK_BF16_TFLOPS, 2)}, kt2, wl2.head_dim)
+        # the streaming step (linear layout: 20 cached + 4 in-flight chunks)
+        # and the packed varlen layer with KV-range-limited chunks (seed 0)
+        more = {}
+        for name in ("stream", "varlen"):
+            w = W.make_workload(name)
+            fm = masked_flops(w)
+            sm, km, nw = run_gpu(w, 3, 1)
+            kt = fm / (km * 1e-3) / 1e12
+            more[name] = with_ceilings(
+                {"description": w.description, "masked_flops": fm, "work_items": nw, "ms_per_step": round(sm, 4),
+                 "value": round(fm / (sm * 1e-3) / 1e12, 2), "avg_launch_ms": round(km, 4),
+                 "kernel_tflops": round(kt, 2), "pct_of_bf16_peak": round(100.0 * kt / PEAK_BF16_TFLOPS, 2)},
+                kt, w.head_dim)
+        rec["stream"] = more["stream"]
+        rec["varlen"] = more["varlen"]
     if not args.no_secondary:
         # backward: 5 products of 2 d flops per visible pair and head
         # (S recomputed, dP, dV, dK, dQ) = 2.5 x the forward's masked FLOPs
@@ -562,9 +723,10 @@ def main():
             w = W.make_workload(name)
             ms_s, ms_k, _ = run_gpu(w, 10, 3, window=w_tok)
             fw = 4.0 * w.head_dim * w.hq * window_pairs(w, w_tok)
-            win[name] = {"window_tokens": w_tok, "ms_per_step": round(ms_s, 4), "avg_launch_ms": round(ms_k, 4),
-                         "kernel_tflops": round(fw / (ms_k * 1e-3) / 1e12, 2),
-                         "pct_of_bf16_peak": round(100.0 * fw / (ms_k * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+            kt = fw / (ms_k * 1e-3) / 1e12
+            win[name] = with_ceilings({"window_tokens": w_tok, "ms_per_step": round(ms_s, 4),
+                                       "avg_launch_ms": round(ms_k, 4), "kernel_tflops": round(kt, 2),
+                                       "pct_of_bf16_peak": round(100.0 * kt / PEAK_BF16_TFLOPS, 2)}, kt, w.head_dim)
         rec["sliding_window"] = win
         pro = {}
         for name in ("magi4.5b", "magi24b"):

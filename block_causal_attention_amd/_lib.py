@@ -8,7 +8,10 @@ from __future__ import annotations
 import ctypes as C
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmagi_bca.so")
+# MAGI_BCA_LIBRARY names another build of the same library (the host-
+# sanitized one the CPU tests make); by default the in-tree build is loaded
+LIB_PATH = os.environ.get("MAGI_BCA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                              "libmagi_bca.so")
 
 MAGI_OK = 0
 MAGI_ERR_INVALID_ARG = -1

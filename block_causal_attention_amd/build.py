@@ -13,6 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmagi_bca.so")
+RATES = os.path.join(PKG, "magi_rates")  # issue-rate probe program (csrc/rates.hip)
 SOURCES = ["plan.cpp", "api.cpp", "qknorm_rope.hip", "ffa_fwd.hip", "ffa_bwd.hip", "scratch.hip"]
 ARCH = "gfx950"
 
@@ -37,6 +38,29 @@ def compile_flags():
     ]
 
 
+def build_host_sanitized(out_path: str) -> str:
+    """The same library with its host code under AddressSanitizer and
+    UndefinedBehaviorSanitizer (device code unchanged), for the CPU tests:
+    load it with the sanitizer runtime preloaded (asan_runtime())."""
+    cmd = [hipcc(), *[f for f in compile_flags() if f != "-O3"], "-O1", "-g",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+           "-shared-libsan", "-shared", "-o", out_path, *[os.path.join(CSRC, s) for s in SOURCES]]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc (sanitized host) failed ({res.returncode}):\n{res.stdout}{res.stderr}")
+    return out_path
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.exists(path):
+        raise RuntimeError("AddressSanitizer runtime not found")
+    return path
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     tmp = LIB + ".tmp"
@@ -51,6 +75,12 @@ def build(verbose: bool = False) -> str:
     if verbose and out.strip():
         print(out)
     os.replace(tmp, LIB)
+    # the issue-rate probe behind the kernels' ceilings (a separate program)
+    cmd = [hipcc(), *compile_flags(), "-o", RATES + ".tmp", os.path.join(CSRC, "rates.hip")]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on rates.hip ({res.returncode}):\n{res.stdout}{res.stderr}")
+    os.replace(RATES + ".tmp", RATES)
     return LIB
 
 

@@ -127,7 +127,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
   const bool rvalid = t < qlen;
   const int32_t qi = wi.q_start + (rvalid ? t : 0);
   float lse2 = a.lse[(int64_t)qi * a.hq + head] * kLog2e;
-  if (!(lse2 > -INFINITY && lse2 < INFINITY)) lse2 = 0.f;  // a row that sees no key
+  // a row that sees no key (LSE = -inf); tested on the bits, which no
+  // no-NaN assumption of the device compile can fold: exponent all ones
+  if ((__float_as_uint(lse2) & 0x7f800000u) == 0x7f800000u) lse2 = 0.f;
   const float dl = a.delta[(int64_t)qi * a.hq + head];
   __bf16 qa0, qa1, da0, da1;
   split_bf16(-lse2 / c, qa0, qa1);
@@ -451,7 +453,7 @@ __global__ __launch_bounds__(2 * kKeys / KB, 2) void bwd_dkdv_bf16(BwdArgs a) {
       const int64_t tok = r.t0 + tid / G;
       const int64_t idx = tok * a.hq + g * G + tid % G;
       float l2 = a.lse[idx] * kLog2e;
-      if (!(l2 > -INFINITY && l2 < INFINITY)) l2 = 0.f;
+      if ((__float_as_uint(l2) & 0x7f800000u) == 0x7f800000u) l2 = 0.f;  // no key: -inf (bit test)
       split_bf16(-l2 * cinv, aq0, aq1);
       split_bf16(-a.delta[idx], ao0, ao1);
     }

@@ -241,8 +241,11 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
   // max.
   bool bounded = false;
   if (a.k_norm_max != nullptr) {
-    const float B = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(a.k_norm_max[g])));
-    bool ok = B > 0.f;  // also false for NaN
+    const uint32_t Bbits = __builtin_amdgcn_readfirstlane(__float_as_uint(a.k_norm_max[g]));
+    const float B = __uint_as_float(Bbits);
+    // positive and finite, tested on the bits (the device code is compiled
+    // assuming no NaN, so a float compare could be folded): 0 < bits < +inf
+    bool ok = Bbits - 1u < 0x7f7fffffu;
     float mb_row[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {

@@ -376,8 +376,9 @@ def qknorm_rope(q: torch.Tensor, k: Optional[torch.Tensor], gain_q: torch.Tensor
             raise ValueError("v_out must match k_out in shape, strides and dtype")
     elif v_out is not None:
         raise ValueError("v_out needs v")
-    if k_norm_max is not None and (k_norm_max.dtype != torch.float32 or k_norm_max.numel() < hkv):
-        raise ValueError("k_norm_max must be float32 with one entry per K head")
+    if k_norm_max is not None and (k_norm_max.dtype != torch.float32 or k_norm_max.numel() < hkv or
+                                   not k_norm_max.is_contiguous() or k_norm_max.device != q.device):
+        raise ValueError("k_norm_max must be a contiguous float32 tensor of >= hkv entries on q's device")
     for t in (gain_q, gain_k, rope_base):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError("gains and rope_base must be contiguous float32")
@@ -428,6 +429,9 @@ def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
     if (plan.nq, plan.nk, plan.hq, plan.hkv, plan.head_dim, plan.dtype) != \
             (q.shape[0], k.shape[0], hq, hkv, d, dtype_code(q.dtype)):
         raise ValueError("plan was made for a different shape or dtype")
+    if k_norm_max is not None and (k_norm_max.dtype != torch.float32 or k_norm_max.numel() < hkv or
+                                   not k_norm_max.is_contiguous() or k_norm_max.device != q.device):
+        raise ValueError("k_norm_max must be a contiguous float32 tensor of >= hkv entries on q's device")
     out = torch.empty_like(q) if out is None else out
     _check_3d("out", out, hq, d)
     if lse is None and return_lse:

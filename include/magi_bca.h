@@ -135,6 +135,15 @@ const char* magi_last_error(void);
 /*
  * magi_slices_build -- mask description -> AttnSlices.           [host only]
  *
+ * The mask it writes out: block-causal attention, full inside a chunk and
+ * causal across chunks (study notes, "整体 pipeline" and "自回归去噪 DiT",
+ * Block-Causal Attention bullet); a KV range r that lets a chunk see only
+ * itself and its r predecessors (study notes, "推理技巧", KV Cache bullet);
+ * several unrelated videos packed into one sequence, invisible to each
+ * other (interview with Zhang Zheng, answer on how FFA expresses the mask);
+ * each expressed as AttnSlices (q range, k range, mask type), the FFA
+ * formulation (study notes, "训练 Infra", Flex-Flash-Attention bullet).
+ *
  * For every query chunk c of every video emits one FULL slice
  *   q = [q_offset + j*C, q_offset + (j+1)*C)          (j = c - first query chunk)
  *   k = [k_offset + lo*C, k_offset + (c+1)*C)         (lo = 0, or max(0, c - r) with KV range r)
@@ -156,10 +165,11 @@ int32_t magi_slices_build(const magi_seq_desc* seqs, int32_t num_seqs,
  * AttnSlices.                                                    [host only]
  *
  * The pages cache the keys and values of denoised chunks and reuse them for
- * new chunks, with up to 4 chunks in flight, a KV range that bounds the
- * history a chunk sees (constant peak memory), and per-denoising-stage KV
- * ranges for controllable transitions (study notes, "推理 Infra", KV Cache
- * bullet; InfoQ article, inference paragraph).  A ring of ring_slots chunk
+ * new chunks, with up to 4 chunks in flight (study notes, "整体 pipeline"), a
+ * KV range that bounds the history a chunk sees (constant peak memory), and
+ * per-denoising-stage KV ranges for controllable transitions (study notes,
+ * "推理技巧", KV Cache bullet; yaliqi.com article, KV Cache and transition
+ * items).  A ring of ring_slots chunk
  * slots holds exactly that history: the prologue writes each in-flight
  * chunk's keys (and the caller its values) into the chunk's slot, and a
  * chunk stays there once denoised until the ring wraps over it.  In-flight
@@ -245,6 +255,14 @@ int32_t magi_schedule(const magi_attn_slice* slices, int32_t num_slices,
 /*
  * magi_qknorm_rope -- QK-Norm then 3D RoPE on Q and (optionally) K.  [device]
  *
+ * The pages normalise Q and K before attention (study notes, "自回归去噪
+ * DiT", QK-Norm + GQA bullet; 量子位 article, "QK-Norm和GQA") and encode
+ * positions with a 3D RoPE over time and space whose base frequency is
+ * learnable (study notes, "自回归去噪 DiT", Block-Causal Attention bullet;
+ * 量子位 article, "Block-Causal Attention", 3D RoPE item).  They give no
+ * formula; the RMS norm, the equal t/h/w thirds of head_dim and the pairing
+ * below are this library's reading.
+ *
  * For every token i and head h of X in {Q, K}:
  *   y = x / sqrt(mean_d(x^2) + eps) * gain           (RMS over head_dim)
  *   then for axis a in (t, h, w), channel pair (2j, 2j+1) of section a
@@ -294,6 +312,13 @@ int32_t magi_qknorm_rope(const void* q_in, void* q_out, int64_t nq, int32_t hq, 
 
 /*
  * magi_ffa_fwd -- Flex-Flash-Attention forward over a work list.   [device]
+ *
+ * Softmax attention restricted to the union of AttnSlices, the FFA kernel
+ * of the pages (study notes, "训练 Infra", Flex-Flash-Attention bullet;
+ * 量子位 article, "Flex-Flash-Attention"), with grouped-query attention at
+ * 128 query heads over 8 KV groups (study notes, "模型规格（Table 2）" and
+ * "自回归去噪 DiT", QK-Norm + GQA bullet).  The pages' kernel uses atomics;
+ * here each work item owns its output rows, so none are needed.
  *
  * For every query row i and head h (KV group g = h / (hq/hkv)):
  *   O[i,h]   = sum_k softmax_k(scale * q[i,h].k[k,g]) v[k,g]   over the visible k
