@@ -377,8 +377,8 @@ def qknorm_rope(q: torch.Tensor, k: Optional[torch.Tensor], gain_q: torch.Tensor
     elif v_out is not None:
         raise ValueError("v_out needs v")
     if k_norm_max is not None and (k_norm_max.dtype != torch.float32 or k_norm_max.numel() < hkv or
-                                   not k_norm_max.is_contiguous() or k_norm_max.device != q.device):
-        raise ValueError("k_norm_max must be a contiguous float32 tensor of >= hkv entries on q's device")
+                                   not k_norm_max.is_contiguous() or (k is None or k_norm_max.device != k.device)):
+        raise ValueError("k_norm_max must be a contiguous float32 tensor of >= hkv entries on k's device")
     for t in (gain_q, gain_k, rope_base):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError("gains and rope_base must be contiguous float32")

@@ -124,30 +124,119 @@ def test_bwd_fp32_tiny():
     bwd_case(inp.q.numpy(), inp.k.numpy(), inp.v.numpy(), rand(tuple(inp.q.shape), 9), sl, "fp32")
 
 
+def oracle_prologue(wl, inp, rows=None):
+    """q_hat (of ``rows``, all rows if None) and the prescaled k_hat from the
+    oracle's QK-Norm + 3D RoPE of the raw inputs, float64 (never the GPU's)"""
+    inv = oracle.rope_inv_freq(wl.rope_base, wl.head_dim)
+    q = inp.q if rows is None else inp.q[rows]
+    pq = inp.pos_q if rows is None else inp.pos_q[rows]
+    qn = oracle.rope_3d(oracle.qk_norm(np64(q), np64(inp.gain_q), wl.eps), pq.numpy(), inv)
+    kn = oracle.rope_3d(oracle.qk_norm(np64(inp.k), np64(inp.gain_k), wl.eps), inp.pos_k.numpy(), inv)
+    return qn, kn * (wl.softmax_scale * ops.LOG2E)
+
+
+def gpu_fwd_bwd(wl, inp, dO):
+    """the path as the benchmark runs it: prologue (scale folded into K, K
+    and V written group-major, key-norm bound), forward, then the backward
+    over the same plan; returns (dq, dk, dv, plan)"""
+    g = lambda t: t.to(DEV)
+    knm = torch.empty(wl.hkv, dtype=torch.float32, device=DEV)
+    qh, kh, vh = ops.qknorm_rope(g(inp.q), g(inp.k), g(inp.gain_q), g(inp.gain_k), g(inp.pos_q), g(inp.pos_k),
+                                 torch.tensor(wl.rope_base, dtype=torch.float32, device=DEV), wl.eps,
+                                 k_out=ops.kv_group_major(wl.nk, wl.hkv, wl.head_dim, torch.bfloat16),
+                                 k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm, v=g(inp.v))
+    plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, torch.bfloat16, backward=True)
+    O, L = ops.ffa_fwd(qh, kh, vh, plan, softmax_scale=ops.LN2, k_norm_max=knm)
+    dq, dk, dv = ops.ffa_bwd(qh, kh, vh, O, g(dO), L, plan, softmax_scale=ops.LN2)
+    torch.cuda.synchronize()
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert not torch.isnan(t).any(), f"{name} has NaN entries"
+    return dq, dk, dv, plan
+
+
 def test_bwd_video_after_prologue():
     # the path as the model runs it: QK-Norm + RoPE prologue, scale folded
     # into K, forward, then the backward of the attention on 4 chunks x 240
-    # tokens, 32 query heads over 2 groups
+    # tokens, 32 query heads over 2 groups; the oracle takes q_hat and k_hat
+    # from its own prologue of the raw inputs, so the difference also holds
+    # the bf16 storage of q_hat and k_hat (about 2^-9 relative)
     note("bwd video after prologue")
     seqs = [W.SeqDesc(240, 4, 4, 0, 0, (-1, -1, -1, -1), 1, 15, 16)]
     wl = W.Workload("bwdvideo", seqs, 960, 960, 32, 2, 24, "bf16", (0.8, 1.2))
     inp = W.make_inputs(wl, 3)
-    g = lambda t: t.to(DEV)
-    knm = torch.empty(wl.hkv, dtype=torch.float32, device=DEV)
-    qh, kh = ops.qknorm_rope(g(inp.q), g(inp.k), g(inp.gain_q), g(inp.gain_k), g(inp.pos_q), g(inp.pos_k),
-                             torch.tensor(wl.rope_base, dtype=torch.float32, device=DEV), wl.eps,
-                             k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm)
-    v = g(inp.v)
-    plan = ops.plan_for_videos(wl.seqs, wl.nq, wl.nk, wl.hq, wl.hkv, wl.head_dim, torch.bfloat16, backward=True)
-    O, L = ops.ffa_fwd(qh, kh, v, plan, softmax_scale=ops.LN2, k_norm_max=knm)
-    dO = torch.from_numpy(rand((960, 32, 24), 10)).to(torch.bfloat16).to(DEV)
-    dq, dk, dv = ops.ffa_bwd(qh, kh, v, O, dO, L, plan, softmax_scale=ops.LN2)
-    torch.cuda.synchronize()
+    dO = torch.from_numpy(rand((960, 32, 24), 10)).to(torch.bfloat16)
+    dq, dk, dv, _ = gpu_fwd_bwd(wl, inp, dO)
     mask = oracle.video_mask(wl.seqs, wl.nq, wl.nk)
-    gq, gk, gv = oracle.attention_backward(np64(qh), np64(kh), np64(v), np64(dO), mask, ops.LN2)
+    qn, kn = oracle_prologue(wl, inp)
+    gq, gk, gv = oracle.attention_backward(qn, kn, np64(inp.v), np64(dO), mask, ops.LN2)
     compare(np64(dq), gq, "bf16", "dQ")
     compare(np64(dk), gk, "bf16", "dK")
     compare(np64(dv), gv, "bf16", "dV")
+
+
+def test_bwd_full_size_magi45b():
+    # the 4.5B-shaped layer at full size in the benchmark's configuration
+    # (split key tiles and the partial-slot reduce included): every dQ row of
+    # one KV group's 16 heads and every key's dK, dV of that group against
+    # the oracle (rows in blocks; dK, dV summed over them), plus sampled dQ
+    # rows over all 128 heads
+    wl = W.make_workload("magi4.5b")
+    note("bwd full size magi4.5b: inputs")
+    inp = W.make_inputs(wl, 0)
+    dO = torch.from_numpy(rand((wl.nq, wl.hq, wl.head_dim), 31)).to(torch.bfloat16)
+    note("bwd full size magi4.5b: GPU forward + backward")
+    dq, dk, dv, plan = gpu_fwd_bwd(wl, inp, dO)
+    assert plan.num_slots > 0 and plan.host["kreduce"].shape[0] > 0, "the split dK/dV path must run"
+    note(f"bwd full size magi4.5b: oracle ({plan.num_slots} partial slots on the GPU)")
+    qn, kn = oracle_prologue(wl, inp)
+    v64, do64 = np64(inp.v), np64(dO)
+    mask = oracle.video_mask(wl.seqs, wl.nq, wl.nk)
+    g, G = 5, wl.hq // wl.hkv
+    hs = slice(g * G, (g + 1) * G)
+    gq = np.zeros((wl.nq, G, wl.head_dim))
+    gk = np.zeros((wl.nk, 1, wl.head_dim))
+    gv = np.zeros((wl.nk, 1, wl.head_dim))
+    for r0 in range(0, wl.nq, 720):
+        rs = slice(r0, r0 + 720)
+        a, b, c = oracle.attention_backward(qn[rs, hs], kn[:, g:g + 1], v64[:, g:g + 1], do64[rs, hs], mask[rs],
+                                            ops.LN2)
+        gq[rs], gk, gv = a, gk + b, gv + c
+    compare(np64(dq[:, hs]), gq, "bf16", f"dQ group {g}")
+    compare(np64(dk[:, g]), gk[:, 0], "bf16", f"dK group {g}")
+    compare(np64(dv[:, g]), gv[:, 0], "bf16", f"dV group {g}")
+    rows = W.sample_rows(wl, 48, 1)
+    a, _, _ = oracle.attention_backward(qn[rows], kn, v64, do64[rows], mask[rows], ops.LN2)
+    compare(np64(dq[rows]), a, "bf16", "dQ sampled rows, all heads")
+
+
+def test_bwd_full_size_magi24b():
+    # the 24B-shaped layer at full size: sampled dQ rows over all heads
+    # against the oracle, and two sums that hold at any size for every KV
+    # group (every row sees a key): sum_k dV[k] = sum over the group's rows
+    # and heads of dO, and sum_k dK[k] = 0 (sum_k dS = dO.O - delta = 0 per row)
+    wl = W.make_workload("magi24b")
+    note("bwd full size magi24b: inputs")
+    inp = W.make_inputs(wl, 0)
+    dO = torch.from_numpy(rand((wl.nq, wl.hq, wl.head_dim), 41)).to(torch.bfloat16)
+    note("bwd full size magi24b: GPU forward + backward")
+    dq, dk, dv, plan = gpu_fwd_bwd(wl, inp, dO)
+    assert plan.num_slots > 0
+    rows = W.sample_rows(wl, 24, 2)
+    note(f"bwd full size magi24b: oracle on {len(rows)} rows")
+    qn, kn = oracle_prologue(wl, inp, rows)
+    mask = oracle.video_mask(wl.seqs, wl.nq, wl.nk, rows)
+    a, _, _ = oracle.attention_backward(qn, kn, np64(inp.v), np64(dO[rows]), mask, ops.LN2)
+    compare(np64(dq[rows]), a, "bf16", "dQ sampled rows, all heads")
+    G = wl.hq // wl.hkv
+    do_sum = dO.double().view(wl.nq, wl.hkv, G, wl.head_dim).sum(dim=(0, 2)).numpy()
+    dv_sum = dv.double().sum(dim=0).cpu().numpy()
+    dk_sum = dk.double().sum(dim=0).cpu().numpy()
+    scale_v = np.linalg.norm(do_sum)
+    err_v = np.linalg.norm(dv_sum - do_sum) / scale_v
+    # against the sum of |dK| entries: cancellation leaves rounding of that order
+    err_k = np.abs(dk_sum).max() / dk.double().abs().sum(dim=0).max().item()
+    note(f"sum dV vs sum dO rel {err_v:.3e}; |sum dK| / sum |dK| {err_k:.3e}")
+    assert err_v <= 1e-2 and err_k <= 1e-2
 
 
 def test_bwd_bitwise_deterministic():
