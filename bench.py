@@ -407,11 +407,6 @@ def run_ring(steps, warmup, seed=0):
     dev = "cuda"
     g = torch.Generator(device="cpu").manual_seed(seed + 11)
     mk = lambda *shape: torch.randn(shape, generator=g).to(torch.bfloat16).to(dev)
-    # cached chunks (already processed), stored group-major like the prologue writes them
-    ring_k, ring_v = ops.kv_group_major(S * C, hkv, d, torch.bfloat16, dev), \
-        ops.kv_group_major(S * C, hkv, d, torch.bfloat16, dev)
-    ring_k.copy_(mk(S * C, hkv, d))
-    ring_v.copy_(mk(S * C, hkv, d))
     q, knew, vnew = mk(n * C, hq, d), mk(n * C, hkv, d), mk(n * C, hkv, d)
     gq = (0.8 + 0.4 * torch.rand(d, generator=g)).to(dev)
     gk = (0.8 + 0.4 * torch.rand(d, generator=g)).to(dev)
@@ -420,7 +415,15 @@ def run_ring(steps, warmup, seed=0):
     qh = torch.empty_like(q)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[0], hq, dtype=torch.float32, device=dev)
+    knm = torch.empty(hkv, dtype=torch.float32, device=dev)
     scale = d ** -0.5
+    # cached chunks, processed by earlier steps: normalised, rotated and
+    # scaled by the prologue into their slots, group-major
+    ring_k, ring_v = ops.kv_group_major(S * C, hkv, d, torch.bfloat16, dev), \
+        ops.kv_group_major(S * C, hkv, d, torch.bfloat16, dev)
+    pos_c = torch.randint(0, 24, (S * C, 3), generator=g, dtype=torch.int32).to(dev)
+    ops.qknorm_rope(q[:1], mk(S * C, hkv, d), gq, gk, pos[:1], pos_c, base, 1e-6, q_out=qh[:1], k_out=ring_k,
+                    k_scale=scale * ops.LOG2E, v=mk(S * C, hkv, d), v_out=ring_v)
     stream = torch.cuda.current_stream()
     runs = ops.ring_slot_runs(S, first + count - n, n)
     ev = []
@@ -436,14 +439,16 @@ def run_ring(steps, warmup, seed=0):
             ops.qknorm_rope(q[:1] if done else q, knew[done * C:(done + m) * C], gq, gk,
                             pos[:1] if done else pos, pos[done * C:(done + m) * C], base, 1e-6,
                             q_out=qh[:1] if done else qh, k_out=ring_k[s0 * C:(s0 + m) * C],
-                            k_scale=scale * ops.LOG2E, v=vnew[done * C:(done + m) * C],
+                            k_scale=scale * ops.LOG2E, k_norm_max=knm, v=vnew[done * C:(done + m) * C],
                             v_out=ring_v[s0 * C:(s0 + m) * C])
             done += m
         if record:
             stream.wait_event(plan.ready)  # the upload wait stays outside the kernel's events
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-        ops.ffa_fwd(qh, ring_k, ring_v, plan, out=out, lse=lse, softmax_scale=ops.LN2)
+        # the bound on key norms follows from the QK-Norm gains, so it holds
+        # for the cached keys as well as for this step's
+        ops.ffa_fwd(qh, ring_k, ring_v, plan, out=out, lse=lse, softmax_scale=ops.LN2, k_norm_max=knm)
         if record:
             b.record(stream)
             ev.append((a, b))
@@ -577,6 +582,34 @@ def traffic_record(wl_name, kernel, fetch_csv, write_csv, copy_fetch_csv, copy_w
             "kernel_sources_sha256": kernel_sources_sha256()}
 
 
+def counter_table(kernel, d, csvs, blocks):
+    """Derived figures of the forward kernel from rocprofv3 --pmc CSVs (the
+    four passes in profiles/counters_ffa_fwd.md): MFMA busy share, co-issue,
+    LDS bank-conflict share, resident waves, instructions per 32 x 32 score
+    block.  Returns a dict of counter means per dispatch and the derived
+    values."""
+    c = {}
+    for path in csvs:
+        c.update(counter_means(path, kernel))
+    out = dict(c)
+    cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / 8.0        # summed over the 8 XCDs
+    simds = 1024
+    if cyc:
+        out["kernel_cycles"] = cyc
+        out["mfma_busy"] = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (simds * cyc)
+        out["waves_per_simd"] = 4.0 * c.get("SQ_WAVE_CYCLES", 0.0) / (simds * cyc)
+    if c.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+        out["mfma_coexec"] = c.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / c["SQ_VALU_MFMA_BUSY_CYCLES"]
+    if c.get("SQ_ACTIVE_INST_LDS"):
+        out["lds_conflict_share"] = c.get("SQ_LDS_BANK_CONFLICT", 0.0) / c["SQ_ACTIVE_INST_LDS"]
+    # per 32-key x 32-row score block of one wave (blocks = masked FLOPs / (4 d 1024))
+    for name in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_VALU_CVT", "SQ_INSTS_LDS",
+                 "SQ_INSTS_SALU"):
+        if name in c:
+            out[name + "_per_block"] = c[name] / blocks
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -597,7 +630,16 @@ def main():
                     help="print the HBM-traffic record of the workload's attention kernel from four rocprofv3 "
                          "--pmc CSVs (FETCH_SIZE, WRITE_SIZE of this script; the same of --copy-bytes 1 GiB) "
                          "and exit (no GPU needed)")
+    ap.add_argument("--counter-table", nargs="+", metavar="PMC_CSV",
+                    help="print the forward kernel's derived counter figures (workload's head_dim) from "
+                         "rocprofv3 --pmc CSVs of this script and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.counter_table:
+        d = 24 if args.workload == "magi4.5b" else 48
+        import workloads as W
+        blocks = masked_flops(W.make_workload(args.workload)) / (4.0 * d * 1024)
+        print(json.dumps(counter_table(f"ffa_fwd_bf16<{d}", d, args.counter_table, blocks), indent=1))
+        return
     if args.traffic_record:
         d = 24 if args.workload == "magi4.5b" else 48
         print(json.dumps(traffic_record(args.workload, f"ffa_fwd_bf16<{d}", *args.traffic_record, 1 << 30),
