@@ -336,6 +336,27 @@ def run_prologue(wl, steps=200, warmup=50, seed=0):
     return float(np.mean(ms)), ms[len(ms) // 2], nbytes
 
 
+def run_copy(nbytes, steps=200, warmup=50):
+    """A plain device-to-device copy (torch copy_) that reads and writes
+    nbytes / 2 bytes each, timed like run_prologue: what a streaming kernel
+    with the prologue's traffic reaches on this GPU (mean ms)."""
+    import torch
+    src = torch.ones(nbytes // 2, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    ev = []
+    with steady_timing():
+        warm_up(lambda rec: dst.copy_(src), warmup)
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            dst.copy_(src)
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
 def run_first_chunk(steps=300, warmup=100, d=24):
     """A streaming generation's first chunk (2 latent frames x 12 x 16 = 384
     tokens, 128/8 heads): prologue + attention, launch-bound.  Wall time per
@@ -774,9 +795,12 @@ def main():
         for name in ("magi4.5b", "magi24b"):
             w = W.make_workload(name)
             mean_ms, med_ms, nbytes = run_prologue(w)
+            copy_ms = run_copy(nbytes)
             pro[name] = {"avg_launch_ms": round(mean_ms, 5), "median_launch_ms": round(med_ms, 5),
                          "algorithmic_bytes": nbytes, "GB/s": round(nbytes / (mean_ms * 1e-3) / 1e9, 1),
-                         "frac_of_hbm_peak": round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                         "frac_of_hbm_peak": round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "same_size_copy_GB/s": round(nbytes / (copy_ms * 1e-3) / 1e9, 1),
+                         "frac_of_same_size_copy": round(copy_ms / mean_ms, 4)}
         rec["prologue"] = pro
         ms_s, ms_k, fr = run_ring(5, 2)
         rec["streaming_ring"] = {"shape": "4 in-flight x 3600 queries over a 24-slot ring (86400 keys), 128/8, d=48",
