@@ -42,10 +42,14 @@ using namespace dev;
 
 constexpr int kRows = 256;      // query rows per dQ work item (the forward's items)
 constexpr int kKeys = 128;      // keys per dK/dV work item (4 waves x 32)
-constexpr int NT = 512;         // threads per workgroup of the bf16 dQ pass
+constexpr int NT = 512;         // threads per workgroup of the bf16 dQ pass at one row block per wave
 // 32-key blocks per wave of the bf16 dK/dV pass (head_dim 24 / 48).  Two blocks per
 // wave at head_dim 24 need 256 VGPRs (2 waves per SIMD) and measured no faster.
 constexpr int KB24 = 1, KB48 = 1;
+// 32-row blocks per wave of the bf16 dQ pass (head_dim 24 / 48): two halve
+// the K/V operand reads per score; measured 5 % (24, 3 waves per SIMD at
+// 168 VGPRs) and 11 % (48, 2 waves per SIMD) faster than one
+constexpr int RBQ24 = 2, RBQ48 = 2;
 constexpr int TK = 64;          // keys per K/V tile (dQ pass)
 constexpr int TQ = 64;          // query rows per Q/dO tile (dK/dV pass)
 constexpr int kThreads32 = 256;  // fp32 kernels
@@ -88,10 +92,14 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
 
 // ----------------------------------------------------------------- dQ pass
 
-template <int D, bool PRESCALED>
-__global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
+// RB: 32-row blocks per wave.  The item's kRows rows are spread over
+// kRows / (32 RB) waves; RB = 2 lets one wave's K/V operand reads (and the
+// transposed K reads) serve 64 rows, halving those LDS reads per score.
+template <int D, bool PRESCALED, int RB>
+__global__ __launch_bounds__(NT / RB, RB == 2 && D == 24 ? 3 : 2) void bwd_dq_bf16(BwdArgs a) {
   using C = BCfg<D>;
-  constexpr int NCH = (TK * C::CH + NT - 1) / NT;
+  constexpr int NTQ = NT / RB;                       // threads per workgroup
+  constexpr int NCH = (TK * C::CH + NTQ - 1) / NTQ;  // 16-byte chunks per thread per tile (K and V each)
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][TK * C::PITCH];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[2][TK * C::PITCH];
 
@@ -114,30 +122,35 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
   // padding columns of every K and V buffer: D and D+1 are 1 (they meet the
   // augmented slots), the rest 0; tile stores never touch them
   for (int b = 0; b < 2; ++b)
-    for (int i = tid; i < TK * (C::DA - D); i += NT) {
+    for (int i = tid; i < TK * (C::DA - D); i += NTQ) {
       const int col = D + i % (C::DA - D), row = i / (C::DA - D);
       const __bf16 x = (__bf16)(col < D + 2 ? 1.0f : 0.0f);
       Ks[b][row * C::PITCH + col] = x;
       Vs[b][row * C::PITCH + col] = x;
     }
 
-  // this lane's query row (one 32-row MFMA column block per wave)
-  const int n = wave * 32 + ln;
-  const int t = n / G, hg = n % G, head = g * G + hg;
-  const bool rvalid = t < qlen;
-  const int32_t qi = wi.q_start + (rvalid ? t : 0);
-  float lse2 = a.lse[(int64_t)qi * a.hq + head] * kLog2e;
-  // a row that sees no key (LSE = -inf); tested on the bits, which no
-  // no-NaN assumption of the device compile can fold: exponent all ones
-  if ((__float_as_uint(lse2) & 0x7f800000u) == 0x7f800000u) lse2 = 0.f;
-  const float dl = a.delta[(int64_t)qi * a.hq + head];
-  __bf16 qa0, qa1, da0, da1;
-  split_bf16(-lse2 / c, qa0, qa1);
-  split_bf16(-dl, da0, da1);
-  bf16x8 qreg[C::KS], dreg[C::KS];
-  {
-    const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q) + (int64_t)qi * a.q_stride + (int64_t)head * D;
-    const __bf16* drow = reinterpret_cast<const __bf16*>(a.dout) + (int64_t)qi * a.o_stride + (int64_t)head * D;
+  // this lane's query rows (one per 32-row MFMA column block of the wave)
+  int32_t qi[RB];
+  bool rvalid[RB];
+  int head[RB];
+  bf16x8 qreg[RB][C::KS], dreg[RB][C::KS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int n = (wave * RB + rb) * 32 + ln;
+    const int t = n / G, hg = n % G;
+    head[rb] = g * G + hg;
+    rvalid[rb] = t < qlen;
+    qi[rb] = wi.q_start + (rvalid[rb] ? t : 0);
+    float lse2 = a.lse[(int64_t)qi[rb] * a.hq + head[rb]] * kLog2e;
+    // a row that sees no key (LSE = -inf); tested on the bits, which no
+    // no-NaN assumption of the device compile can fold: exponent all ones
+    if ((__float_as_uint(lse2) & 0x7f800000u) == 0x7f800000u) lse2 = 0.f;
+    const float dl = a.delta[(int64_t)qi[rb] * a.hq + head[rb]];
+    __bf16 qa0, qa1, da0, da1;
+    split_bf16(-lse2 / c, qa0, qa1);
+    split_bf16(-dl, da0, da1);
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q) + (int64_t)qi[rb] * a.q_stride + (int64_t)head[rb] * D;
+    const __bf16* drow = reinterpret_cast<const __bf16*>(a.dout) + (int64_t)qi[rb] * a.o_stride + (int64_t)head[rb] * D;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       const int d0 = 16 * ks + 8 * h;
@@ -151,9 +164,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
         y[0] = da0;
         y[1] = da1;
       }
-      if (!rvalid) x = y = (bf16x8){};
-      qreg[ks] = x;
-      dreg[ks] = y;
+      if (!rvalid[rb]) x = y = (bf16x8){};
+      qreg[rb][ks] = x;
+      dreg[rb][ks] = y;
     }
   }
 
@@ -163,7 +176,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
   int ch_off[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
-    const int ci = tid + j * NT;
+    const int ci = tid + j * NTQ;
     ch_off[j] = (ci / C::CH) * (int)a.kv_stride * 2 + (ci % C::CH) * 16;
   }
   const int32_t kv_row_bytes = (int32_t)a.kv_stride * 2;
@@ -175,7 +188,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vp + elem0), (short)0, nrec, kBufCfg);
 #pragma unroll
     for (int j = 0; j < NCH; ++j)
-      if (tid + j * NT < TK * C::CH) {
+      if (tid + j * NTQ < TK * C::CH) {
         kr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ch_off[j], 0, 0));
         vr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ch_off[j], 0, 0));
       }
@@ -183,7 +196,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
   auto store_tile = [&](int b) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int ci = tid + j * NT;
+      const int ci = tid + j * NTQ;
       if (ci < TK * C::CH) {
         const int r = ci / C::CH, part = ci % C::CH;
         *reinterpret_cast<u32x4*>(&Ks[b][r * C::PITCH + part * 8]) = kr[j];
@@ -196,9 +209,11 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
   const SliceLists lists{a.slices, a.num_slices, a.q_tile_slices, a.num_q_tile_slices};
   constexpr auto key_of0 = [](int i) { return 8 * (i / 4) + (i % 4); };
 
-  f32x16 dq[C::MB];
+  f32x16 dq[RB][C::MB];
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb) dq[mb] = (f32x16){};
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) dq[rb][mb] = (f32x16){};
 
   SliceGeo cg;
   bool have = find_slice(lists, wi.slice_end, (int32_t)a.nk, wi.slice_begin, first_tok, last_tok, cg);
@@ -227,34 +242,43 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
     const __attribute__((address_space(3))) __bf16* Kt = (const __attribute__((address_space(3))) __bf16*)Ks[buf];
 #pragma unroll
     for (int kb = 0; kb < TK / 32; ++kb) {
-      // S'^T = K . Q'^T and dP'^T = V . dO'^T (keys on M, rows on N)
-      f32x16 s = {}, dp = {};
+      // S'^T = K . Q'^T and dP'^T = V . dO'^T (keys on M, rows on N); the K
+      // and V operands are read once for all RB row blocks
+      bf16x8 ka[C::KS], va[C::KS];
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Kb[(kb * 32 + ln) * C::PITCH + 16 * ks + 8 * h]);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vb[(kb * 32 + ln) * C::PITCH + 16 * ks + 8 * h]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dreg[ks], dp, 0, 0, 0);
-      }
-      if (masked) {
-        // keys at block offset >= lim or < lim_lo are hidden from the row
-        const int32_t kb0 = kt + kb * 32 + 4 * h;
-        const int32_t lim = geo_row_end(cg, qi) - kb0;
-        const int32_t lim_lo = (cg.type & MAGI_MASK_INVCAUSAL) ? cg.loff + qi - kb0 : -TK;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (key_of0(i) >= lim || key_of0(i) < lim_lo) s[i] = -INFINITY;
+        ka[ks] = *reinterpret_cast<const bf16x8*>(&Kb[(kb * 32 + ln) * C::PITCH + 16 * ks + 8 * h]);
+        va[ks] = *reinterpret_cast<const bf16x8*>(&Vb[(kb * 32 + ln) * C::PITCH + 16 * ks + 8 * h]);
       }
       // dS^T = P^T * dP'^T, rounded to bf16 in the B-operand layout
-      bf16x8 dsb[2];
+      bf16x8 dsb[RB][2];
 #pragma unroll
-      for (int i2 = 0; i2 < 2; ++i2)
+      for (int rb = 0; rb < RB; ++rb) {
+        f32x16 s = {}, dp = {};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = PRESCALED ? s[8 * i2 + e] : s[8 * i2 + e] * c;
-          dsb[i2][e] = (__bf16)(__builtin_amdgcn_exp2f(x) * dp[8 * i2 + e]);
+        for (int ks = 0; ks < C::KS; ++ks) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[rb][ks], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], dreg[rb][ks], dp, 0, 0, 0);
         }
-      // dQ^T += K^T . dS^T (K^T through the transposed LDS read)
+        if (masked) {
+          // keys at block offset >= lim or < lim_lo are hidden from the row
+          const int32_t kb0 = kt + kb * 32 + 4 * h;
+          const int32_t lim = geo_row_end(cg, qi[rb]) - kb0;
+          const int32_t lim_lo = (cg.type & MAGI_MASK_INVCAUSAL) ? cg.loff + qi[rb] - kb0 : -TK;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (key_of0(i) >= lim || key_of0(i) < lim_lo) s[i] = -INFINITY;
+        }
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = PRESCALED ? s[8 * i2 + e] : s[8 * i2 + e] * c;
+            dsb[rb][i2][e] = (__bf16)(__builtin_amdgcn_exp2f(x) * dp[8 * i2 + e]);
+          }
+      }
+      // dQ^T += K^T . dS^T (K^T through the transposed LDS read, shared by
+      // the row blocks)
 #pragma unroll
       for (int i2 = 0; i2 < 2; ++i2) {
         const int krow = kb * 32 + 16 * i2 + 4 * h + li / 4;
@@ -262,7 +286,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
         for (int mb = 0; mb < C::MB; ++mb) {
           const int dcol = mb * 32 + dgrp + 4 * (li % 4);
           const bf16x8 kt8 = read_tr8(Kt + krow * C::PITCH + dcol, C::PITCH);
-          dq[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt8, dsb[i2], dq[mb], 0, 0, 0);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            dq[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt8, dsb[rb][i2], dq[rb][mb], 0, 0, 0);
         }
       }
     }
@@ -275,8 +301,10 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
   }
 
   // epilogue: dQ = scale * (dQ^T)^T; lane half h holds d = 8 grp + 4 h + r
-  if (rvalid) {
-    __bf16* dqp = reinterpret_cast<__bf16*>(a.dq) + (int64_t)qi * a.q_stride + (int64_t)head * D;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if (!rvalid[rb]) continue;
+    __bf16* dqp = reinterpret_cast<__bf16*>(a.dq) + (int64_t)qi[rb] * a.q_stride + (int64_t)head[rb] * D;
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
@@ -285,7 +313,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_bf16(BwdArgs a) {
         if (d < D) {
           bf16x4 w;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) w[r] = (__bf16)(dq[mb][4 * grp + r] * a.scale);
+          for (int r = 0; r < 4; ++r) w[r] = (__bf16)(dq[rb][mb][4 * grp + r] * a.scale);
           *reinterpret_cast<bf16x4*>(dqp + d) = w;
         }
       }
@@ -798,38 +826,56 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
       (int64_t)r.slot_begin + r.slot_count > a.num_slots)
     return;
   constexpr int Q4 = D / 4;
-  const int n = 2 * r.key_len * Q4;  // (dK | dV, key, 4 channels)
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const int which = i / (r.key_len * Q4), rem = i % (r.key_len * Q4);
-    const int kr = rem / Q4, d = 4 * (rem % Q4);
-    const float* src = a.partial + (int64_t)r.slot_begin * 2 * kKeys * D + (int64_t)which * kKeys * D +
-                       (int64_t)kr * D + d;
-    float4 acc = *reinterpret_cast<const float4*>(src);
-    for (int sl = 1; sl < r.slot_count; ++sl) {
-      const float4 x = *reinterpret_cast<const float4*>(src + (int64_t)sl * 2 * kKeys * D);
-      acc.x += x.x;
-      acc.y += x.y;
-      acc.z += x.z;
-      acc.w += x.w;
+  constexpr int64_t kSlot = 2 * kKeys * D;  // floats per slot
+  constexpr int kAhead = 8;                 // slot loads in flight per thread
+  // one thread per (dK | dV, key, 4 channels) of the tile, spread over
+  // gridDim.y blocks; the parts are added in slot order, whatever the
+  // batching of the loads
+  const int n = 2 * r.key_len * Q4;
+  const int i = blockIdx.y * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int which = i / (r.key_len * Q4), rem = i % (r.key_len * Q4);
+  const int kr = rem / Q4, d = 4 * (rem % Q4);
+  const float* src = a.partial + (int64_t)r.slot_begin * kSlot + (int64_t)which * kKeys * D + (int64_t)kr * D + d;
+  float4 acc = *reinterpret_cast<const float4*>(src);
+  int sl = 1;
+  for (; sl + kAhead <= r.slot_count; sl += kAhead) {
+    float4 x[kAhead];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) x[u] = *reinterpret_cast<const float4*>(src + (int64_t)(sl + u) * kSlot);
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      acc.x += x[u].x;
+      acc.y += x[u].y;
+      acc.z += x[u].z;
+      acc.w += x[u].w;
     }
-    if (which == 0) {
-      acc.x *= a.scale;
-      acc.y *= a.scale;
-      acc.z *= a.scale;
-      acc.w *= a.scale;
-    }
-    T* dst = reinterpret_cast<T*>(which == 0 ? a.dk : a.dv) + (int64_t)(r.key_start + kr) * a.kv_stride +
-             (int64_t)r.kv_group * a.kv_hstride + d;
-    dst[0] = (T)acc.x;
-    dst[1] = (T)acc.y;
-    dst[2] = (T)acc.z;
-    dst[3] = (T)acc.w;
   }
+  for (; sl < r.slot_count; ++sl) {
+    const float4 x = *reinterpret_cast<const float4*>(src + (int64_t)sl * kSlot);
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
+  }
+  if (which == 0) {
+    acc.x *= a.scale;
+    acc.y *= a.scale;
+    acc.z *= a.scale;
+    acc.w *= a.scale;
+  }
+  T* dst = reinterpret_cast<T*>(which == 0 ? a.dk : a.dv) + (int64_t)(r.key_start + kr) * a.kv_stride +
+           (int64_t)r.kv_group * a.kv_hstride + d;
+  dst[0] = (T)acc.x;
+  dst[1] = (T)acc.y;
+  dst[2] = (T)acc.z;
+  dst[3] = (T)acc.w;
 }
 
 template <int D>
 hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
   constexpr int KB = D == 24 ? KB24 : KB48;
+  constexpr int RBQ = D == 24 ? RBQ24 : RBQ48;
   const bool bf = a.dtype == MAGI_DTYPE_BF16;
   const int64_t nvec = a.nq * a.hq;
   if (nvec > 0) {
@@ -845,9 +891,9 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
     if (!bf)
       hipLaunchKernelGGL((bwd_dq_f32<D>), grid, dim3(kThreads32), 0, stream, a);
     else if (pre)
-      hipLaunchKernelGGL((bwd_dq_bf16<D, true>), grid, dim3(NT), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_bf16<D, true, RBQ>), grid, dim3(NT / RBQ), 0, stream, a);
     else
-      hipLaunchKernelGGL((bwd_dq_bf16<D, false>), grid, dim3(NT), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_bf16<D, false, RBQ>), grid, dim3(NT / RBQ), 0, stream, a);
   }
   if (a.num_kwork > 0) {
     const dim3 grid(a.num_kwork);
@@ -859,7 +905,8 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((bwd_dkdv_bf16<D, false, KB>), grid, dim3(2 * kKeys / KB), 0, stream, a);
   }
   if (a.num_reduce > 0) {
-    const dim3 grid(a.num_reduce);
+    // gridDim.y covers the 2 x kKeys x D / 4 float4 outputs of a full tile
+    const dim3 grid(a.num_reduce, (2 * kKeys * (D / 4) + 255) / 256);
     if (bf)
       hipLaunchKernelGGL((bwd_reduce<D, __bf16>), grid, dim3(256), 0, stream, a);
     else
