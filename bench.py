@@ -52,29 +52,42 @@ def masked_flops(wl) -> float:
 CLOCK_GHZ = 2.4   # the clock the published peaks assume (256 CUs, 1024 SIMDs)
 
 
+MFMA_EXP_OVERLAP = 0.41  # measured: MFMA and exp streams overlap by 41 % of the shorter one
+
+
 def ceilings(d: int) -> dict:
-    """The two ceilings of the bf16 forward at head_dim d, in masked TFLOP/s.
+    """The ceilings of the bf16 forward at head_dim d, in masked TFLOP/s at
+    the 2.4 GHz of the published peak.
 
     Per 32-key x 32-row score block of one wave (4 d 1024 useful FLOPs):
     * VALU: 16 v_exp_f32 at half rate (8 issue cycles each; 31 of 64 lanes
       per clock per CU measured) + 8 v_cvt_pk_bf16_f32 (4 cycles each) =
       160 issue cycles of one SIMD, the softmax work that cannot leave it;
     * MFMA: the padded products, ceil(d/16) Q.K steps and 2 x ceil((d+1)/32)
-      P.V steps of v_mfma_f32_32x32x16_bf16 (32768 FLOPs each), of which
-      d / 8 carry the counted work (d = 24: 3 of 4; d = 48: 6 of 7).
+      P.V steps of v_mfma_f32_32x32x16_bf16 (32768 FLOPs, 32 cycles each),
+      of which d / 8 carry the counted work (d = 24: 3 of 4; d = 48: 6 of 7);
+    * co-issue: both on one SIMD, whose MFMA and exp streams overlap by only
+      MFMA_EXP_OVERLAP of the shorter one (the magi_rates probe with half
+      the waves of every SIMD on each): MFMA + VALU - 0.41 min(MFMA, VALU)
+      cycles per block (d = 24: 235.5, d = 48: 318.4).
     """
-    valu = 1024 * CLOCK_GHZ * 1e9 * 4.0 * d * 1024 / 160 / 1e12
+    valu_cyc = 16 * 8 + 8 * 4
     issued = -(-d // 16) + 2 * -(-(d + 1) // 32)
+    mfma_cyc = 32 * issued
+    both_cyc = mfma_cyc + valu_cyc - MFMA_EXP_OVERLAP * min(mfma_cyc, valu_cyc)
+    valu = 1024 * CLOCK_GHZ * 1e9 * 4.0 * d * 1024 / valu_cyc / 1e12
     mfma = PEAK_BF16_TFLOPS * (d / 8.0) / issued
-    return {"valu_tflops": round(valu, 1), "mfma_padded_tflops": round(mfma, 1)}
+    return {"valu_tflops": round(valu, 1), "mfma_padded_tflops": round(mfma, 1),
+            "coissue_tflops": round(mfma * mfma_cyc / both_cyc, 1)}
 
 
 def with_ceilings(rec: dict, tflops: float, d: int) -> dict:
-    """add the fractions of the VALU and padded-MFMA ceilings beside the
-    fraction of the bf16 peak"""
+    """add the fractions of the VALU, padded-MFMA and co-issue ceilings
+    beside the fraction of the bf16 peak"""
     c = ceilings(d)
     rec["frac_of_valu_ceiling"] = round(tflops / c["valu_tflops"], 4)
     rec["frac_of_mfma_padded_ceiling"] = round(tflops / c["mfma_padded_tflops"], 4)
+    rec["frac_of_coissue_ceiling"] = round(tflops / c["coissue_tflops"], 4)
     return rec
 
 
