@@ -273,6 +273,9 @@ int32_t bwd_args(BwdArgs& a, const void* q, const void* k, const void* v, const 
     if ((st = check_layout(t.name, t.p, nk, hkv, kv_tok_stride, kv_head_stride, head_dim, dtype)) != MAGI_OK) return st;
   if (kv_tok_stride >= (int64_t)1 << 23)
     return fail(MAGI_ERR_UNSUPPORTED, "kv row stride %lld >= 2^23 elements", (long long)kv_tok_stride);
+  // the dK/dV pass addresses one Q/dO tile with 32-bit byte offsets
+  if (q_tok_stride >= (int64_t)1 << 23 || o_tok_stride >= (int64_t)1 << 23)
+    return fail(MAGI_ERR_UNSUPPORTED, "q or out row stride >= 2^23 elements");
   if (nq > 0 && lse == nullptr) return fail(MAGI_ERR_INVALID_ARG, "lse is required");
   if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(MAGI_ERR_INVALID_ARG, "lse not 4-byte aligned");
   if (!finite_bits(softmax_scale))

@@ -453,29 +453,40 @@ __global__ __launch_bounds__(2 * kKeys / KB, 2) void bwd_dkdv_bf16(BwdArgs a) {
   }
 
   // Q'/dO' tiles: row n of a tile is (token t0 + n / G, head g G + n % G);
-  // 16-byte chunks of the rows plus, per row, the augmented pairs
+  // 16-byte chunks of the rows plus, per row, the augmented pairs.  A
+  // thread's chunks sit at fixed byte offsets from the tile's first token
+  // (strides below 2^23 elements, checked by the entry point); the loads go
+  // through buffer resources whose range ends with the run's last token, so
+  // rows past it read as zeros without per-lane tests, and chunks of no row
+  // (past the tile, or past tq_rows when G does not divide TQ) stay zero.
   u32x4 qr[NCH], orr[NCH];
+  int32_t q_off[NCH], o_off[NCH];
+  bool ch_row[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int ci = tid + j * NTK;
+    const int row = ci / C::CH, part = ci % C::CH;
+    const int tt = row / G, hh = row % G;
+    ch_row[j] = ci < TQ * C::CH && row < tq_rows;
+    q_off[j] = tt * (int32_t)a.q_stride * 2 + hh * (D * 2) + part * 16;
+    o_off[j] = tt * (int32_t)a.o_stride * 2 + hh * (D * 2) + part * 16;
+    qr[j] = orr[j] = (u32x4){0, 0, 0, 0};
+  }
   __bf16 aq0 = 0, aq1 = 0, ao0 = 0, ao1 = 0;  // augmented values of row tid (tid < TQ)
   auto load_tile = [&](const QRun& r) {
     const int32_t ntok = r.t_end - r.t0 < TQT ? r.t_end - r.t0 : TQT;
+    const __bf16* qb = reinterpret_cast<const __bf16*>(a.q) + (int64_t)r.t0 * a.q_stride + (int64_t)g * G * D;
+    const __bf16* ob = reinterpret_cast<const __bf16*>(a.dout) + (int64_t)r.t0 * a.o_stride + (int64_t)g * G * D;
+    const int32_t qrec = (ntok - 1) * (int32_t)a.q_stride * 2 + G * (D * 2);
+    const int32_t orec = (ntok - 1) * (int32_t)a.o_stride * 2 + G * (D * 2);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)qb, (short)0, qrec, kBufCfg);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)ob, (short)0, orec, kBufCfg);
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int ci = tid + j * NTK;
-      u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-      if (ci < TQ * C::CH) {
-        const int row = ci / C::CH, part = ci % C::CH;
-        const int tt = row / G, hh = row % G;
-        if (row < tq_rows && tt < ntok) {
-          const int64_t tok = r.t0 + tt;
-          x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(a.q) + tok * a.q_stride +
-                                              (int64_t)(g * G + hh) * D + part * 8);
-          y = *reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(a.dout) + tok * a.o_stride +
-                                              (int64_t)(g * G + hh) * D + part * 8);
-        }
+    for (int j = 0; j < NCH; ++j)
+      if (ch_row[j]) {
+        qr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, q_off[j], 0, 0));
+        orr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, o_off[j], 0, 0));
       }
-      qr[j] = x;
-      orr[j] = y;
-    }
     aq0 = aq1 = ao0 = ao1 = (__bf16)0.0f;
     if (tid < tq_rows && tid / G < ntok) {
       const int64_t tok = r.t0 + tid / G;

@@ -486,7 +486,8 @@ int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_slices,
  *              contents needed), for the parts of split key tiles; a last
  *              launch sums them into dk, dv
  * Supported: head_dim 24 or 48; hq % hkv == 0; hq/hkv <= 64;
- * kv_tok_stride < 2^23.  Errors as magi_ffa_fwd.
+ * kv_tok_stride, q_tok_stride and o_tok_stride < 2^23 (MAGI_ERR_UNSUPPORTED
+ * otherwise).  Errors as magi_ffa_fwd.
  */
 int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                      const float* lse, void* dq, void* dk, void* dv, float* delta,

@@ -531,6 +531,10 @@ def test_backward_entry_validates_split_workspace():
     assert bwd(delta=None) == _lib.MAGI_ERR_INVALID_ARG
     assert bwd(kvhs=20) == _lib.MAGI_ERR_INVALID_ARG                    # K/V layout overlaps
     assert b"K/V" in L.magi_last_error() or b"overlap" in L.magi_last_error()
+    # a Q/dO tile of the dK/dV pass would pass 32-bit byte offsets
+    assert bwd(qs=1 << 23) == _lib.MAGI_ERR_UNSUPPORTED
+    assert bwd(os_=1 << 23) == _lib.MAGI_ERR_UNSUPPORTED
+    assert b"2^23" in L.magi_last_error()
 
 
 def test_noalloc_backward_entry_validates_and_bounds_its_scratch():
