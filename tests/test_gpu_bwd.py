@@ -239,6 +239,43 @@ def test_bwd_full_size_magi24b():
     assert err_v <= 1e-2 and err_k <= 1e-2
 
 
+def test_bwd_full_size_varlen():
+    # the packed varlen layer at full size (6 videos of 5-15 chunks x 2400
+    # tokens, 10 chunks at KV range 3, 129,600 tokens, split key tiles):
+    # sampled dQ rows of every video over all heads against the oracle, which
+    # is given only the row's own video (its mask is empty elsewhere), and
+    # per video and KV group the sums that hold at any size when every row
+    # sees a key: sum_k dV[k] over the video's keys = sum of the group's dO
+    # over the video's rows, sum_k dK[k] = 0
+    wl = W.make_workload("varlen")
+    note("bwd full size varlen: inputs")
+    inp = W.make_inputs(wl, 0)
+    dO = torch.from_numpy(rand((wl.nq, wl.hq, wl.head_dim), 51)).to(torch.bfloat16)
+    note("bwd full size varlen: GPU forward + backward")
+    dq, dk, dv, plan = gpu_fwd_bwd(wl, inp, dO)
+    assert plan.num_slots > 0
+    G = wl.hq // wl.hkv
+    rng = np.random.Generator(np.random.PCG64(52))
+    v64 = np64(inp.v)
+    for vi, s in enumerate(wl.seqs):
+        q0, q1 = s.q_offset, s.q_offset + s.num_q_chunks * s.chunk_len
+        k0, k1 = s.k_offset, s.k_offset + s.num_kv_chunks * s.chunk_len
+        rows = np.unique(np.concatenate([[q0, q1 - 1], rng.integers(q0, q1, size=3)])).astype(np.int64)
+        note(f"bwd full size varlen: video {vi} ({s.num_q_chunks} chunks), rows {rows.tolist()}")
+        qn, kn = oracle_prologue(wl, inp, rows)
+        mask = oracle.video_mask(wl.seqs, wl.nq, wl.nk, rows)[:, k0:k1]
+        assert mask.any(axis=1).all()
+        a, _, _ = oracle.attention_backward(qn, kn[k0:k1], v64[k0:k1], np64(dO[rows]), mask, ops.LN2)
+        compare(np64(dq[rows]), a, "bf16", f"dQ video {vi}, sampled rows, all heads")
+        do_sum = dO[q0:q1].double().view(q1 - q0, wl.hkv, G, wl.head_dim).sum(dim=(0, 2)).numpy()
+        dv_sum = dv[k0:k1].double().sum(dim=0).cpu().numpy()
+        dk_sum = dk[k0:k1].double().sum(dim=0).cpu().numpy()
+        err_v = np.linalg.norm(dv_sum - do_sum) / np.linalg.norm(do_sum)
+        err_k = np.abs(dk_sum).max() / dk[k0:k1].double().abs().sum(dim=0).max().item()
+        note(f"video {vi}: sum dV vs sum dO rel {err_v:.3e}; |sum dK| / sum |dK| {err_k:.3e}")
+        assert err_v <= 1e-2 and err_k <= 1e-2
+
+
 def test_bwd_bitwise_deterministic():
     note("bwd determinism")
     d, G, hkv = 24, 16, 2
