@@ -147,6 +147,30 @@ def test_prologue_per_head_gain_in_place_and_strided():
     assert torch.count_nonzero(buf[:, :2]) == 0 and torch.count_nonzero(buf[:, 18:]) == 0
 
 
+@pytest.mark.parametrize("d", [24, 48])
+def test_prologue_more_heads_than_threads(d):
+    # 320 query heads and 40 key heads: a Q token has more heads than a
+    # 256-thread block has threads, so threads take a second vector of the
+    # token (at d = 48 after the first was loaded before the rotation table)
+    note(f"prologue with 320 heads, d={d}")
+    n, hq, hk = 37, 320, 40
+    rng = np.random.Generator(np.random.PCG64(60 + d))
+    q = rng.standard_normal((n, hq, d)).astype(np.float32)
+    k = rng.standard_normal((n, hk, d)).astype(np.float32)
+    gq = rng.uniform(0.8, 1.2, d).astype(np.float32)
+    gk = rng.uniform(0.8, 1.2, d).astype(np.float32)
+    pos = rng.integers(0, 50, (n, 3)).astype(np.int32)
+    base = (1e4, 2e3, 7e2)
+    dv = lambda x: torch.from_numpy(x).to(DEV)
+    qd, kd = dv(q).to(torch.bfloat16), dv(k).to(torch.bfloat16)
+    qh, kh = ops.qknorm_rope(qd, kd, dv(gq), dv(gk), dv(pos), dv(pos),
+                             torch.tensor(base, dtype=torch.float32, device=DEV), 1e-6)
+    torch.cuda.synchronize()
+    inv = oracle.rope_inv_freq(base, d)
+    compare(np64(qh), oracle.rope_3d(oracle.qk_norm(np64(qd), gq, 1e-6), pos, inv), "bf16", "q_hat")
+    compare(np64(kh), oracle.rope_3d(oracle.qk_norm(np64(kd), gk, 1e-6), pos, inv), "bf16", "k_hat")
+
+
 # --------------------------------------------------------------------------- attention alone
 
 def ffa_case(q, k, v, slices, kind, scale=None, check_lse=True, knm=None):
