@@ -190,7 +190,7 @@ def run_gpu(wl, steps, warmup, seed=0, window=None):
             # the wait for the plan upload (a side stream) goes before the
             # start event, so that the events bracket the attention kernel
             # alone; the step time still includes it
-            stream.wait_event(plan.ready)
+            plan.wait(stream)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
         ops.ffa_fwd(qh, kh, vh, plan, out=out, lse=lse, softmax_scale=ops.LN2, k_norm_max=knm)
@@ -238,7 +238,7 @@ def run_backward(wl, steps, warmup, seed=0):
 
     def step(rec):
         if rec:
-            stream.wait_event(plan.ready)  # the upload wait stays outside the kernels' events
+            plan.wait(stream)  # the upload wait stays outside the kernels' events
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
         ops.ffa_bwd(qh, kh, vh, out, dout, lse, plan, softmax_scale=ops.LN2, dq=dq, dk=dk, dv=dv)
@@ -291,7 +291,7 @@ def run_cross(wl, steps, warmup, seed=0):
             # the wait for the plan upload (a side stream) goes before the
             # start event, so that the events bracket the attention kernel
             # alone; the step time still includes it
-            stream.wait_event(plan.ready)
+            plan.wait(stream)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
         ops.ffa_fwd(qh, kh, vh, plan, out=out, lse=lse, softmax_scale=ops.LN2, k_norm_max=knm)
@@ -477,7 +477,7 @@ def run_ring(steps, warmup, seed=0):
                             v_out=ring_v[s0 * C:(s0 + m) * C])
             done += m
         if record:
-            stream.wait_event(plan.ready)  # the upload wait stays outside the kernel's events
+            plan.wait(stream)  # the upload wait stays outside the kernel's events
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
         # the bound on key norms follows from the QK-Norm gains, so it holds

@@ -202,10 +202,18 @@ class Plan:
     kitem_ext: Optional[torch.Tensor] = None    # {partial slot or -1, token window} per key-major item
     kreduce: Optional[torch.Tensor] = None      # int32 [r, 5] sums of split key tiles
     num_slots: int = 0
+    waited: list = field(default_factory=list)  # streams already ordered after ``ready``
 
     @property
     def num_work(self) -> int:
         return int(self.host["work"].shape[0])
+
+    def wait(self, stream) -> None:
+        """Order ``stream`` after the plan's upload, once per stream (later
+        work on a stream that has waited is ordered after the upload too)."""
+        if self.ready is not None and not any(s == stream for s in self.waited):
+            stream.wait_event(self.ready)
+            self.waited.append(stream)
 
     def settle(self) -> "Plan":
         """Wait on the host for the plan's upload and drop its event, so that
@@ -436,8 +444,7 @@ def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
     _check_3d("out", out, hq, d)
     if lse is None and return_lse:
         lse = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
-    if plan.ready is not None:
-        torch.cuda.current_stream(q.device).wait_event(plan.ready)
+    plan.wait(torch.cuda.current_stream(q.device))
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q.shape[0], k.shape[0], hq, hkv, d,
             dtype_code(q.dtype), q.stride(0), k.stride(0), k.stride(1), out.stride(0),
             0.0 if softmax_scale is None else float(softmax_scale), _ptr(k_norm_max),
@@ -504,8 +511,7 @@ def ffa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor
     # partial sums of split key tiles: 2 x 128 keys x d fp32 per slot
     nfl = plan.num_slots * 2 * 128 * d
     partial = torch.empty(max(nfl, 4), dtype=torch.float32, device=q.device)
-    if plan.ready is not None:
-        torch.cuda.current_stream(q.device).wait_event(plan.ready)
+    plan.wait(torch.cuda.current_stream(q.device))
     check(lib().magi_ffa_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
         q.shape[0], k.shape[0], hq, k.shape[1], d, dtype_code(q.dtype), q.stride(0), k.stride(0), k.stride(1),
@@ -521,8 +527,7 @@ def ffa_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     static device scratch; the gradients go into the caller's dq, dk, dv and
     nothing is allocated (the plan must already be on the device)."""
     _bwd_common(q, k, v, out, dout, lse, plan, dq, dk, dv)
-    if plan.ready is not None:
-        torch.cuda.current_stream(q.device).wait_event(plan.ready)
+    plan.wait(torch.cuda.current_stream(q.device))
     check(lib().magi_ffa_bwd_noalloc(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
         q.shape[0], k.shape[0], q.shape[1], k.shape[1], q.shape[-1], dtype_code(q.dtype), q.stride(0), k.stride(0),
