@@ -609,6 +609,45 @@ def test_end_to_end_stream():
     sampled_forward_parity("stream", 256)
 
 
+def test_streaming_ring_cache_full_size():
+    # the streaming layer (4 in-flight chunks of 3600 tokens over 24 chunks of
+    # keys, 128/8 heads, d = 48) with its keys and values in a 24-slot ring
+    # holding global chunks 100..123, so the ring wraps inside the in-flight
+    # chunks: every chunk written into its slot by the prologue, the key-norm
+    # bound passed, FULL slices over the ring; sampled rows against the oracle
+    # of the same chunks in linear order
+    wl = W.make_workload("stream")
+    C, S, first, n = 3600, 24, 100, 4
+    note("streaming ring cache full size: inputs")
+    inp = W.make_inputs(wl, 0)
+    d = dev_inputs(wl, inp)
+    ring_k = ops.kv_group_major(S * C, wl.hkv, wl.head_dim, torch.bfloat16)
+    ring_v = ops.kv_group_major(S * C, wl.hkv, wl.head_dim, torch.bfloat16)
+    knm = torch.empty(wl.hkv, dtype=torch.float32, device=DEV)
+    kscale = wl.softmax_scale * ops.LOG2E
+    j = 0
+    for s0, m in ops.ring_slot_runs(S, first, S):   # linear chunk j holds global chunk first + j
+        ops.qknorm_rope(d["q"][:1], d["k"][j * C:(j + m) * C], d["gq"], d["gk"], d["pq"][:1],
+                        d["pk"][j * C:(j + m) * C], d["base"], wl.eps, q_out=torch.empty_like(d["q"][:1]),
+                        k_out=ring_k[s0 * C:(s0 + m) * C], k_scale=kscale, k_norm_max=knm,
+                        v=d["v"][j * C:(j + m) * C], v_out=ring_v[s0 * C:(s0 + m) * C])
+        j += m
+    qh, _ = ops.qknorm_rope(d["q"], None, d["gq"], None, d["pq"], None, d["base"], wl.eps)
+    sl = ops.build_ring_slices(C, S, first, S, n)
+    plan = ops.make_plan(sl, n * C, S * C, wl.hq, wl.hkv, wl.head_dim, torch.bfloat16)
+    note("streaming ring cache full size: GPU run")
+    O, L = ops.ffa_fwd(qh, ring_k, ring_v, plan, softmax_scale=ops.LN2, k_norm_max=knm)
+    torch.cuda.synchronize()
+    rows = W.sample_rows(wl, 96, 3)
+    note(f"streaming ring cache full size: oracle on {len(rows)} rows")
+    mask = oracle.video_mask(wl.seqs, wl.nq, wl.nk, rows)
+    Ow, Lw = oracle.forward(np64(inp.q[rows]), np64(inp.k), np64(inp.v), np64(inp.gain_q), np64(inp.gain_k),
+                            inp.pos_q[rows].numpy(), inp.pos_k.numpy(), wl.rope_base, wl.eps, mask, wl.softmax_scale)
+    compare(np64(O[rows]), Ow, "bf16")
+    compare(np64(L[rows]), Lw, "bf16", "LSE")
+    assert not torch.isnan(O).any()
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_end_to_end_varlen(seed):
     # the seed also draws the videos' chunk counts and range-limited chunks
