@@ -725,6 +725,38 @@ def test_window_packing_equals_separate_sequences_gpu():
 
 # --------------------------------------------------------------------------- cross-attention
 
+@pytest.mark.parametrize("name", ["magi4.5b", "magi24b"])
+def test_cross_attention_full_size(name):
+    # the layer's video tokens over 800 condition tokens, run as the
+    # benchmark runs it (QK-Norm on both sides without rotation, the softmax
+    # scale folded into K, K and V group-major, the key-norm bound): sampled
+    # rows over all heads against the oracle
+    wl = W.make_workload(name)
+    T = 800
+    note(f"cross-attention full size {name}")
+    q, k, v = rand((wl.nq, wl.hq, wl.head_dim), 70), rand((T, wl.hkv, wl.head_dim), 71), rand((T, wl.hkv, wl.head_dim), 72)
+    gq = np.random.Generator(np.random.PCG64(73)).uniform(0.8, 1.2, wl.head_dim).astype(np.float32)
+    gk = np.random.Generator(np.random.PCG64(74)).uniform(0.8, 1.2, wl.head_dim).astype(np.float32)
+    qd, kd, vd = (torch.from_numpy(x).to(torch.bfloat16).to(DEV) for x in (q, k, v))
+    zq = torch.zeros((wl.nq, 3), dtype=torch.int32, device=DEV)
+    zk = torch.zeros((T, 3), dtype=torch.int32, device=DEV)
+    base = torch.tensor(wl.rope_base, dtype=torch.float32, device=DEV)
+    knm = torch.empty(wl.hkv, dtype=torch.float32, device=DEV)
+    qh, kh, vh = ops.qknorm_rope(qd, kd, torch.from_numpy(gq).to(DEV), torch.from_numpy(gk).to(DEV), zq, zk, base,
+                                 wl.eps, k_out=ops.kv_group_major(T, wl.hkv, wl.head_dim, torch.bfloat16),
+                                 k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm, v=vd)
+    plan = ops.make_plan(ops.build_cross_slices([(0, wl.nq, 0, T)]), wl.nq, T, wl.hq, wl.hkv, wl.head_dim,
+                         torch.bfloat16)
+    O, L = ops.ffa_fwd(qh, kh, vh, plan, softmax_scale=ops.LN2, k_norm_max=knm)
+    torch.cuda.synchronize()
+    rows = W.sample_rows(wl, 64, 5)
+    Ow, Lw = oracle.forward(np64(qd[rows]), np64(kd), np64(vd), gq.astype(np.float64), gk.astype(np.float64),
+                            np.zeros((len(rows), 3), np.int32), np.zeros((T, 3), np.int32), wl.rope_base, wl.eps,
+                            np.ones((len(rows), T), bool), wl.softmax_scale)
+    compare(np64(O[rows]), Ow, "bf16")
+    compare(np64(L[rows]), Lw, "bf16", "LSE")
+
+
 @pytest.mark.parametrize("group_major", [False, True])
 def test_cross_attention_packed_samples(group_major):
     # the parallel block's cross-attention: each sample's video tokens see its
