@@ -506,10 +506,20 @@ extern "C" int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_s
       reduce[r++] = {(int32_t)t.k0, (int32_t)t.len, g, slot + g * u.nparts, u.nparts};
     slot += u.nparts * hkv;
   }
-  // heaviest units first; ties keep key order (deterministic)
+  // heaviest units first.  Ties (most parts of split tiles cost the same)
+  // go window by window, key tiles in key order within a window: the units
+  // that run side by side then walk the same query rows, so each Q/dO tile
+  // is fetched once into the L2 of an XCD (a KV group's items share one XCD)
+  // and served from there to the other units.  Deterministic.
   std::vector<size_t> ord(units.size());
   std::iota(ord.begin(), ord.end(), 0);
-  std::stable_sort(ord.begin(), ord.end(), [&](size_t x, size_t y) { return units[x].cost > units[y].cost; });
+  std::stable_sort(ord.begin(), ord.end(), [&](size_t x, size_t y) {
+    const Unit& ux = units[x];
+    const Unit& uy = units[y];
+    if (ux.cost != uy.cost) return ux.cost > uy.cost;
+    if (ux.lo != uy.lo) return ux.lo < uy.lo;
+    return ux.tile < uy.tile;
+  });
   int32_t w = 0;
   for (size_t rank = 0; rank < ord.size(); ++rank) {
     const Unit& u = units[ord[rank]];

@@ -190,7 +190,8 @@ def check_schedule_kv(slices, nq, nk, hq, hkv, d, dtype=_lib.DTYPE_BF16, tile_k=
     """Key-major schedule: every (key, group) owned once -- by a direct item
     or by a reduce entry whose parts are items --, each owner's slices
     reproduce the mask's columns over its keys, costs are the visible pairs,
-    heaviest first with the groups interleaved, deterministic."""
+    heaviest first (equal costs token window by window, keys ascending within
+    a window) with the groups interleaved, deterministic."""
     work, ts, ext, red, nslots = ops.schedule_kv(slices, nq, nk, hq, hkv, d, dtype, tile_k)
     slot, wlo, whi = ext[:, 0], ext[:, 1], ext[:, 2]
     tk = tile_k or 128
@@ -262,6 +263,10 @@ def check_schedule_kv(slices, nq, nk, hq, hkv, d, dtype=_lib.DTYPE_BF16, tile_k=
     assert sum(int(c) for c in red[:, 4]) == nslots if len(red) else nslots == 0
     assert (owner >= 0).all(), "a (key, group) has no owner"
     assert (np.diff(work[::hkv, 5]) <= 0).all(), "not heaviest-first"
+    u, ulo = work[::hkv], wlo[::hkv]
+    for x in range(len(u) - 1):
+        if u[x, 5] == u[x + 1, 5]:
+            assert (ulo[x], u[x, 0]) <= (ulo[x + 1], u[x + 1, 0]), "equal-cost units not window by window"
     for r in range(len(work) // hkv):
         np.testing.assert_array_equal(work[r * hkv:(r + 1) * hkv, 4], np.arange(hkv))
     again = ops.schedule_kv(slices, nq, nk, hq, hkv, d, dtype, tile_k)
