@@ -64,7 +64,11 @@ struct BCfg {
   // in disjoint banks; the transposed reads then see at most 2-way conflicts
   static constexpr int PITCH = 72;
   static constexpr int CH = D / 8;  // 16-byte chunks per row
-  static_assert(DA <= PITCH && D % 8 == 0, "layout");
+  // Q'/dO' tiles of the dK/dV pass filled by direct loads: 16-byte slots
+  // per row (odd, so the 16 rows of a b128 row read fall in disjoint banks;
+  // at least DM / 8 for the transposed reads)
+  static constexpr int NC = 9;
+  static_assert(DA <= PITCH && D % 8 == 0 && 8 * NC >= DM && NC % 2 == 1, "layout");
 };
 
 // bf16 high and low parts of x (x = hi + lo to about 2^-16 relative)
@@ -381,15 +385,42 @@ __device__ __forceinline__ bool find_qrun(const SliceLists& L, int32_t slice_end
 // kKeys / (32 KB) waves; KB = 2 lets one wave's Q'/dO' operand reads (and
 // their transposes) serve 64 keys, halving those LDS reads per key.
 template <int D, bool PRESCALED, int KB>
-__global__ __launch_bounds__(2 * kKeys / KB, 2) void bwd_dkdv_bf16(BwdArgs a) {
+__global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16(BwdArgs a) {
   using C = BCfg<D>;
   constexpr int NTK = 2 * kKeys / KB;                // threads per workgroup
-  constexpr int NCH = (TQ * C::CH + NTK - 1) / NTK;  // 16-byte chunks per thread per tile (Q and dO each)
-  __shared__ __attribute__((aligned(16))) __bf16 Qs[2][TQ * C::PITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 Os[2][TQ * C::PITCH];
+  // Two ways to stage the Q'/dO' tiles of TQ rows in LDS:
+  //  * head_dim 48 (DMA): three buffers filled straight from global memory
+  //    (buffer loads with an LDS destination) two tiles ahead of the tile
+  //    being computed, so no registers stage them.  Such a load writes each
+  //    lane's 16 bytes to consecutive LDS addresses: a tile row is NC 16-byte
+  //    slots, of which the first D / 8 receive data and the others zeros, and
+  //    one load fills 64 consecutive slots.  The two augmented columns of a
+  //    row (Q': -LSE2/c, dO': -delta, each a bf16 high and low part) live in
+  //    small arrays of their own, written by threads.  30.8 against 32.0 ms
+  //    for the pass on a 24B-shaped layer.
+  //  * head_dim 24: two buffers, the next tile loaded into registers while
+  //    this one is computed and stored with its augmented columns at the
+  //    end.  The direct loads measured 12 % slower here: the pass runs at 3
+  //    waves per SIMD on the edge of its register budget, and their longer
+  //    loop (more scalar work, spills to lanes) costs more than it hides.
+  constexpr bool DMA = D >= 48;
+  constexpr int NC = C::NC;
+  constexpr int QP = DMA ? 8 * NC : C::PITCH;  // tile row pitch (elements)
+  constexpr int NW = NTK / 64;                 // waves
+  constexpr int NLD = 2 * NC;                  // DMA: loads per tile, Q' slots then dO' slots
+  constexpr int LPW = (NLD + NW - 1) / NW;     // DMA: loads per wave
+  constexpr int NCH = (TQ * C::CH + NTK - 1) / NTK;  // registers: 16-byte chunks per thread (Q' and dO' each)
+  __shared__ __attribute__((aligned(16))) __bf16 Qs[DMA ? 3 : 2][TQ * QP];
+  __shared__ __attribute__((aligned(16))) __bf16 Os[DMA ? 3 : 2][TQ * QP];
+  __shared__ uint32_t Qa[DMA ? 3 : 1][TQ], Oa[DMA ? 3 : 1][TQ];
+  // DMA: target of the loads past NLD.  Every wave issues LPW loads per
+  // tile, so the number in flight is the same in every wave and on every
+  // path, and the wait-count bookkeeping stays exact.
+  __shared__ __attribute__((aligned(16))) __bf16 Spare[DMA ? 64 * 8 : 8];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the loads branch per wave
   const int h = lane >> 5, ln = lane & 31, li = lane & 15;
   const int dgrp = ((lane >> 4) & 1) * 16;
   const magi_work_item wi = load_item(a.kwork, blockIdx.x);
@@ -415,14 +446,16 @@ __global__ __launch_bounds__(2 * kKeys / KB, 2) void bwd_dkdv_bf16(BwdArgs a) {
   const int32_t ginv = ((1 << 16) + G - 1) / G;
   const int tq_rows = TQT * G;
 
-  // zero padding columns D+2.. of both buffers once; columns D, D+1 are
-  // rewritten with each tile's augmented values
-  for (int b = 0; b < 2; ++b)
-    for (int i = tid; i < TQ * (C::DA - D - 2); i += NTK) {
-      const int col = D + 2 + i % (C::DA - D - 2), row = i / (C::DA - D - 2);
-      Qs[b][row * C::PITCH + col] = (__bf16)0.0f;
-      Os[b][row * C::PITCH + col] = (__bf16)0.0f;
-    }
+  if constexpr (!DMA) {
+    // zero padding columns D+2.. of both buffers once; columns D, D+1 are
+    // rewritten with each tile's augmented values
+    for (int b = 0; b < 2; ++b)
+      for (int i = tid; i < TQ * (C::DA - D - 2); i += NTK) {
+        const int col = D + 2 + i % (C::DA - D - 2), row = i / (C::DA - D - 2);
+        Qs[b][row * QP + col] = (__bf16)0.0f;
+        Os[b][row * QP + col] = (__bf16)0.0f;
+      }
+  }
 
   // this lane's keys (column n of the MFMA, one per key block): K and V
   // rows as B operands with the two ones columns that meet the augmented slots
@@ -452,7 +485,7 @@ __global__ __launch_bounds__(2 * kKeys / KB, 2) void bwd_dkdv_bf16(BwdArgs a) {
     }
   }
 
-  // Q'/dO' tiles: row n of a tile is (token t0 + n / G, head g G + n % G);
+  // Registers: row n of a tile is (token t0 + n / G, head g G + n % G);
   // 16-byte chunks of the rows plus, per row, the augmented pairs.  A
   // thread's chunks sit at fixed byte offsets from the tile's first token
   // (strides below 2^23 elements, checked by the entry point); the loads go
@@ -503,17 +536,95 @@ __global__ __launch_bounds__(2 * kKeys / KB, 2) void bwd_dkdv_bf16(BwdArgs a) {
       const int ci = tid + j * NTK;
       if (ci < TQ * C::CH) {
         const int row = ci / C::CH, part = ci % C::CH;
-        *reinterpret_cast<u32x4*>(&Qs[b][row * C::PITCH + part * 8]) = qr[j];
-        *reinterpret_cast<u32x4*>(&Os[b][row * C::PITCH + part * 8]) = orr[j];
+        *reinterpret_cast<u32x4*>(&Qs[b][row * QP + part * 8]) = qr[j];
+        *reinterpret_cast<u32x4*>(&Os[b][row * QP + part * 8]) = orr[j];
       }
     }
     if (tid < TQ) {
-      Qs[b][tid * C::PITCH + D] = aq0;
-      Qs[b][tid * C::PITCH + D + 1] = aq1;
-      Os[b][tid * C::PITCH + D] = ao0;
-      Os[b][tid * C::PITCH + D + 1] = ao1;
+      Qs[b][tid * QP + D] = aq0;
+      Qs[b][tid * QP + D + 1] = aq1;
+      Os[b][tid * QP + D] = ao0;
+      Os[b][tid * QP + D + 1] = ao1;
     }
   };
+
+  // DMA: load k of this wave (load index I = wave + NW k) fills the 64 slots
+  // from 64 (I mod NC) of the Q' (I < NC) or dO' tile; slot s is row s / NC
+  // (token t0 + row / G, head g G + row % G), chunk s % NC.  A lane's byte
+  // offset from the tile's first token is fixed (strides below 2^23
+  // elements, checked by the entry point); the loads go through buffer
+  // resources whose range ends with the tile's last token, so rows past it
+  // read as zeros, and slots of no data (chunks >= D / 8, rows past
+  // tq_rows when G does not divide TQ) take an offset past any range.
+  constexpr int32_t kPastRange = 0x7ffffff0;
+  int32_t ld_off[LPW];
+#pragma unroll
+  for (int k = 0; k < LPW; ++k) {
+    const int I = wave + NW * k;
+    const bool isq = I < NC;
+    const int sl = 64 * (isq ? I : I - NC) + lane;
+    const int row = sl / NC, part = sl % NC;
+    const int32_t stride2 = (isq ? (int32_t)a.q_stride : (int32_t)a.o_stride) * 2;
+    ld_off[k] = I < NLD && part < C::CH && row < tq_rows ? (row / G) * stride2 + (row % G) * (D * 2) + part * 16
+                                                         : kPastRange;
+  }
+  auto issue_tile = [&](const QRun& r, int b) {
+    const int32_t ntok = r.t_end - r.t0 < TQT ? r.t_end - r.t0 : TQT;
+    const __bf16* qb = reinterpret_cast<const __bf16*>(a.q) + (int64_t)r.t0 * a.q_stride + (int64_t)g * G * D;
+    const __bf16* ob = reinterpret_cast<const __bf16*>(a.dout) + (int64_t)r.t0 * a.o_stride + (int64_t)g * G * D;
+    const int32_t qrec = (ntok - 1) * (int32_t)a.q_stride * 2 + G * (D * 2);
+    const int32_t orec = (ntok - 1) * (int32_t)a.o_stride * 2 + G * (D * 2);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)qb, (short)0, qrec, kBufCfg);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)ob, (short)0, orec, kBufCfg);
+#pragma unroll
+    for (int k = 0; k < LPW; ++k) {
+      const int I = wave + NW * k;
+      __bf16* dst = I < NC ? &Qs[b][I * 64 * 8] : (I < NLD ? &Os[b][(I - NC) * 64 * 8] : Spare);
+      load_lds16(I < NC ? rq : ro, dst, ld_off[k]);
+    }
+  };
+  // augmented values of row tid (tid < TQ) of a tile: loaded when its slots
+  // are issued, written to LDS at the end of the tile being computed
+  float aug_lse = 0.f, aug_delta = 0.f;
+  bool aug_ok = false;
+  auto load_aug = [&](const QRun& r) {
+    const int32_t ntok = r.t_end - r.t0 < TQT ? r.t_end - r.t0 : TQT;
+    aug_ok = tid < tq_rows && tid / G < ntok;
+    if (aug_ok) {
+      const int64_t idx = ((int64_t)r.t0 + tid / G) * a.hq + g * G + tid % G;
+      aug_lse = a.lse[idx];
+      aug_delta = a.delta[idx];
+    }
+  };
+  auto store_aug = [&](int b) {
+    if (tid < TQ) {
+      __bf16 q0 = 0, q1 = 0, o0 = 0, o1 = 0;
+      if (aug_ok) {
+        float l2 = aug_lse * kLog2e;
+        if ((__float_as_uint(l2) & 0x7f800000u) == 0x7f800000u) l2 = 0.f;  // no key: -inf (bit test)
+        split_bf16(-l2 * cinv, q0, q1);
+        split_bf16(-aug_delta, o0, o1);
+      }
+      Qa[b][tid] = (uint32_t)__builtin_bit_cast(unsigned short, q0) | ((uint32_t)__builtin_bit_cast(unsigned short, q1) << 16);
+      Oa[b][tid] = (uint32_t)__builtin_bit_cast(unsigned short, o0) | ((uint32_t)__builtin_bit_cast(unsigned short, o1) << 16);
+    }
+  };
+  // End of a tile: this wave's LPW loads of the tile after next may stay in
+  // flight (issued last, so they are the youngest vmcnt entries), all older
+  // ones (the next tile's slots) must have landed; then the barrier makes
+  // every wave's slots and augmented values visible.  A plain s_barrier: a
+  // release fence would wait for the young loads too.
+  auto end_tile = [&](bool pending) {
+    // s_waitcnt: vmcnt(n) in bits 3:0, expcnt 7 (no wait), lgkmcnt(0)
+    if (pending)
+      __builtin_amdgcn_s_waitcnt(0x70 | LPW);
+    else
+      __builtin_amdgcn_s_waitcnt(0x70);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+  };
+  static_assert(LPW <= 15, "vmcnt field");
   auto next_run = [&](const QRun& r, QRun& n) {
     n = r;
     n.t0 = r.t0 + TQT;
@@ -528,20 +639,45 @@ __global__ __launch_bounds__(2 * kKeys / KB, 2) void bwd_dkdv_bf16(BwdArgs a) {
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) dk[kb][mb] = dv[kb][mb] = (f32x16){};
 
-  QRun cur;
+  QRun cur, nxt;
   find_qrun(SliceLists{a.slices, a.num_slices, a.k_tile_slices, a.num_k_tile_slices}, wi.slice_end, (int32_t)a.nq,
             (int32_t)a.nk, wi.slice_begin, k0, k1, w_lo, w_hi, cur);
-  if (cur.valid) {
-    load_tile(cur);
-    store_tile(0);
+  if constexpr (DMA) {
+    next_run(cur, nxt);
+    if (cur.valid) issue_tile(cur, 0);
+    if (nxt.valid) issue_tile(nxt, 1);
+    if (cur.valid) {
+      load_aug(cur);
+      store_aug(0);
+    }
+    if (nxt.valid) {
+      load_aug(nxt);
+      store_aug(1);
+    }
+    end_tile(false);
+  } else {
+    if (cur.valid) {
+      load_tile(cur);
+      store_tile(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  lds_barrier();
   int buf = 0;
   while (cur.valid) {
-    QRun nxt;
-    next_run(cur, nxt);
-    if (nxt.valid) load_tile(nxt);  // in flight while this tile is computed
+    QRun nx2;
+    int buf2 = 0;
+    if constexpr (DMA) {
+      next_run(nxt, nx2);
+      buf2 = buf == 0 ? 2 : buf - 1;  // (buf + 2) mod 3
+      if (nx2.valid) {
+        load_aug(nx2);
+        issue_tile(nx2, buf2);  // in flight during this tile and the next
+      }
+    } else {
+      next_run(cur, nxt);
+      if (nxt.valid) load_tile(nxt);  // in flight while this tile is computed
+    }
     const int32_t ntok = cur.t_end - cur.t0 < TQT ? cur.t_end - cur.t0 : TQT;
     // every element visible: the item's keys inside the slice's key range,
     // a whole tile of rows, the tile's first token already seeing the item's
@@ -552,6 +688,8 @@ __global__ __launch_bounds__(2 * kKeys / KB, 2) void bwd_dkdv_bf16(BwdArgs a) {
                       (!(cur.type & MAGI_MASK_INVCAUSAL) || k0 >= cur.loff + cur.t0 + TQT - 1);
     const __bf16* Qb = Qs[buf];
     const __bf16* Ob = Os[buf];
+    const uint32_t* Qab = Qa[buf];
+    const uint32_t* Oab = Oa[buf];
     const __attribute__((address_space(3))) __bf16* Qt = (const __attribute__((address_space(3))) __bf16*)Qs[buf];
     const __attribute__((address_space(3))) __bf16* Ot = (const __attribute__((address_space(3))) __bf16*)Os[buf];
 #pragma unroll
@@ -563,8 +701,26 @@ __global__ __launch_bounds__(2 * kKeys / KB, 2) void bwd_dkdv_bf16(BwdArgs a) {
       for (int kb = 0; kb < KB; ++kb) s[kb] = dp[kb] = (f32x16){};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qb[(rb * 32 + ln) * C::PITCH + 16 * ks + 8 * h]);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&Ob[(rb * 32 + ln) * C::PITCH + 16 * ks + 8 * h]);
+        // columns 16 ks + 8 h .. + 7: tile data below D, the augmented pair
+        // at D, D + 1 (DMA: from its own array), zeros above
+        const int row = rb * 32 + ln;
+        bf16x8 qa, oa;
+        if (!DMA || 16 * ks + 16 <= D) {
+          qa = *reinterpret_cast<const bf16x8*>(&Qb[row * QP + 16 * ks + 8 * h]);
+          oa = *reinterpret_cast<const bf16x8*>(&Ob[row * QP + 16 * ks + 8 * h]);
+        } else {
+          const bf16x8 qaug = __builtin_bit_cast(bf16x8, (u32x4){Qab[row], 0u, 0u, 0u});
+          const bf16x8 oaug = __builtin_bit_cast(bf16x8, (u32x4){Oab[row], 0u, 0u, 0u});
+          if (16 * ks + 8 == D) {  // lane half 0 data, half 1 the augmented pair
+            const bf16x8 qd = *reinterpret_cast<const bf16x8*>(&Qb[row * QP + 16 * ks]);
+            const bf16x8 od = *reinterpret_cast<const bf16x8*>(&Ob[row * QP + 16 * ks]);
+            qa = h ? qaug : qd;
+            oa = h ? oaug : od;
+          } else {  // 16 ks == D: half 0 the augmented pair, half 1 zeros
+            qa = h ? (bf16x8){} : qaug;
+            oa = h ? (bf16x8){} : oaug;
+          }
+        }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[kb][ks], s[kb], 0, 0, 0);
@@ -620,8 +776,8 @@ __global__ __launch_bounds__(2 * kKeys / KB, 2) void bwd_dkdv_bf16(BwdArgs a) {
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb) {
           const int dcol = mb * 32 + dgrp + 4 * (li % 4);
-          const bf16x8 ot8 = read_tr8(Ot + qrow * C::PITCH + dcol, C::PITCH);
-          const bf16x8 qt8 = read_tr8(Qt + qrow * C::PITCH + dcol, C::PITCH);
+          const bf16x8 ot8 = read_tr8(Ot + qrow * QP + dcol, QP);
+          const bf16x8 qt8 = read_tr8(Qt + qrow * QP + dcol, QP);
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
             dv[kb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot8, pb[kb][i2], dv[kb][mb], 0, 0, 0);
@@ -630,10 +786,18 @@ __global__ __launch_bounds__(2 * kKeys / KB, 2) void bwd_dkdv_bf16(BwdArgs a) {
         }
       }
     }
-    if (nxt.valid) store_tile(buf ^ 1);
-    lds_barrier();
-    cur = nxt;
-    buf ^= 1;
+    if constexpr (DMA) {
+      if (nx2.valid) store_aug(buf2);
+      end_tile(nx2.valid);
+      cur = nxt;
+      nxt = nx2;
+      buf = buf == 2 ? 0 : buf + 1;
+    } else {
+      if (nxt.valid) store_tile(buf ^ 1);
+      lds_barrier();
+      cur = nxt;
+      buf ^= 1;
+    }
   }
 
   // epilogue: lane (key) holds d = mb 32 + 8 grp + 4 h + r of dK^T / dV^T.
