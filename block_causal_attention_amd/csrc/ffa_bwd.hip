@@ -251,8 +251,16 @@ __global__ __launch_bounds__(NT / RB, RB == 2 && D == 24 ? 3 : 2) void bwd_dq_bf
       bf16x8 ka[C::KS], va[C::KS];
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        ka[ks] = *reinterpret_cast<const bf16x8*>(&Kb[(kb * 32 + ln) * C::PITCH + 16 * ks + 8 * h]);
-        va[ks] = *reinterpret_cast<const bf16x8*>(&Vb[(kb * 32 + ln) * C::PITCH + 16 * ks + 8 * h]);
+        if (16 * ks >= D) {
+          // a step of padding columns only (head_dim 48: 48..63): the two
+          // ones columns in lane half 0, zeros elsewhere, as in the buffers
+          bf16x8 ones = {};
+          ones[0] = ones[1] = (__bf16)1.0f;
+          ka[ks] = va[ks] = h ? (bf16x8){} : ones;
+        } else {
+          ka[ks] = *reinterpret_cast<const bf16x8*>(&Kb[(kb * 32 + ln) * C::PITCH + 16 * ks + 8 * h]);
+          va[ks] = *reinterpret_cast<const bf16x8*>(&Vb[(kb * 32 + ln) * C::PITCH + 16 * ks + 8 * h]);
+        }
       }
       // dS^T = P^T * dP'^T, rounded to bf16 in the B-operand layout
       bf16x8 dsb[RB][2];
