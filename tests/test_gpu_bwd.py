@@ -316,6 +316,40 @@ def test_bwd_group_major_kv_identical(d):
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("d", [24, 48])
+@pytest.mark.parametrize("G", [16, 3])
+def test_bwd_strided_rows_identical(d, G):
+    # Q, O, dO and dQ as views into wider rows (token stride above heads x d,
+    # as for a fused projection): only addressing changes, so outputs and
+    # gradients equal the contiguous run's bit for bit.  G = 3 leaves the
+    # last row of every 64-row Q/dO tile of the dK/dV pass empty.
+    note(f"bwd row-strided Q/O/dO d={d} G={G}")
+    hkv, n, pad = 2, 210, 3
+    hq = G * hkv
+    sl = ops.build_slices([W.SeqDesc(70, 3, 3, 0, 0, (-1, -1, -1), 1, 1, 70)])
+    q, k, v, dO = (torch.from_numpy(x).to(torch.bfloat16).to(DEV) for x in
+                   (rand((n, hq, d), 61), rand((n, hkv, d), 62), rand((n, hkv, d), 63), rand((n, hq, d), 64)))
+    plan = ops.make_plan(sl, n, n, hq, hkv, d, torch.bfloat16, backward=True)
+    O, L = ops.ffa_fwd(q, k, v, plan)
+    a = ops.ffa_bwd(q, k, v, O, dO, L, plan)
+
+    def wide(x=None):
+        w = torch.full((n, hq + pad, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+        if x is not None:
+            w[:, :hq] = x
+        return w[:, :hq]
+
+    qs, dOs, Os, dqs = wide(q), wide(dO), wide(), wide()
+    assert qs.stride(0) == (hq + pad) * d and not qs.is_contiguous()
+    Ls = torch.empty_like(L)
+    ops.ffa_fwd(qs, k, v, plan, out=Os, lse=Ls)
+    b = ops.ffa_bwd(qs, k, v, Os, dOs, Ls, plan, dq=dqs)
+    torch.cuda.synchronize()
+    assert torch.equal(O, Os) and torch.equal(L, Ls)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("case", range(6))
 def test_bwd_fuzz_raw_slices(case):
     # seeded random shapes, group sizes and slice lists against the oracle's gradients
