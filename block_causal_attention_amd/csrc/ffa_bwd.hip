@@ -40,6 +40,15 @@ namespace {
 
 using namespace dev;
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer load of 16 bytes per lane straight into LDS: lane l's bytes land
+// at dst + 16 l (dst wave-uniform); lanes past the resource's range write
+// zeros.  Counted by vmcnt like any other load.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, __bf16* dst, int32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
+}
+
 constexpr int kRows = 256;      // query rows per dQ work item (the forward's items)
 constexpr int kKeys = 128;      // keys per dK/dV work item (4 waves x 32)
 constexpr int NT = 512;         // threads per workgroup of the bf16 dQ pass at one row block per wave

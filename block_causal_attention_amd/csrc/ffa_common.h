@@ -17,7 +17,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -155,13 +154,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Buffer load of 16 bytes per lane straight into LDS: lane l's bytes land
-// at dst + 16 l (dst wave-uniform); lanes past the resource's range write
-// zeros.  Counted by vmcnt like any other load.
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, __bf16* dst, int32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
 }
 
 // V^T (or any row-major tile read as a transposed A operand) for one
