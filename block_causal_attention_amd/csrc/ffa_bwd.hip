@@ -622,8 +622,13 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
         split_bf16(-l2 * cinv, q0, q1);
         split_bf16(-aug_delta, o0, o1);
       }
-      Qa[b][tid] = (uint32_t)__builtin_bit_cast(unsigned short, q0) | ((uint32_t)__builtin_bit_cast(unsigned short, q1) << 16);
-      Oa[b][tid] = (uint32_t)__builtin_bit_cast(unsigned short, o0) | ((uint32_t)__builtin_bit_cast(unsigned short, o1) << 16);
+      // element 0 (column D) in the low half, as a b128 row read would see it
+      auto pack2 = [](__bf16 lo, __bf16 hi) {
+        return (uint32_t)__builtin_bit_cast(unsigned short, lo) |
+               ((uint32_t)__builtin_bit_cast(unsigned short, hi) << 16);
+      };
+      Qa[b][tid] = pack2(q0, q1);
+      Oa[b][tid] = pack2(o0, o1);
     }
   };
   // End of a tile: this wave's LPW loads of the tile after next may stay in
