@@ -413,8 +413,9 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
   //    slots, of which the first D / 8 receive data and the others zeros, and
   //    one load fills 64 consecutive slots.  The two augmented columns of a
   //    row (Q': -LSE2/c, dO': -delta, each a bf16 high and low part) live in
-  //    small arrays of their own, written by threads.  30.8 against 32.0 ms
-  //    for the pass on a 24B-shaped layer.
+  //    small arrays of their own, written by threads.  Waves 0-1 load the
+  //    Q' tile, waves 2-3 the dO' tile (one buffer resource per wave and
+  //    tile).  29.8 against 32.0 ms for the pass on a 24B-shaped layer.
   //  * head_dim 24: two buffers, the next tile loaded into registers while
   //    this one is computed and stored with its augmented columns at the
   //    end.  The direct loads measured 12 % slower here: the pass runs at 3
@@ -424,15 +425,14 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
   constexpr int NC = C::NC;
   constexpr int QP = DMA ? 8 * NC : C::PITCH;  // tile row pitch (elements)
   constexpr int NW = NTK / 64;                 // waves
-  constexpr int NLD = 2 * NC;                  // DMA: loads per tile, Q' slots then dO' slots
-  constexpr int LPW = (NLD + NW - 1) / NW;     // DMA: loads per wave
+  constexpr int LPW = (NC + 1) / 2;            // DMA: loads per wave (two waves per tile)
   constexpr int NCH = (TQ * C::CH + NTK - 1) / NTK;  // registers: 16-byte chunks per thread (Q' and dO' each)
   __shared__ __attribute__((aligned(16))) __bf16 Qs[DMA ? 3 : 2][TQ * QP];
   __shared__ __attribute__((aligned(16))) __bf16 Os[DMA ? 3 : 2][TQ * QP];
   __shared__ uint32_t Qa[DMA ? 3 : 1][TQ], Oa[DMA ? 3 : 1][TQ];
-  // DMA: target of the loads past NLD.  Every wave issues LPW loads per
-  // tile, so the number in flight is the same in every wave and on every
-  // path, and the wait-count bookkeeping stays exact.
+  // DMA: target of the loads past a tile's NC.  Every wave issues LPW loads
+  // per tile, so the number in flight is the same in every wave and on
+  // every path, and the wait-count bookkeeping stays exact.
   __shared__ __attribute__((aligned(16))) __bf16 Spare[DMA ? 64 * 8 : 8];
 
   const int tid = threadIdx.x;
@@ -565,39 +565,40 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
     }
   };
 
-  // DMA: load k of this wave (load index I = wave + NW k) fills the 64 slots
-  // from 64 (I mod NC) of the Q' (I < NC) or dO' tile; slot s is row s / NC
-  // (token t0 + row / G, head g G + row % G), chunk s % NC.  A lane's byte
-  // offset from the tile's first token is fixed (strides below 2^23
-  // elements, checked by the entry point); the loads go through buffer
-  // resources whose range ends with the tile's last token, so rows past it
-  // read as zeros, and slots of no data (chunks >= D / 8, rows past
-  // tq_rows when G does not divide TQ) take an offset past any range.
+  // DMA: waves 0 and 1 fill the Q' tile, waves 2 and 3 the dO' tile, so a
+  // wave builds one buffer resource per tile.  Load k of a wave fills the
+  // 64 slots from 64 J, J = (wave & 1) + 2 k (J >= NC: the spare target);
+  // slot s is row s / NC (token t0 + row / G, head g G + row % G), chunk
+  // s % NC.  A lane's byte offset from the tile's first token is fixed
+  // (strides below 2^23 elements, checked by the entry point); the loads go
+  // through buffer resources whose range ends with the tile's last token,
+  // so rows past it read as zeros, and slots of no data (chunks >= D / 8,
+  // rows past tq_rows when G does not divide TQ) take an offset past any
+  // range.
   constexpr int32_t kPastRange = 0x7ffffff0;
+  const bool ldq = wave < 2;
+  const int64_t ld_stride = ldq ? a.q_stride : a.o_stride;
+  const __bf16* ld_base = reinterpret_cast<const __bf16*>(ldq ? a.q : a.dout) + (int64_t)g * G * D;
   int32_t ld_off[LPW];
 #pragma unroll
   for (int k = 0; k < LPW; ++k) {
-    const int I = wave + NW * k;
-    const bool isq = I < NC;
-    const int sl = 64 * (isq ? I : I - NC) + lane;
+    const int J = (wave & 1) + 2 * k;
+    const int sl = 64 * J + lane;
     const int row = sl / NC, part = sl % NC;
-    const int32_t stride2 = (isq ? (int32_t)a.q_stride : (int32_t)a.o_stride) * 2;
-    ld_off[k] = I < NLD && part < C::CH && row < tq_rows ? (row / G) * stride2 + (row % G) * (D * 2) + part * 16
-                                                         : kPastRange;
+    ld_off[k] = J < NC && part < C::CH && row < tq_rows
+                    ? (row / G) * (int32_t)ld_stride * 2 + (row % G) * (D * 2) + part * 16
+                    : kPastRange;
   }
   auto issue_tile = [&](const QRun& r, int b) {
     const int32_t ntok = r.t_end - r.t0 < TQT ? r.t_end - r.t0 : TQT;
-    const __bf16* qb = reinterpret_cast<const __bf16*>(a.q) + (int64_t)r.t0 * a.q_stride + (int64_t)g * G * D;
-    const __bf16* ob = reinterpret_cast<const __bf16*>(a.dout) + (int64_t)r.t0 * a.o_stride + (int64_t)g * G * D;
-    const int32_t qrec = (ntok - 1) * (int32_t)a.q_stride * 2 + G * (D * 2);
-    const int32_t orec = (ntok - 1) * (int32_t)a.o_stride * 2 + G * (D * 2);
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)qb, (short)0, qrec, kBufCfg);
-    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)ob, (short)0, orec, kBufCfg);
+    const int32_t rec = (ntok - 1) * (int32_t)ld_stride * 2 + G * (D * 2);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(ld_base + (int64_t)r.t0 * ld_stride), (short)0, rec, kBufCfg);
+    __bf16* tile = ldq ? Qs[b] : Os[b];
 #pragma unroll
     for (int k = 0; k < LPW; ++k) {
-      const int I = wave + NW * k;
-      __bf16* dst = I < NC ? &Qs[b][I * 64 * 8] : (I < NLD ? &Os[b][(I - NC) * 64 * 8] : Spare);
-      load_lds16(I < NC ? rq : ro, dst, ld_off[k]);
+      const int J = (wave & 1) + 2 * k;
+      load_lds16(rs, J < NC ? tile + J * 64 * 8 : Spare, ld_off[k]);
     }
   };
   // augmented values of row tid (tid < TQ) of a tile: loaded when its slots
@@ -646,7 +647,7 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
   };
-  static_assert(LPW <= 15, "vmcnt field");
+  static_assert(LPW <= 15 && (!DMA || NW == 4), "vmcnt field; two waves per tile");
   auto next_run = [&](const QRun& r, QRun& n) {
     n = r;
     n.t0 = r.t0 + TQT;
