@@ -426,7 +426,7 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
   constexpr int QP = DMA ? 8 * NC : C::PITCH;  // tile row pitch (elements)
   constexpr int NW = NTK / 64;                 // waves
   constexpr int LPW = (NC + 1) / 2;            // DMA: loads per wave (two waves per tile)
-  constexpr int NCH = (TQ * C::CH + NTK - 1) / NTK;  // registers: 16-byte chunks per thread (Q' and dO' each)
+  constexpr int NCH = (TQ * C::CH + NTK / 2 - 1) / (NTK / 2);  // registers: 16-byte chunks per thread
   __shared__ __attribute__((aligned(16))) __bf16 Qs[DMA ? 3 : 2][TQ * QP];
   __shared__ __attribute__((aligned(16))) __bf16 Os[DMA ? 3 : 2][TQ * QP];
   __shared__ uint32_t Qa[DMA ? 3 : 1][TQ], Oa[DMA ? 3 : 1][TQ];
@@ -502,41 +502,37 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
     }
   }
 
-  // Registers: row n of a tile is (token t0 + n / G, head g G + n % G);
-  // 16-byte chunks of the rows plus, per row, the augmented pairs.  A
-  // thread's chunks sit at fixed byte offsets from the tile's first token
-  // (strides below 2^23 elements, checked by the entry point); the loads go
-  // through buffer resources whose range ends with the run's last token, so
-  // rows past it read as zeros without per-lane tests, and chunks of no row
-  // (past the tile, or past tq_rows when G does not divide TQ) stay zero.
-  u32x4 qr[NCH], orr[NCH];
-  int32_t q_off[NCH], o_off[NCH];
-  bool ch_row[NCH];
+  // Waves 0 and 1 stage the Q' tile, waves 2 and 3 the dO' tile, so a wave
+  // builds one buffer resource per tile.  Row n of a tile is (token t0 +
+  // n / G, head g G + n % G).  A lane's byte offsets from the tile's first
+  // token are fixed (strides below 2^23 elements, checked by the entry
+  // point); the loads go through buffer resources whose range ends with the
+  // tile's last token, so rows past it read as zeros without per-lane tests.
+  const bool ldq = wave < 2;
+  const int64_t ld_stride = ldq ? a.q_stride : a.o_stride;
+  const __bf16* ld_base = reinterpret_cast<const __bf16*>(ldq ? a.q : a.dout) + (int64_t)g * G * D;
+  // registers: chunk ci = tid mod 128 + 128 j of the wave pair's tile; chunks
+  // of no row (past tq_rows when G does not divide TQ) stay zero
+  u32x4 stg[NCH];
+  int32_t st_off[NCH];
+  bool st_row[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
-    const int ci = tid + j * NTK;
+    const int ci = (tid & 127) + 128 * j;
     const int row = ci / C::CH, part = ci % C::CH;
-    const int tt = row / G, hh = row % G;
-    ch_row[j] = ci < TQ * C::CH && row < tq_rows;
-    q_off[j] = tt * (int32_t)a.q_stride * 2 + hh * (D * 2) + part * 16;
-    o_off[j] = tt * (int32_t)a.o_stride * 2 + hh * (D * 2) + part * 16;
-    qr[j] = orr[j] = (u32x4){0, 0, 0, 0};
+    st_row[j] = ci < TQ * C::CH && row < tq_rows;
+    st_off[j] = (row / G) * (int32_t)ld_stride * 2 + (row % G) * (D * 2) + part * 16;
+    stg[j] = (u32x4){0, 0, 0, 0};
   }
   __bf16 aq0 = 0, aq1 = 0, ao0 = 0, ao1 = 0;  // augmented values of row tid (tid < TQ)
   auto load_tile = [&](const QRun& r) {
     const int32_t ntok = r.t_end - r.t0 < TQT ? r.t_end - r.t0 : TQT;
-    const __bf16* qb = reinterpret_cast<const __bf16*>(a.q) + (int64_t)r.t0 * a.q_stride + (int64_t)g * G * D;
-    const __bf16* ob = reinterpret_cast<const __bf16*>(a.dout) + (int64_t)r.t0 * a.o_stride + (int64_t)g * G * D;
-    const int32_t qrec = (ntok - 1) * (int32_t)a.q_stride * 2 + G * (D * 2);
-    const int32_t orec = (ntok - 1) * (int32_t)a.o_stride * 2 + G * (D * 2);
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)qb, (short)0, qrec, kBufCfg);
-    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)ob, (short)0, orec, kBufCfg);
+    const int32_t rec = (ntok - 1) * (int32_t)ld_stride * 2 + G * (D * 2);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(ld_base + (int64_t)r.t0 * ld_stride), (short)0, rec, kBufCfg);
 #pragma unroll
     for (int j = 0; j < NCH; ++j)
-      if (ch_row[j]) {
-        qr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, q_off[j], 0, 0));
-        orr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, o_off[j], 0, 0));
-      }
+      if (st_row[j]) stg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, st_off[j], 0, 0));
     aq0 = aq1 = ao0 = ao1 = (__bf16)0.0f;
     if (tid < tq_rows && tid / G < ntok) {
       const int64_t tok = r.t0 + tid / G;
@@ -548,13 +544,13 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
     }
   };
   auto store_tile = [&](int b) {
+    __bf16* tile = ldq ? Qs[b] : Os[b];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int ci = tid + j * NTK;
+      const int ci = (tid & 127) + 128 * j;
       if (ci < TQ * C::CH) {
         const int row = ci / C::CH, part = ci % C::CH;
-        *reinterpret_cast<u32x4*>(&Qs[b][row * QP + part * 8]) = qr[j];
-        *reinterpret_cast<u32x4*>(&Os[b][row * QP + part * 8]) = orr[j];
+        *reinterpret_cast<u32x4*>(&tile[row * QP + part * 8]) = stg[j];
       }
     }
     if (tid < TQ) {
@@ -565,20 +561,11 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
     }
   };
 
-  // DMA: waves 0 and 1 fill the Q' tile, waves 2 and 3 the dO' tile, so a
-  // wave builds one buffer resource per tile.  Load k of a wave fills the
-  // 64 slots from 64 J, J = (wave & 1) + 2 k (J >= NC: the spare target);
-  // slot s is row s / NC (token t0 + row / G, head g G + row % G), chunk
-  // s % NC.  A lane's byte offset from the tile's first token is fixed
-  // (strides below 2^23 elements, checked by the entry point); the loads go
-  // through buffer resources whose range ends with the tile's last token,
-  // so rows past it read as zeros, and slots of no data (chunks >= D / 8,
-  // rows past tq_rows when G does not divide TQ) take an offset past any
-  // range.
+  // DMA: load k of a wave fills the 64 slots from 64 J, J = (wave & 1) +
+  // 2 k (J >= NC: the spare target); slot s is row s / NC, chunk s % NC;
+  // slots of no data (chunks >= D / 8, rows past tq_rows when G does not
+  // divide TQ) take an offset past any range.
   constexpr int32_t kPastRange = 0x7ffffff0;
-  const bool ldq = wave < 2;
-  const int64_t ld_stride = ldq ? a.q_stride : a.o_stride;
-  const __bf16* ld_base = reinterpret_cast<const __bf16*>(ldq ? a.q : a.dout) + (int64_t)g * G * D;
   int32_t ld_off[LPW];
 #pragma unroll
   for (int k = 0; k < LPW; ++k) {
@@ -647,7 +634,7 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
   };
-  static_assert(LPW <= 15 && (!DMA || NW == 4), "vmcnt field; two waves per tile");
+  static_assert(LPW <= 15 && NW == 4, "vmcnt field; two waves per tile");
   auto next_run = [&](const QRun& r, QRun& n) {
     n = r;
     n.t0 = r.t0 + TQT;
