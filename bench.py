@@ -617,8 +617,9 @@ def traffic_record(wl_name, kernel, fetch_csv, write_csv, copy_fetch_csv, copy_w
 
 
 def counter_table(kernel, d, csvs, blocks):
-    """Derived figures of the forward kernel from rocprofv3 --pmc CSVs (the
-    four passes in profiles/counters_ffa_fwd.md): MFMA busy share, co-issue,
+    """Derived figures of a kernel (the forward by default) from rocprofv3
+    --pmc CSVs (the passes in profiles/counters_ffa_fwd.md and
+    profiles/counters_ffa_bwd.md): MFMA busy share, co-issue,
     LDS bank-conflict share, resident waves, instructions per 32 x 32 score
     block.  Returns a dict of counter means per dispatch and the derived
     values."""
@@ -667,12 +668,16 @@ def main():
     ap.add_argument("--counter-table", nargs="+", metavar="PMC_CSV",
                     help="print the forward kernel's derived counter figures (workload's head_dim) from "
                          "rocprofv3 --pmc CSVs of this script and exit (no GPU needed)")
+    ap.add_argument("--counter-kernel", metavar="NAME",
+                    help="kernel-name prefix for --counter-table instead of the forward's (e.g. bwd_dkdv_bf16<48); "
+                         "per-block figures still count the layer's 32 x 32 score blocks")
     args = ap.parse_args()
     if args.counter_table:
         d = 24 if args.workload == "magi4.5b" else 48
         import workloads as W
         blocks = masked_flops(W.make_workload(args.workload)) / (4.0 * d * 1024)
-        print(json.dumps(counter_table(f"ffa_fwd_bf16<{d}", d, args.counter_table, blocks), indent=1))
+        kernel = args.counter_kernel or f"ffa_fwd_bf16<{d}"
+        print(json.dumps(counter_table(kernel, d, args.counter_table, blocks), indent=1))
         return
     if args.traffic_record:
         d = 24 if args.workload == "magi4.5b" else 48
