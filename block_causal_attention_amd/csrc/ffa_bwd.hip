@@ -49,6 +49,15 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, __bf16* dst
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
 }
 
+// read_tr8 for a tile whose rows are permuted separately: the 4-row halves
+// of the 8-row step come from their own addresses
+__device__ __forceinline__ bf16x8 read_tr8_pair(const __attribute__((address_space(3))) __bf16* lo,
+                                                const __attribute__((address_space(3))) __bf16* hi) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lo);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)hi);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 constexpr int kRows = 256;      // query rows per dQ work item (the forward's items)
 constexpr int kKeys = 128;      // keys per dK/dV work item (4 waves x 32)
 constexpr int NT = 512;         // threads per workgroup of the bf16 dQ pass at one row block per wave
@@ -73,12 +82,19 @@ struct BCfg {
   // in disjoint banks; the transposed reads then see at most 2-way conflicts
   static constexpr int PITCH = 72;
   static constexpr int CH = D / 8;  // 16-byte chunks per row
-  // Q'/dO' tiles of the dK/dV pass filled by direct loads: 16-byte slots
-  // per row (odd, so the 16 rows of a b128 row read fall in disjoint banks;
-  // at least DM / 8 for the transposed reads)
-  static constexpr int NC = 9;
-  static_assert(DA <= PITCH && D % 8 == 0 && 8 * NC >= DM && NC % 2 == 1, "layout");
+  // Q'/dO' tiles of the dK/dV pass filled by direct loads: 8 16-byte slots
+  // per row, the chunks of row r permuted by tile_swizzle(r)
+  static constexpr int NC = 8;
+  static_assert(DA <= PITCH && D % 8 == 0 && 8 * NC >= DM && D / 8 <= NC, "layout");
 };
+
+// Slot of 16-byte chunk c in row r of a direct-loaded dK/dV tile of 128-byte
+// rows: c ^ tile_swizzle(r).  With 64 banks of 4 bytes, a b128 row read
+// (16 lanes: 16 consecutive rows, one chunk) and a transposed read (32
+// lanes: 4 consecutive rows from a multiple of 4, chunks 0-3 or 4-7) then
+// each touch every bank once; unswizzled 128-byte rows would put 2 or 4
+// lanes on one bank.  The value is 4 * bit 1 of r + bits 2-3 of r.
+__device__ __forceinline__ int tile_swizzle(int r) { return ((r >> 1) & 1) * 4 + ((r >> 2) & 3); }
 
 // bf16 high and low parts of x (x = hi + lo to about 2^-16 relative)
 __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
@@ -409,9 +425,10 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
   //  * head_dim 48 (DMA): three buffers filled straight from global memory
   //    (buffer loads with an LDS destination) two tiles ahead of the tile
   //    being computed, so no registers stage them.  Such a load writes each
-  //    lane's 16 bytes to consecutive LDS addresses: a tile row is NC 16-byte
-  //    slots, of which the first D / 8 receive data and the others zeros, and
-  //    one load fills 64 consecutive slots.  The two augmented columns of a
+  //    lane's 16 bytes to consecutive LDS addresses: a tile row is NC = 8
+  //    16-byte slots holding its D / 8 data chunks (and zeros) in the order
+  //    tile_swizzle gives, chosen by each lane's source offset, and one load
+  //    fills 8 rows.  The two augmented columns of a
   //    row (Q': -LSE2/c, dO': -delta, each a bf16 high and low part) live in
   //    small arrays of their own, written by threads.  Waves 0-1 load the
   //    Q' tile, waves 2-3 the dO' tile (one buffer resource per wave and
@@ -425,15 +442,15 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
   constexpr int NC = C::NC;
   constexpr int QP = DMA ? 8 * NC : C::PITCH;  // tile row pitch (elements)
   constexpr int NW = NTK / 64;                 // waves
-  constexpr int LPW = (NC + 1) / 2;            // DMA: loads per wave (two waves per tile)
+  constexpr int LPW = NC / 2;                  // DMA: loads per wave (two waves per tile)
   constexpr int NCH = (TQ * C::CH + NTK / 2 - 1) / (NTK / 2);  // registers: 16-byte chunks per thread
   __shared__ __attribute__((aligned(16))) __bf16 Qs[DMA ? 3 : 2][TQ * QP];
   __shared__ __attribute__((aligned(16))) __bf16 Os[DMA ? 3 : 2][TQ * QP];
   __shared__ uint32_t Qa[DMA ? 3 : 1][TQ], Oa[DMA ? 3 : 1][TQ];
-  // DMA: target of the loads past a tile's NC.  Every wave issues LPW loads
-  // per tile, so the number in flight is the same in every wave and on
-  // every path, and the wait-count bookkeeping stays exact.
-  __shared__ __attribute__((aligned(16))) __bf16 Spare[DMA ? 64 * 8 : 8];
+  // DMA: every wave issues the same LPW loads per tile, so the number in
+  // flight is the same in every wave and on every path, and the wait-count
+  // bookkeeping stays exact.
+  static_assert(!DMA || NC % 2 == 0, "two waves share a tile's loads evenly");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -562,17 +579,17 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
   };
 
   // DMA: load k of a wave fills the 64 slots from 64 J, J = (wave & 1) +
-  // 2 k (J >= NC: the spare target); slot s is row s / NC, chunk s % NC;
-  // slots of no data (chunks >= D / 8, rows past tq_rows when G does not
-  // divide TQ) take an offset past any range.
+  // 2 k; slot s is row s / NC, and its chunk the one tile_swizzle puts
+  // there; slots of no data (chunks >= D / 8, rows past tq_rows when G
+  // does not divide TQ) take an offset past any range.
   constexpr int32_t kPastRange = 0x7ffffff0;
   int32_t ld_off[LPW];
 #pragma unroll
   for (int k = 0; k < LPW; ++k) {
     const int J = (wave & 1) + 2 * k;
     const int sl = 64 * J + lane;
-    const int row = sl / NC, part = sl % NC;
-    ld_off[k] = J < NC && part < C::CH && row < tq_rows
+    const int row = sl / NC, part = (sl % NC) ^ tile_swizzle(sl / NC);
+    ld_off[k] = part < C::CH && row < tq_rows
                     ? (row / G) * (int32_t)ld_stride * 2 + (row % G) * (D * 2) + part * 16
                     : kPastRange;
   }
@@ -585,7 +602,7 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
 #pragma unroll
     for (int k = 0; k < LPW; ++k) {
       const int J = (wave & 1) + 2 * k;
-      load_lds16(rs, J < NC ? tile + J * 64 * 8 : Spare, ld_off[k]);
+      load_lds16(rs, tile + J * 64 * 8, ld_off[k]);
     }
   };
   // augmented values of row tid (tid < TQ) of a tile: loaded when its slots
@@ -715,12 +732,17 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
         // at D, D + 1 (DMA: from its own array), zeros above
         const int row = rb * 32 + ln;
         bf16x8 qa, oa;
-        if (!DMA || 16 * ks + 16 <= D) {
+        if (!DMA) {
           qa = *reinterpret_cast<const bf16x8*>(&Qb[row * QP + 16 * ks + 8 * h]);
           oa = *reinterpret_cast<const bf16x8*>(&Ob[row * QP + 16 * ks + 8 * h]);
+        } else if (16 * ks + 16 <= D) {
+          const int col = ((2 * ks + h) ^ tile_swizzle(row)) * 8;
+          qa = *reinterpret_cast<const bf16x8*>(&Qb[row * QP + col]);
+          oa = *reinterpret_cast<const bf16x8*>(&Ob[row * QP + col]);
         } else {
           const bf16x8 qaug = __builtin_bit_cast(bf16x8, (u32x4){Qab[row], 0u, 0u, 0u});
           const bf16x8 oaug = __builtin_bit_cast(bf16x8, (u32x4){Oab[row], 0u, 0u, 0u});
+          static_assert(!DMA || D % 16 == 0, "the mixed data/augmented step is read unswizzled");
           if (16 * ks + 8 == D) {  // lane half 0 data, half 1 the augmented pair
             const bf16x8 qd = *reinterpret_cast<const bf16x8*>(&Qb[row * QP + 16 * ks]);
             const bf16x8 od = *reinterpret_cast<const bf16x8*>(&Ob[row * QP + 16 * ks]);
@@ -786,8 +808,17 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb) {
           const int dcol = mb * 32 + dgrp + 4 * (li % 4);
-          const bf16x8 ot8 = read_tr8(Ot + qrow * QP + dcol, QP);
-          const bf16x8 qt8 = read_tr8(Qt + qrow * QP + dcol, QP);
+          bf16x8 ot8, qt8;
+          if constexpr (DMA) {
+            // rows qrow and qrow + 8, each with its own chunk permutation
+            const int lo = qrow * QP + (((dcol >> 3) ^ tile_swizzle(qrow)) << 3) + (dcol & 7);
+            const int hi = (qrow + 8) * QP + (((dcol >> 3) ^ tile_swizzle(qrow + 8)) << 3) + (dcol & 7);
+            ot8 = read_tr8_pair(Ot + lo, Ot + hi);
+            qt8 = read_tr8_pair(Qt + lo, Qt + hi);
+          } else {
+            ot8 = read_tr8(Ot + qrow * QP + dcol, QP);
+            qt8 = read_tr8(Qt + qrow * QP + dcol, QP);
+          }
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
             dv[kb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot8, pb[kb][i2], dv[kb][mb], 0, 0, 0);
