@@ -50,9 +50,16 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, __bf16* dst
 }
 
 // read_tr8 for a tile whose rows are permuted separately: the 4-row halves
-// of the 8-row step come from their own addresses
-__device__ __forceinline__ bf16x8 read_tr8_pair(const __attribute__((address_space(3))) __bf16* lo,
-                                                const __attribute__((address_space(3))) __bf16* hi) {
+// of the 8-row step come from their own addresses.  The restrict-qualified
+// sources (both only read) give the inlined reads alias-scope metadata; for
+// such a read the compiler's wait-count pass waits only on direct-to-LDS
+// loads whose scopes it can match, and the tile loads carry none, so no
+// `vmcnt(0)` lands in the middle of a tile (a transposed read without
+// scope metadata drains every direct load in flight).  The tiles stay
+// correct without that wait: a buffer being filled is read only after the
+// tile's explicit vmcnt wait and barrier.
+__device__ __forceinline__ bf16x8 read_tr8_pair(const __attribute__((address_space(3))) __bf16* __restrict__ lo,
+                                                const __attribute__((address_space(3))) __bf16* __restrict__ hi) {
   const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lo);
   const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)hi);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -128,12 +135,24 @@ template <int D, bool PRESCALED, int RB>
 __global__ __launch_bounds__(NT / RB, RB == 2 && D == 24 ? 3 : 2) void bwd_dq_bf16(BwdArgs a) {
   using C = BCfg<D>;
   constexpr int NTQ = NT / RB;                       // threads per workgroup
-  constexpr int NCH = (TK * C::CH + NTQ - 1) / NTQ;  // 16-byte chunks per thread per tile (K and V each)
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][TK * C::PITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][TK * C::PITCH];
+  constexpr int NCH = (TK * C::CH + NTQ - 1) / NTQ;  // registers: 16-byte chunks per thread per tile (K and V each)
+  // K/V tiles as the dK/dV pass stages its Q'/dO' tiles: at head_dim 48 in
+  // three LDS buffers filled by direct loads two tiles ahead, 128-byte rows
+  // permuted by tile_swizzle, waves 0-1 loading K and 2-3 V (the padding-only
+  // contraction step is built in registers); at 24 in two buffers staged
+  // through registers, 144-byte rows.
+  constexpr bool DMA = D >= 48;
+  constexpr int NC = C::NC;
+  constexpr int KP = DMA ? 8 * NC : C::PITCH;  // tile row pitch (elements)
+  constexpr int NW = NTQ / 64;                 // waves
+  constexpr int LPW = NC / 2;                  // DMA: loads per wave (two waves per tile)
+  static_assert(!DMA || (NW == 4 && NC % 2 == 0 && D % 16 == 0), "two waves per tile; no mixed step");
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[DMA ? 3 : 2][TK * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[DMA ? 3 : 2][TK * KP];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the loads branch per wave
   const int h = lane >> 5, ln = lane & 31, li = lane & 15;
   const int dgrp = ((lane >> 4) & 1) * 16;
   const magi_work_item wi = load_item(a.qwork, blockIdx.x);
@@ -148,15 +167,16 @@ __global__ __launch_bounds__(NT / RB, RB == 2 && D == 24 ? 3 : 2) void bwd_dq_bf
   const __bf16* __restrict__ kp = reinterpret_cast<const __bf16*>(a.k);
   const __bf16* __restrict__ vp = reinterpret_cast<const __bf16*>(a.v);
 
-  // padding columns of every K and V buffer: D and D+1 are 1 (they meet the
-  // augmented slots), the rest 0; tile stores never touch them
-  for (int b = 0; b < 2; ++b)
-    for (int i = tid; i < TK * (C::DA - D); i += NTQ) {
-      const int col = D + i % (C::DA - D), row = i / (C::DA - D);
-      const __bf16 x = (__bf16)(col < D + 2 ? 1.0f : 0.0f);
-      Ks[b][row * C::PITCH + col] = x;
-      Vs[b][row * C::PITCH + col] = x;
-    }
+  // registers: padding columns of every K and V buffer: D and D+1 are 1
+  // (they meet the augmented slots), the rest 0; tile stores never touch them
+  if constexpr (!DMA)
+    for (int b = 0; b < 2; ++b)
+      for (int i = tid; i < TK * (C::DA - D); i += NTQ) {
+        const int col = D + i % (C::DA - D), row = i / (C::DA - D);
+        const __bf16 x = (__bf16)(col < D + 2 ? 1.0f : 0.0f);
+        Ks[b][row * KP + col] = x;
+        Vs[b][row * KP + col] = x;
+      }
 
   // this lane's query rows (one per 32-row MFMA column block of the wave)
   int32_t qi[RB];
@@ -228,10 +248,43 @@ __global__ __launch_bounds__(NT / RB, RB == 2 && D == 24 ? 3 : 2) void bwd_dq_bf
       const int ci = tid + j * NTQ;
       if (ci < TK * C::CH) {
         const int r = ci / C::CH, part = ci % C::CH;
-        *reinterpret_cast<u32x4*>(&Ks[b][r * C::PITCH + part * 8]) = kr[j];
-        *reinterpret_cast<u32x4*>(&Vs[b][r * C::PITCH + part * 8]) = vr[j];
+        *reinterpret_cast<u32x4*>(&Ks[b][r * KP + part * 8]) = kr[j];
+        *reinterpret_cast<u32x4*>(&Vs[b][r * KP + part * 8]) = vr[j];
       }
     }
+  };
+  // DMA: load k of a wave fills the 64 slots from 64 J, J = (wave & 1) + 2 k,
+  // of the K (waves 0-1) or V tile; slot s is key row s / NC, its chunk the
+  // one tile_swizzle puts there; chunks >= D / 8 read past the range (zeros)
+  constexpr int32_t kPastRange = 0x7ffffff0;
+  const bool ldk = wave < 2;
+  int32_t ld_off[LPW];
+#pragma unroll
+  for (int k = 0; k < LPW; ++k) {
+    const int sl = 64 * ((wave & 1) + 2 * k) + lane;
+    const int row = sl / NC, part = (sl % NC) ^ tile_swizzle(sl / NC);
+    ld_off[k] = part < C::CH ? row * kv_row_bytes + part * 16 : kPastRange;
+  }
+  auto issue_tile = [&](int32_t kt, int32_t khi, int b) {
+    const int64_t elem0 = (int64_t)kt * a.kv_stride + (int64_t)g * a.kv_hstride;
+    const int32_t rows = khi - kt < TK ? khi - kt : TK;
+    const int nrec = (rows - 1) * kv_row_bytes + D * 2;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)((ldk ? kp : vp) + elem0), (short)0, nrec, kBufCfg);
+    __bf16* tile = ldk ? Ks[b] : Vs[b];
+#pragma unroll
+    for (int k = 0; k < LPW; ++k) load_lds16(rs, tile + ((wave & 1) + 2 * k) * 64 * 8, ld_off[k]);
+  };
+  // DMA: end of a tile, as in the dK/dV pass: this wave's LPW loads of the
+  // tile after next may stay in flight, the older ones must have landed
+  auto end_tile = [&](bool pending) {
+    if (pending)
+      __builtin_amdgcn_s_waitcnt(0x70 | LPW);  // vmcnt(LPW), expcnt 7, lgkmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x70);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
   };
 
   const int32_t first_tok = wi.q_start, last_tok = wi.q_start + qlen - 1;
@@ -244,27 +297,51 @@ __global__ __launch_bounds__(NT / RB, RB == 2 && D == 24 ? 3 : 2) void bwd_dq_bf
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) dq[rb][mb] = (f32x16){};
 
-  SliceGeo cg;
+  // the tile after (g0, t0): TK keys on in the slice, else the next slice
+  // that shows the item a key
+  auto next_tile = [&](const SliceGeo& g0, int32_t t0, SliceGeo& g1, int32_t& t1) {
+    g1 = g0;
+    t1 = t0 + TK;
+    bool ok = true;
+    if (t1 >= g0.khi) {
+      ok = find_slice(lists, wi.slice_end, (int32_t)a.nk, g0.si + 1, first_tok, last_tok, g1);
+      t1 = g1.ks;
+    }
+    return ok;
+  };
+  SliceGeo cg, ng;
   bool have = find_slice(lists, wi.slice_end, (int32_t)a.nk, wi.slice_begin, first_tok, last_tok, cg);
-  int32_t kt = cg.ks;
-  if (have) {
-    load_tile(kt, cg.khi);
-    store_tile(0);
+  int32_t kt = cg.ks, nkt = 0;
+  bool have_next = false;
+  if constexpr (DMA) {
+    if (have) {
+      issue_tile(kt, cg.khi, 0);
+      have_next = next_tile(cg, kt, ng, nkt);
+      if (have_next) issue_tile(nkt, ng.khi, 1);
+    }
+    end_tile(false);
+  } else {
+    if (have) {
+      load_tile(kt, cg.khi);
+      store_tile(0);
+    }
+    // drain once: the lane-masked loads and stores above would otherwise make
+    // the wait-count bookkeeping serialise every tile on its own prefetch
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
   }
-  // drain once: the lane-masked loads and stores above would otherwise make
-  // the wait-count bookkeeping serialise every tile on its own prefetch
-  __builtin_amdgcn_s_waitcnt(0);
-  lds_barrier();
   int buf = 0;
   while (have) {
-    SliceGeo ng = cg;
-    int32_t nkt = kt + TK;
-    bool have_next = true;
-    if (nkt >= cg.khi) {
-      have_next = find_slice(lists, wi.slice_end, (int32_t)a.nk, cg.si + 1, first_tok, last_tok, ng);
-      nkt = ng.ks;
+    SliceGeo ng2;
+    int32_t nkt2 = 0;
+    bool have2 = false;
+    if constexpr (DMA) {
+      if (have_next) have2 = next_tile(ng, nkt, ng2, nkt2);
+      if (have2) issue_tile(nkt2, ng2.khi, buf == 0 ? 2 : buf - 1);  // in flight during this tile and the next
+    } else {
+      have_next = next_tile(cg, kt, ng, nkt);
+      if (have_next) load_tile(nkt, ng.khi);  // in flight while this tile is computed
     }
-    if (have_next) load_tile(nkt, ng.khi);  // in flight while this tile is computed
     const bool masked = kt < cg.klo || kt + TK > cg.kfull;
     const __bf16* Kb = Ks[buf];
     const __bf16* Vb = Vs[buf];
@@ -283,8 +360,10 @@ __global__ __launch_bounds__(NT / RB, RB == 2 && D == 24 ? 3 : 2) void bwd_dq_bf
           ones[0] = ones[1] = (__bf16)1.0f;
           ka[ks] = va[ks] = h ? (bf16x8){} : ones;
         } else {
-          ka[ks] = *reinterpret_cast<const bf16x8*>(&Kb[(kb * 32 + ln) * C::PITCH + 16 * ks + 8 * h]);
-          va[ks] = *reinterpret_cast<const bf16x8*>(&Vb[(kb * 32 + ln) * C::PITCH + 16 * ks + 8 * h]);
+          const int row = kb * 32 + ln;
+          const int col = DMA ? ((2 * ks + h) ^ tile_swizzle(row)) * 8 : 16 * ks + 8 * h;
+          ka[ks] = *reinterpret_cast<const bf16x8*>(&Kb[row * KP + col]);
+          va[ks] = *reinterpret_cast<const bf16x8*>(&Vb[row * KP + col]);
         }
       }
       // dS^T = P^T * dP'^T, rounded to bf16 in the B-operand layout
@@ -322,19 +401,37 @@ __global__ __launch_bounds__(NT / RB, RB == 2 && D == 24 ? 3 : 2) void bwd_dq_bf
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb) {
           const int dcol = mb * 32 + dgrp + 4 * (li % 4);
-          const bf16x8 kt8 = read_tr8(Kt + krow * C::PITCH + dcol, C::PITCH);
+          bf16x8 kt8;
+          if constexpr (DMA) {
+            const int lo = krow * KP + (((dcol >> 3) ^ tile_swizzle(krow)) << 3) + (dcol & 7);
+            const int hi = (krow + 8) * KP + (((dcol >> 3) ^ tile_swizzle(krow + 8)) << 3) + (dcol & 7);
+            kt8 = read_tr8_pair(Kt + lo, Kt + hi);
+          } else {
+            kt8 = read_tr8(Kt + krow * KP + dcol, KP);
+          }
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             dq[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt8, dsb[rb][i2], dq[rb][mb], 0, 0, 0);
         }
       }
     }
-    if (have_next) store_tile(buf ^ 1);
-    lds_barrier();  // the next tile is in LDS; this buffer is free again
-    cg = ng;
-    kt = nkt;
-    have = have_next;
-    buf ^= 1;
+    if constexpr (DMA) {
+      end_tile(have2);
+      cg = ng;
+      kt = nkt;
+      have = have_next;
+      ng = ng2;
+      nkt = nkt2;
+      have_next = have2;
+      buf = buf == 2 ? 0 : buf + 1;
+    } else {
+      if (have_next) store_tile(buf ^ 1);
+      lds_barrier();  // the next tile is in LDS; this buffer is free again
+      cg = ng;
+      kt = nkt;
+      have = have_next;
+      buf ^= 1;
+    }
   }
 
   // epilogue: dQ = scale * (dQ^T)^T; lane half h holds d = 8 grp + 4 h + r
