@@ -62,11 +62,14 @@ struct Cfg {
   static constexpr int KS = DK / 16;                  // MFMA k-steps for Q.K
   static constexpr int DV = (D + 1 + 31) / 32 * 32;   // V columns incl. the ones column
   static constexpr int MB = DV / 32;                  // 32-row blocks of O^T
-  static constexpr int KROW = DK + 8;                 // LDS pitch of a K row (elements)
-  // LDS pitch of a V row (elements): ds_read_b64_tr_b16 has each group of
-  // 16 lanes read 4 consecutive rows x 32 bytes, so the pitch is chosen to
-  // put 4 consecutive rows in disjoint bank ranges
-  static constexpr int VROW = DV == 32 ? 32 : DV + 32;
+  // K and V tile rows in LDS, so that neither the b128 row reads of K nor
+  // the transposed reads of V put two lanes of a pass on one bank: at
+  // head_dim 24 64-byte rows with the chunks of K rows permuted by kswz; at
+  // 48 padded rows of 112 bytes (K) and 192 bytes (V), which need no
+  // permutation (the reads of 4 consecutive V rows x 32 bytes fall in
+  // disjoint bank ranges)
+  static constexpr int KROW = DK > 32 ? DK + 8 : 32;  // LDS pitch of a K row (elements)
+  static constexpr int VROW = DK > 32 ? DV + 32 : DV;  // LDS pitch of a V row (elements)
   static constexpr int CH = D / 8;                    // 16-byte chunks per K/V row
   // position of the denominator (the ones column, V column D) in the O^T
   // accumulator of lane half 0: block D/32, index 4*((D%32)/8) + D%4
@@ -74,6 +77,39 @@ struct Cfg {
   static constexpr int LIDX = 4 * ((D % 32) / 8) + (D % 4);
   static_assert(((D % 32) / 4) % 2 == 0, "ones column must fall in lane half 0");
 };
+
+// Slot of chunk c in row r of a K or V tile: c ^ swizzle(r).  The 64-byte
+// K rows of head_dim 24 move chunks by bits 2-3 of r, so that 16
+// consecutive rows of one chunk cover all 16 four-bank groups; V there (4
+// consecutive rows x 4 chunks are 16 consecutive slots) and both tiles at
+// 48 (padded rows) keep their order.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return D > 32 ? 0 : (r >> 2) & 3;
+}
+template <int D>
+__device__ __forceinline__ int vswz(int) {
+  return 0;
+}
+
+// Buffer load of 16 bytes per lane straight into LDS: lane l's bytes land
+// at dst + 16 l (dst wave-uniform); lanes past the resource's range write
+// zeros, inactive lanes write nothing.  Counted by vmcnt like other loads.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, __bf16* dst, int32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+}
+
+// Transposed read of an 8-row step whose 4-row halves sit at their own
+// addresses.  Restrict-qualified sources (both only read) give the inlined
+// reads alias-scope metadata, so the compiler's wait-count pass does not
+// drain the direct tile loads in flight before them; the tile they read
+// was completed before the barrier that precedes its use.
+__device__ __forceinline__ bf16x8 read_tr_pair(const __attribute__((address_space(3))) __bf16* __restrict__ lo,
+                                               const __attribute__((address_space(3))) __bf16* __restrict__ hi) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lo);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)hi);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 // Largest bf16 value <= x (x finite).
 __device__ __forceinline__ __bf16 bf16_floor(float x) {
@@ -89,15 +125,15 @@ __device__ __forceinline__ __bf16 bf16_floor(float x) {
 // PRESCALED: the caller folded softmax_scale * log2(e) into Q or K, so the
 // scores leave the MFMA already in log2 units and need no multiply.
 // NB: 32-row column blocks per wave.  The 256 rows of a work item are
-// spread over 256 / (32 NB) waves, so NB = 1 doubles the waves per SIMD
-// (more latency hiding) at the price of more LDS reads per score.
+// spread over 256 / (32 NB) waves, so NB = 1 doubles the waves of a
+// workgroup at the price of more LDS reads per score.  Both run 4 waves
+// per SIMD (NB = 2 fits 128 VGPRs once no registers stage the tiles).
 // QN: q holds the raw queries; each lane applies QK-Norm and the 3D RoPE to
 // its rows after loading them (as the prologue kernel does for K).
 template <int D, bool PRESCALED, int NB, bool QN>
-__global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(FfaArgs a) {
+__global__ __launch_bounds__(2 * kRows / NB, 4) void ffa_fwd_bf16(FfaArgs a) {
   using C = Cfg<D>;
   constexpr int NT = 2 * kRows / NB;  // threads per workgroup: 32 NB rows per wave
-  constexpr int NCH = (TK * C::CH + NT - 1) / NT;  // 16-byte K (and V) chunks per thread per tile
   __shared__ __attribute__((aligned(16))) __bf16 Ks[3][TK * C::KROW];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[3][TK * C::VROW];
 
@@ -124,15 +160,16 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
   // constant padding columns of both LDS buffers: K column D is 1 (AUG),
   // K columns D+1..DK-1 are 0, V column D is 1 (it accumulates the softmax
   // denominator), V columns D+1..DV-1 are 0
+  // (the tile loads never write those chunks)
   for (int b = 0; b < 3; ++b) {
     if constexpr (AUG)
       for (int i = tid; i < TK * (C::DK - D); i += NT) {
-        const int col = D + i % (C::DK - D);
-        Ks[b][(i / (C::DK - D)) * C::KROW + col] = (__bf16)(col == D ? 1.0f : 0.0f);
+        const int col = D + i % (C::DK - D), r = i / (C::DK - D);
+        Ks[b][r * C::KROW + (((col >> 3) ^ kswz<D>(r)) << 3) + (col & 7)] = (__bf16)(col == D ? 1.0f : 0.0f);
       }
     for (int i = tid; i < TK * (C::DV - D); i += NT) {
-      const int col = D + i % (C::DV - D);
-      Vs[b][(i / (C::DV - D)) * C::VROW + col] = (__bf16)(col == D ? 1.0f : 0.0f);
+      const int col = D + i % (C::DV - D), r = i / (C::DV - D);
+      Vs[b][r * C::VROW + (((col >> 3) ^ vswz<D>(r)) << 3) + (col & 7)] = (__bf16)(col == D ? 1.0f : 0.0f);
     }
   }
 
@@ -272,18 +309,36 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
   // of its 32-key block; the lane-independent part is a compile-time
   // constant, so masking compares against constants.
   constexpr auto key_of0 = [](int i) { return 8 * (i / 4) + (i % 4); };
-  // K/V tiles are fetched with buffer loads whose range ends at the last
-  // visible key, so rows past it read as zeros with no per-lane test; each
-  // thread's byte offset inside a tile never changes.  A tile spans TK rows
-  // of kv_stride elements, which the entry point keeps under 2^31 bytes.
-  u32x4 kr[NCH], vr[NCH];
-  int ch_off[NCH];
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int ci = tid + j * NT;
-    ch_off[j] = (ci / C::CH) * (int)a.kv_stride * 2 + (ci % C::CH) * 16;
-  }
+  // K/V tiles go straight from global memory into LDS (buffer loads with an
+  // LDS destination, no staging registers): one load fills 64 consecutive
+  // 16-byte slots, so a lane's slot fixes which chunk of which key row it
+  // fetches; the first half of the waves fetches K, the second V, LPW loads
+  // each per tile.  The loads' range ends at the last visible key, so rows
+  // past it read as zeros with no per-lane test; lanes whose slot holds a
+  // constant chunk (the ones and zero columns) stay inactive.  A lane's byte
+  // offset inside a tile never changes; a tile spans TK rows of kv_stride
+  // elements, which the entry point keeps under 2^31 bytes.
+  constexpr int NWV = NT / 64;                        // waves
+  constexpr int HW = NWV / 2;                         // waves per tensor
+  constexpr int KSL = C::KROW / 8, VSL = C::VROW / 8;  // slots per row
+  constexpr int NLK = TK * KSL / 64, NLV = TK * VSL / 64;  // loads per tile
+  static_assert((TK * KSL) % 64 == 0 && (TK * VSL) % 64 == 0, "whole loads per tile");
+  constexpr int LPW = ((NLK > NLV ? NLK : NLV) + HW - 1) / HW;  // loads per wave and tile, at most
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool ld_k = wave_u < HW;
+  const int ld_n = ld_k ? NLK : NLV;       // loads of this wave's tensor
+  const int ld_sl = ld_k ? KSL : VSL;      // its slots per row
   const int32_t kv_row_bytes = (int32_t)a.kv_stride * 2;
+  int32_t ld_off[LPW];
+  bool ld_on[LPW];
+#pragma unroll
+  for (int k = 0; k < LPW; ++k) {
+    const int sl = 64 * (wave_u % HW + HW * k) + lane;
+    const int r = sl / ld_sl;
+    const int chunk = (sl % ld_sl) ^ (ld_k ? kswz<D>(r) : vswz<D>(r));
+    ld_on[k] = chunk < C::CH;
+    ld_off[k] = r * kv_row_bytes + chunk * 16;
+  }
 
   // The item's tiles in visiting order: TK-key steps through one slice's
   // visible key range, then on to the next slice that shows the item a key.
@@ -301,29 +356,17 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
       n.kt = n.geo.ks;
     }
   };
-  auto load_tile = [&](const TileRef& t, u32x4 (&kd)[NCH], u32x4 (&vd)[NCH]) {
+  auto issue_tile = [&](const TileRef& t, int b) {
     const int64_t elem0 = (int64_t)t.kt * a.kv_stride + (int64_t)g * a.kv_hstride;
     const int32_t rows = t.geo.khi - t.kt < TK ? t.geo.khi - t.kt : TK;  // >= 1
     const int nrec = (rows - 1) * kv_row_bytes + D * 2;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kp + elem0), (short)0, nrec, kBufCfg);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vp + elem0), (short)0, nrec, kBufCfg);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)((ld_k ? kp : vp) + elem0), (short)0, nrec, kBufCfg);
+    __bf16* tile = ld_k ? Ks[b] : Vs[b];
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      if (tid + j * NT < TK * C::CH) {
-        kd[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ch_off[j], 0, 0));
-        vd[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ch_off[j], 0, 0));
-      }
-    }
-  };
-  auto store_tile = [&](int b, const u32x4 (&kd)[NCH], const u32x4 (&vd)[NCH]) {
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int ci = tid + j * NT;
-      if (ci < TK * C::CH) {
-        const int r = ci / C::CH, part = ci % C::CH;
-        *reinterpret_cast<u32x4*>(&Ks[b][r * C::KROW + part * 8]) = kd[j];
-        *reinterpret_cast<u32x4*>(&Vs[b][r * C::VROW + part * 8]) = vd[j];
-      }
+    for (int k = 0; k < LPW; ++k) {
+      const int J = wave_u % HW + HW * k;
+      if (J < ld_n && ld_on[k]) load_lds16(rs, tile + J * 64 * 8, ld_off[k]);
     }
   };
 
@@ -331,7 +374,8 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
   auto read_k = [&](int b, int kb, bf16x8 (&kop)[C::KS]) {
 #pragma unroll
     for (int ks2 = 0; ks2 < C::KS; ++ks2)
-      kop[ks2] = *reinterpret_cast<const bf16x8*>(&Ks[b][(kb * 32 + ln) * C::KROW + 16 * ks2 + 8 * h]);
+      kop[ks2] = *reinterpret_cast<const bf16x8*>(
+          &Ks[b][(kb * 32 + ln) * C::KROW + (((2 * ks2 + h) ^ kswz<D>(kb * 32 + ln)) << 3)]);
   };
 
   // Pipeline.  Three LDS buffers hold consecutive tiles.  While a tile is
@@ -352,19 +396,11 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
   T0.kt = T0.geo.ks;
   next_tile(T0, T1);
   bf16x8 kcur[C::KS];
-  {
-    // the first two tiles are fetched together; the second one stays in the
-    // staging registers until the first tile's pass stores it
-    u32x4 k0r[NCH], v0r[NCH];
-    if (T0.valid) load_tile(T0, k0r, v0r);
-    if (T1.valid) load_tile(T1, kr, vr);
-    // Drain every outstanding memory operation before the loop (both tiles
-    // are in flight together, so this costs one latency).  Without it the
-    // wait-count bookkeeping merges the lane-masked paths above into the
-    // loop header and makes every tile wait for its own prefetch.
-    __builtin_amdgcn_s_waitcnt(0);
-    if (T0.valid) store_tile(0, k0r, v0r);
-  }
+  // the first two tiles are fetched together; the barrier's release fence
+  // waits for both
+  if (T0.valid) issue_tile(T0, 0);
+  if (T1.valid) issue_tile(T1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();
   read_k(0, 0, kcur);  // unused if the item sees no key
   int b0 = 0;  // buffer of T0
@@ -396,9 +432,12 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
       for (int kb = 0; kb < NBLK; ++kb) {
         bf16x8 knext[C::KS];
         if (kb == NBLK - 1) {
-          lds_barrier();  // tile T1 is in buffer b1
+          // tile T1 is in buffer b1: the release fence of the barrier waits
+          // for this wave's loads of it, the barrier for every wave's
+          __builtin_amdgcn_s_waitcnt(0);
+          lds_barrier();
           next_tile(T1, T2);
-          if (T2.valid) load_tile(T2, kr, vr);  // stored at the end of the next tile's block NBLK-2
+          if (T2.valid) issue_tile(T2, b1 == 2 ? 0 : b1 + 1);  // into the buffer T0's predecessor used
           read_k(b1, 0, knext);  // unused after the last tile
         } else {
           read_k(b0, kb + 1, knext);
@@ -495,16 +534,14 @@ __global__ __launch_bounds__(2 * kRows / NB, NB == 1 ? 4 : 3) void ffa_fwd_bf16(
 #pragma unroll
           for (int mb = 0; mb < C::MB; ++mb) {
             const int dcol = mb * 32 + dgrp + 4 * (li % 4);
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + krow * C::VROW + dcol));
-            const s16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vb + (krow + 8) * C::VROW + dcol));
-            const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            const int plo = krow * C::VROW + (((dcol >> 3) ^ vswz<D>(krow)) << 3) + (dcol & 7);
+            const int phi = (krow + 8) * C::VROW + (((dcol >> 3) ^ vswz<D>(krow + 8)) << 3) + (dcol & 7);
+            const bf16x8 vop = read_tr_pair(Vb + plo, Vb + phi);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
               o[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[nb], o[nb][mb], 0, 0, 0);
           }
         }
-        if (kb == NBLK - 2 && T1.valid) store_tile(b1, kr, vr);
       }
       T0 = T1;
       T1 = T2;
@@ -616,8 +653,8 @@ hipError_t launch_ffa_fwd(const FfaArgs& a, hipStream_t stream) {
   if (a.dtype == MAGI_DTYPE_BF16) {
     // scores arrive in log2 units when the caller folded scale * log2(e) into Q or K
     const bool pre = fabsf(a.scale * kLog2e - 1.0f) < 1e-6f;
-    // head_dim 24: 64 rows per wave halve the LDS operand reads per score
-    // (3 waves per SIMD); head_dim 48: 32 rows per wave (4 waves per SIMD)
+    // head_dim 24: 64 rows per wave halve the LDS operand reads per score;
+    // head_dim 48: 32 rows per wave
     constexpr int NB24 = 2, NB48 = 1;
     const bool qn = a.qn_gain != nullptr;
     if (a.head_dim == 24) {
