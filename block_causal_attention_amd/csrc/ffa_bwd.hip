@@ -85,6 +85,7 @@ struct BCfg {
   static constexpr int KS = DA / 16;                 // MFMA k-steps over it
   static constexpr int DM = (D + 31) / 32 * 32;      // rows of the head_dim-major accumulators
   static constexpr int MB = DM / 32;
+  static constexpr int KD = (D + 15) / 16;           // k-steps over the data columns alone (dK/dV pass)
   // LDS row pitch (elements): 144 bytes puts the 16 rows of a b128 row read
   // in disjoint banks; the transposed reads then see at most 2-way conflicts
   static constexpr int PITCH = 72;
@@ -515,7 +516,7 @@ __device__ __forceinline__ bool find_qrun(const SliceLists& L, int32_t slice_end
 // kKeys / (32 KB) waves; KB = 2 lets one wave's Q'/dO' operand reads (and
 // their transposes) serve 64 keys, halving those LDS reads per key.
 template <int D, bool PRESCALED, int KB>
-__global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16(BwdArgs a) {
+__global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 4 : 3) void bwd_dkdv_bf16(BwdArgs a) {
   using C = BCfg<D>;
   constexpr int NTK = 2 * kKeys / KB;                // threads per workgroup
   // Two ways to stage the Q'/dO' tiles of TQ rows in LDS:
@@ -525,16 +526,17 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
   //    lane's 16 bytes to consecutive LDS addresses: a tile row is NC = 8
   //    16-byte slots holding its D / 8 data chunks (and zeros) in the order
   //    tile_swizzle gives, chosen by each lane's source offset, and one load
-  //    fills 8 rows.  The two augmented columns of a
-  //    row (Q': -LSE2/c, dO': -delta, each a bf16 high and low part) live in
-  //    small arrays of their own, written by threads.  Waves 0-1 load the
-  //    Q' tile, waves 2-3 the dO' tile (one buffer resource per wave and
-  //    tile).  29.8 against 32.0 ms for the pass on a 24B-shaped layer.
+  //    fills 8 rows.  Waves 0-1 load the Q' tile, waves 2-3 the dO' tile
+  //    (one buffer resource per wave and tile).  The data fill whole
+  //    k-steps, so the rows' -LSE2 and -delta start the S' and dP'
+  //    accumulators (from small fp32 arrays) instead of riding in a
+  //    padding step: two MFMAs and eight registers fewer per 32 x 32 block.
   //  * head_dim 24: two buffers, the next tile loaded into registers while
-  //    this one is computed and stored with its augmented columns at the
-  //    end.  The direct loads measured 12 % slower here: the pass runs at 3
-  //    waves per SIMD on the edge of its register budget, and their longer
-  //    loop (more scalar work, spills to lanes) costs more than it hides.
+  //    this one is computed and stored at the end, with the rows' -LSE2 and
+  //    -delta (each a bf16 high and low part) in padding columns D, D + 1,
+  //    which meet ones in K and V inside the last, part-filled k-step (so
+  //    they cost no MFMA here).  Direct loads measured 12 % slower at this
+  //    size: their longer loop (more scalar work) costs more than it hides.
   constexpr bool DMA = D >= 48;
   constexpr int NC = C::NC;
   constexpr int QP = DMA ? 8 * NC : C::PITCH;  // tile row pitch (elements)
@@ -543,7 +545,11 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
   constexpr int NCH = (TQ * C::CH + NTK / 2 - 1) / (NTK / 2);  // registers: 16-byte chunks per thread
   __shared__ __attribute__((aligned(16))) __bf16 Qs[DMA ? 3 : 2][TQ * QP];
   __shared__ __attribute__((aligned(16))) __bf16 Os[DMA ? 3 : 2][TQ * QP];
-  __shared__ uint32_t Qa[DMA ? 3 : 1][TQ], Oa[DMA ? 3 : 1][TQ];
+  // DMA: per row of a tile, -LSE2 (times 1/c unless K is prescaled) and
+  // -delta, the initial values of the row's S' and dP' accumulators, so that
+  // exp2(S') is P and P dP' is dS without per-score subtractions
+  __shared__ __attribute__((aligned(16))) float Qa[DMA ? 3 : 1][DMA ? TQ : 4], Oa[DMA ? 3 : 1][DMA ? TQ : 4];
+  constexpr int KQ = DMA ? C::KD : C::KS;  // k-steps of S' and dP'
   // DMA: every wave issues the same LPW loads per tile, so the number in
   // flight is the same in every wave and on every path, and the wait-count
   // bookkeeping stays exact.
@@ -573,8 +579,6 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
   const float c = a.scale * kLog2e;
   const float cinv = 1.0f / c;
   const int TQT = TQ / G;  // tokens per tile
-  // floor(row / G) = (row * ginv) >> 16 for row < 64, G <= 64
-  const int32_t ginv = ((1 << 16) + G - 1) / G;
   const int tq_rows = TQT * G;
 
   if constexpr (!DMA) {
@@ -589,10 +593,11 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
   }
 
   // this lane's keys (column n of the MFMA, one per key block): K and V
-  // rows as B operands with the two ones columns that meet the augmented slots
+  // rows as B operands; the register path adds the two ones columns that
+  // meet the augmented slots
   int32_t key[KB];
   bool kvalid[KB];
-  bf16x8 kreg[KB][C::KS], vreg[KB][C::KS];
+  bf16x8 kreg[KB][KQ], vreg[KB][KQ];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     key[kb] = k0 + (wave * KB + kb) * 32 + ln;
@@ -601,13 +606,13 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
     const __bf16* krow = reinterpret_cast<const __bf16*>(a.k) + (int64_t)kk * a.kv_stride + (int64_t)g * a.kv_hstride;
     const __bf16* vrow = reinterpret_cast<const __bf16*>(a.v) + (int64_t)kk * a.kv_stride + (int64_t)g * a.kv_hstride;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
+    for (int ks = 0; ks < KQ; ++ks) {
       const int d0 = 16 * ks + 8 * h;
       bf16x8 x = {}, y = {};
       if (d0 < D) {
         x = *reinterpret_cast<const bf16x8*>(krow + d0);
         y = *reinterpret_cast<const bf16x8*>(vrow + d0);
-      } else if (d0 == D) {
+      } else if (!DMA && d0 == D) {
         x[0] = x[1] = y[0] = y[1] = (__bf16)1.0f;
       }
       if (!kvalid[kb]) x = y = (bf16x8){};
@@ -702,8 +707,8 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
       load_lds16(rs, tile + J * 64 * 8, ld_off[k]);
     }
   };
-  // augmented values of row tid (tid < TQ) of a tile: loaded when its slots
-  // are issued, written to LDS at the end of the tile being computed
+  // accumulator initial values of row tid (tid < TQ) of a tile: loaded when
+  // its slots are issued, written to LDS at the end of the tile being computed
   float aug_lse = 0.f, aug_delta = 0.f;
   bool aug_ok = false;
   auto load_aug = [&](const QRun& r) {
@@ -717,20 +722,15 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
   };
   auto store_aug = [&](int b) {
     if (tid < TQ) {
-      __bf16 q0 = 0, q1 = 0, o0 = 0, o1 = 0;
+      float q = 0.f, o = 0.f;
       if (aug_ok) {
         float l2 = aug_lse * kLog2e;
         if ((__float_as_uint(l2) & 0x7f800000u) == 0x7f800000u) l2 = 0.f;  // no key: -inf (bit test)
-        split_bf16(-l2 * cinv, q0, q1);
-        split_bf16(-aug_delta, o0, o1);
+        q = PRESCALED ? -l2 : -l2 * cinv;
+        o = -aug_delta;
       }
-      // element 0 (column D) in the low half, as a b128 row read would see it
-      auto pack2 = [](__bf16 lo, __bf16 hi) {
-        return (uint32_t)__builtin_bit_cast(unsigned short, lo) |
-               ((uint32_t)__builtin_bit_cast(unsigned short, hi) << 16);
-      };
-      Qa[b][tid] = pack2(q0, q1);
-      Oa[b][tid] = pack2(o0, o1);
+      Qa[b][tid] = q;
+      Oa[b][tid] = o;
     }
   };
   // End of a tile: this wave's LPW loads of the tile after next may stay in
@@ -812,43 +812,47 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
                       (!(cur.type & MAGI_MASK_INVCAUSAL) || k0 >= cur.loff + cur.t0 + TQT - 1);
     const __bf16* Qb = Qs[buf];
     const __bf16* Ob = Os[buf];
-    const uint32_t* Qab = Qa[buf];
-    const uint32_t* Oab = Oa[buf];
+    const float* Qab = Qa[buf];
+    const float* Oab = Oa[buf];
     const __attribute__((address_space(3))) __bf16* Qt = (const __attribute__((address_space(3))) __bf16*)Qs[buf];
     const __attribute__((address_space(3))) __bf16* Ot = (const __attribute__((address_space(3))) __bf16*)Os[buf];
 #pragma unroll
     for (int rb = 0; rb < TQ / 32; ++rb) {
-      // S' = Q' . K^T and dP' = dO' . V^T (rows on M, keys on N); the A
-      // operands are read once for all KB key blocks
+      // S' = Q' . K^T - LSE2 and dP' = dO' . V^T - delta (rows on M, keys
+      // on N); the A operands are read once for all KB key blocks.  DMA: the
+      // accumulators start from the rows' values (element i holds row
+      // 8 (i / 4) + 4 h + i % 4 of this 32-row block, so 4 b128 reads each);
+      // registers: from zero, the values riding in the augmented columns
       f32x16 s[KB], dp[KB];
+      if constexpr (!DMA) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) s[kb] = dp[kb] = (f32x16){};
+        for (int kb = 0; kb < KB; ++kb) s[kb] = dp[kb] = (f32x16){};
+      } else {
+        f32x16 s0, d0;
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        // columns 16 ks + 8 h .. + 7: tile data below D, the augmented pair
-        // at D, D + 1 (DMA: from its own array), zeros above
+        for (int q = 0; q < 4; ++q) {
+          const float4 x = *reinterpret_cast<const float4*>(&Qab[rb * 32 + 8 * q + 4 * h]);
+          const float4 y = *reinterpret_cast<const float4*>(&Oab[rb * 32 + 8 * q + 4 * h]);
+          s0[4 * q] = x.x, s0[4 * q + 1] = x.y, s0[4 * q + 2] = x.z, s0[4 * q + 3] = x.w;
+          d0[4 * q] = y.x, d0[4 * q + 1] = y.y, d0[4 * q + 2] = y.z, d0[4 * q + 3] = y.w;
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) s[kb] = s0, dp[kb] = d0;
+      }
+      static_assert(!DMA || D % 16 == 0, "direct-loaded tiles hold whole k-steps");
+#pragma unroll
+      for (int ks = 0; ks < KQ; ++ks) {
+        // columns 16 ks + 8 h .. + 7: tile data below D; registers: the
+        // augmented pair at D, D + 1, zeros above
         const int row = rb * 32 + ln;
         bf16x8 qa, oa;
         if (!DMA) {
           qa = *reinterpret_cast<const bf16x8*>(&Qb[row * QP + 16 * ks + 8 * h]);
           oa = *reinterpret_cast<const bf16x8*>(&Ob[row * QP + 16 * ks + 8 * h]);
-        } else if (16 * ks + 16 <= D) {
+        } else {
           const int col = ((2 * ks + h) ^ tile_swizzle(row)) * 8;
           qa = *reinterpret_cast<const bf16x8*>(&Qb[row * QP + col]);
           oa = *reinterpret_cast<const bf16x8*>(&Ob[row * QP + col]);
-        } else {
-          const bf16x8 qaug = __builtin_bit_cast(bf16x8, (u32x4){Qab[row], 0u, 0u, 0u});
-          const bf16x8 oaug = __builtin_bit_cast(bf16x8, (u32x4){Oab[row], 0u, 0u, 0u});
-          static_assert(!DMA || D % 16 == 0, "the mixed data/augmented step is read unswizzled");
-          if (16 * ks + 8 == D) {  // lane half 0 data, half 1 the augmented pair
-            const bf16x8 qd = *reinterpret_cast<const bf16x8*>(&Qb[row * QP + 16 * ks]);
-            const bf16x8 od = *reinterpret_cast<const bf16x8*>(&Ob[row * QP + 16 * ks]);
-            qa = h ? qaug : qd;
-            oa = h ? oaug : od;
-          } else {  // 16 ks == D: half 0 the augmented pair, half 1 zeros
-            qa = h ? (bf16x8){} : qaug;
-            oa = h ? (bf16x8){} : oaug;
-          }
         }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -863,9 +867,9 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
         // slice or the item), lowered to key - loff - t0 + 1 under the
         // lower bound (top-left aligned: token t sees k >= loff + t); lo =
         // key - koff - t0 under the upper bound (bottom-right aligned: token
-        // t sees k < koff + t + 1).  The hiding mask is built by integer
-        // arithmetic and applied with a bit select, so no lane-mask
-        // registers are tied up.
+        // t sees k < koff + t + 1).  With both clamped to [0, TQT] that is
+        // lo G <= row < hi G, one unsigned compare of row - lo G against
+        // (hi - lo) G, with no per-row constants kept across tiles.
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const bool kin = kvalid[kb] && key[kb] >= cur.ks && key[kb] < cur.ke;
@@ -874,14 +878,14 @@ __global__ __launch_bounds__(2 * kKeys / KB, D == 24 ? 3 : 2) void bwd_dkdv_bf16
             const int32_t e = key[kb] - cur.loff - cur.t0 + 1;
             hi = e < hi ? e : hi;
           }
-          const int32_t lo = (cur.type & MAGI_MASK_CAUSAL) ? key[kb] - cur.koff - cur.t0 : -(1 << 30);
+          int32_t lo = (cur.type & MAGI_MASK_CAUSAL) ? key[kb] - cur.koff - cur.t0 : 0;
+          lo = lo < 0 ? 0 : (lo > TQT ? TQT : lo);
+          hi = hi < lo ? lo : hi;  // hi <= ntok <= TQT
+          const int32_t off = rb * 32 + 4 * h - lo * G;
+          const uint32_t span = (uint32_t)((hi - lo) * G);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int row = rb * 32 + 8 * (i / 4) + 4 * h + (i % 4);  // < 64
-            const int32_t tt = (row * ginv) >> 16;                    // row / G
-            const uint32_t hide = (uint32_t)(((tt - lo) | (hi - 1 - tt)) >> 31);
-            s[kb][i] = __uint_as_float((__float_as_uint(s[kb][i]) & ~hide) | (0xff800000u & hide));
-          }
+          for (int i = 0; i < 16; ++i)
+            if ((uint32_t)(off + 8 * (i / 4) + (i % 4)) >= span) s[kb][i] = -INFINITY;
         }
       }
       // P and dS = P * dP', rounded to bf16 in the B-operand layout
