@@ -3,6 +3,9 @@
 //   exp    v_exp_f32 throughput (the softmax's transcendental)
 //   cvt    v_cvt_pk_bf16_f32 throughput (P rounded to bf16 pairs)
 //   mixed  one MFMA wave and one exp wave per SIMD side by side
+//   inwave every wave issues both: 4 MFMAs and 16 exps per iteration, the
+//          exps independent of the MFMAs, in the compiler's order or pinned
+//          to MFMA, 4 exps, MFMA, 4 exps, ...
 // and the shader clock while the MFMA probe runs (shader-clock counter
 // against the 100 MHz real-time counter).  Prints one JSON object per probe.
 //
@@ -125,6 +128,38 @@ __global__ __launch_bounds__(256) void mixed_probe(int iters, float* sink) {
   sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Every wave: 4 MFMAs (independent chains) and 16 exps (8 chains, two
+// steps each) per iteration, the exps reading none of the MFMA results.
+// PIN fixes the issue order to one MFMA then 4 exps, four times.
+template <bool PIN>
+__global__ __launch_bounds__(256) void inwave_probe(int iters, float* sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (lane + i));
+    b[i] = (__bf16)(0.002f * (lane - i));
+  }
+  f32x16 c[4] = {{}, {}, {}, {}};
+  float x[8];
+  for (int i = 0; i < 8; ++i) x[i] = 0.001f * (threadIdx.x + i);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[(4 * j + i) & 7] = __builtin_amdgcn_exp2f(-x[(4 * j + i) & 7]);
+      if constexpr (PIN) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x400, 4, 0);  // then four transcendentals
+      }
+    }
+  }
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i) s += c[0][i] + c[1][i] + c[2][i] + c[3][i];
+  for (int i = 0; i < 8; ++i) s += x[i];
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 template <typename F>
 float time_ms(F launch, int reps) {
   hipEvent_t a, b;
@@ -190,6 +225,15 @@ int main(int argc, char** argv) {
   std::printf("{\"probe\": \"mixed_mfma_exp\", \"ms\": %.4f, \"mfma_alone_half_waves_ms\": %.4f, "
               "\"exp_alone_equiv_ms\": %.4f}\n",
               t_mix, t_mfma / 2, t_exp);
+  // in-wave: each wave does the MFMA probe's 4 MFMAs and twice the exp
+  // probe's 8 exps per iteration
+  const float t_in0 =
+      time_ms([&] { hipLaunchKernelGGL(inwave_probe<false>, dim3(blocks), dim3(256), 0, 0, iters, sink); }, reps);
+  const float t_in1 =
+      time_ms([&] { hipLaunchKernelGGL(inwave_probe<true>, dim3(blocks), dim3(256), 0, 0, iters, sink); }, reps);
+  std::printf("{\"probe\": \"inwave_mfma_exp\", \"ms_compiler_order\": %.4f, \"ms_pinned_order\": %.4f, "
+              "\"mfma_alone_ms\": %.4f, \"exp_alone_ms\": %.4f}\n",
+              t_in0, t_in1, t_mfma, 2 * t_exp);
   CHECK(hipFree(sink));
   CHECK(hipFree(clk));
   return 0;
