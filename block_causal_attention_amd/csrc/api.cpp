@@ -189,8 +189,9 @@ int32_t ffa_fwd_args(FfaArgs& a, const void* q, const void* k, const void* v, vo
   return MAGI_OK;
 }
 
-int32_t launch(const FfaArgs& a, void* stream) {
-  const hipError_t e = launch_ffa_fwd(a, reinterpret_cast<hipStream_t>(stream));
+int32_t launch(const FfaArgs& a, void* stream, void* start = nullptr, void* stop = nullptr) {
+  const hipError_t e = launch_ffa_fwd(a, reinterpret_cast<hipStream_t>(stream), reinterpret_cast<hipEvent_t>(start),
+                                      reinterpret_cast<hipEvent_t>(stop));
   if (e != hipSuccess) return fail(MAGI_ERR_HIP, "ffa_fwd launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -210,6 +211,21 @@ extern "C" int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, voi
                                   num_slices, work, num_work, tile_slices, num_tile_slices);
   if (st != MAGI_OK) return st;
   return launch(a, stream);
+}
+
+extern "C" int32_t magi_ffa_fwd_timed(const void* q, const void* k, const void* v, void* out, float* lse,
+                                      int64_t nq, int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim,
+                                      int32_t dtype, int64_t q_tok_stride, int64_t kv_tok_stride,
+                                      int64_t kv_head_stride, int64_t o_tok_stride, float softmax_scale,
+                                      const float* k_norm_max, const magi_attn_slice* slices, int32_t num_slices,
+                                      const magi_work_item* work, int32_t num_work, const int32_t* tile_slices,
+                                      int32_t num_tile_slices, void* stream, void* start_event, void* stop_event) {
+  FfaArgs a;
+  const int32_t st = ffa_fwd_args(a, q, k, v, out, lse, nq, nk, hq, hkv, head_dim, dtype, q_tok_stride,
+                                  kv_tok_stride, kv_head_stride, o_tok_stride, softmax_scale, k_norm_max, slices,
+                                  num_slices, work, num_work, tile_slices, num_tile_slices);
+  if (st != MAGI_OK) return st;
+  return launch(a, stream, start_event, stop_event);
 }
 
 extern "C" int32_t magi_ffa_fwd_qknorm(const void* q_raw, const void* k, const void* v, void* out, float* lse,

@@ -36,6 +36,7 @@
 //  * Softmax in fp32 in the log2 domain against a fixed per-row reference
 //    (a bound from the key norms when the caller supplies one, else an
 //    online max that moves only by large steps), exp via v_exp_f32.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -647,9 +648,11 @@ __global__ __launch_bounds__(kThreads) void ffa_fwd_f32(FfaArgs a) {
 
 }  // namespace
 
-hipError_t launch_ffa_fwd(const FfaArgs& a, hipStream_t stream) {
+hipError_t launch_ffa_fwd(const FfaArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (a.num_work == 0) return hipSuccess;
-  const dim3 grid(a.num_work), block(kThreads);
+  const dim3 grid(a.num_work);
+  dim3 block(kThreads);
+  void (*kern)(FfaArgs) = nullptr;
   if (a.dtype == MAGI_DTYPE_BF16) {
     // scores arrive in log2 units when the caller folded scale * log2(e) into Q or K
     const bool pre = fabsf(a.scale * kLog2e - 1.0f) < 1e-6f;
@@ -658,32 +661,23 @@ hipError_t launch_ffa_fwd(const FfaArgs& a, hipStream_t stream) {
     constexpr int NB24 = 2, NB48 = 1;
     const bool qn = a.qn_gain != nullptr;
     if (a.head_dim == 24) {
-      const dim3 block(2 * kRows / NB24);
-      if (qn && pre)
-        hipLaunchKernelGGL((ffa_fwd_bf16<24, true, NB24, true>), grid, block, 0, stream, a);
-      else if (qn)
-        hipLaunchKernelGGL((ffa_fwd_bf16<24, false, NB24, true>), grid, block, 0, stream, a);
-      else if (pre)
-        hipLaunchKernelGGL((ffa_fwd_bf16<24, true, NB24, false>), grid, block, 0, stream, a);
-      else
-        hipLaunchKernelGGL((ffa_fwd_bf16<24, false, NB24, false>), grid, block, 0, stream, a);
+      block = dim3(2 * kRows / NB24);
+      kern = qn ? (pre ? ffa_fwd_bf16<24, true, NB24, true> : ffa_fwd_bf16<24, false, NB24, true>)
+                : (pre ? ffa_fwd_bf16<24, true, NB24, false> : ffa_fwd_bf16<24, false, NB24, false>);
     } else {
-      const dim3 block(2 * kRows / NB48);
-      if (qn && pre)
-        hipLaunchKernelGGL((ffa_fwd_bf16<48, true, NB48, true>), grid, block, 0, stream, a);
-      else if (qn)
-        hipLaunchKernelGGL((ffa_fwd_bf16<48, false, NB48, true>), grid, block, 0, stream, a);
-      else if (pre)
-        hipLaunchKernelGGL((ffa_fwd_bf16<48, true, NB48, false>), grid, block, 0, stream, a);
-      else
-        hipLaunchKernelGGL((ffa_fwd_bf16<48, false, NB48, false>), grid, block, 0, stream, a);
+      block = dim3(2 * kRows / NB48);
+      kern = qn ? (pre ? ffa_fwd_bf16<48, true, NB48, true> : ffa_fwd_bf16<48, false, NB48, true>)
+                : (pre ? ffa_fwd_bf16<48, true, NB48, false> : ffa_fwd_bf16<48, false, NB48, false>);
     }
   } else {
-    if (a.head_dim == 24)
-      hipLaunchKernelGGL(ffa_fwd_f32<24>, grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL(ffa_fwd_f32<48>, grid, block, 0, stream, a);
+    kern = a.head_dim == 24 ? ffa_fwd_f32<24> : ffa_fwd_f32<48>;
   }
+  if (start != nullptr || stop != nullptr) {
+    FfaArgs arg = a;
+    void* args[] = {&arg};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, args, 0, stream, start, stop, 0);
+  }
+  hipLaunchKernelGGL(kern, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

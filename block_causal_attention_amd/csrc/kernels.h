@@ -63,7 +63,10 @@ struct FfaArgs {
   int32_t num_tile_slices;
 };
 
-hipError_t launch_ffa_fwd(const FfaArgs& a, hipStream_t stream);
+// With start/stop events the dispatch itself records them when the kernel
+// starts and when it completes (no marker packets of their own).
+hipError_t launch_ffa_fwd(const FfaArgs& a, hipStream_t stream, hipEvent_t start = nullptr,
+                          hipEvent_t stop = nullptr);
 
 struct BwdArgs {
   const void* q;

@@ -420,13 +420,17 @@ class QNorm:
 def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
             softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
             lse: Optional[torch.Tensor] = None, return_lse: bool = True,
-            k_norm_max: Optional[torch.Tensor] = None, qnorm: Optional[QNorm] = None):
+            k_norm_max: Optional[torch.Tensor] = None, qnorm: Optional[QNorm] = None,
+            events: Optional[tuple] = None):
     """magi_ffa_fwd over ``plan``; returns (out [nq, hq, d], lse [nq, hq] fp32 or None).
     ``k_norm_max`` (float32 [hkv], optional) must bound the norm of every key
     row of each group (qknorm_rope writes one).  k and v are [nk, hkv, d]
     views with contiguous channels and one common layout (token-major, or
     group-major as from kv_group_major).  With ``qnorm`` q is the raw Q and
-    the kernel applies QK-Norm + 3D RoPE to it (magi_ffa_fwd_qknorm)."""
+    the kernel applies QK-Norm + 3D RoPE to it (magi_ffa_fwd_qknorm).
+    ``events`` (start, stop): torch.cuda.Event objects with timing enabled,
+    each recorded once before (so that the HIP event exists); the kernel's
+    dispatch records them when it starts and ends (magi_ffa_fwd_timed)."""
     d = q.shape[-1]
     hq, hkv = q.shape[1], k.shape[1]
     _check_3d("q", q, hq, d)
@@ -450,6 +454,14 @@ def ffa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, plan: Plan,
             0.0 if softmax_scale is None else float(softmax_scale), _ptr(k_norm_max),
             _ptr(plan.slices), int(plan.host["slices"].shape[0]), _ptr(plan.work), plan.num_work,
             _ptr(plan.tile_slices), int(plan.host["tile_slices"].shape[0]))
+    if events is not None:
+        if qnorm is not None:
+            raise ValueError("events and qnorm cannot be combined")
+        handles = [e.cuda_event for e in events]
+        if len(handles) != 2 or not all(handles):
+            raise ValueError("events must be two torch.cuda.Event objects that have been recorded once")
+        check(lib().magi_ffa_fwd_timed(*args, _stream(q), handles[0], handles[1]))
+        return out, lse
     if qnorm is None:
         check(lib().magi_ffa_fwd(*args, _stream(q)))
         return out, lse

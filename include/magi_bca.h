@@ -365,6 +365,33 @@ int32_t magi_ffa_fwd(const void* q, const void* k, const void* v, void* out, flo
                      void* stream);
 
 /*
+ * magi_ffa_fwd_timed -- magi_ffa_fwd whose launch also records two HIP
+ * events.                                                  [device, async]
+ *
+ * The same operation as magi_ffa_fwd (study notes, "训练 Infra",
+ * Flex-Flash-Attention bullet), for callers that time the kernel: the
+ * kernel's dispatch itself records start_event when the kernel starts and
+ * stop_event when it completes, so hipEventElapsedTime(start, stop) is the
+ * kernel's duration and the stream holds no marker packets of its own
+ * around it (recording the events separately adds about 8 us of idle GPU
+ * time per launch on the 4.5B-shaped layer).
+ *
+ * All arguments of magi_ffa_fwd, plus:
+ * start_event, stop_event  hipEvent_t created by the caller with timing
+ *              enabled, or NULL (no event); both recorded on `stream`.  The
+ *              caller keeps ownership.
+ * Errors as magi_ffa_fwd; a launch error is MAGI_ERR_HIP.
+ */
+int32_t magi_ffa_fwd_timed(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int64_t nq, int64_t nk, int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
+                           int64_t q_tok_stride, int64_t kv_tok_stride, int64_t kv_head_stride,
+                           int64_t o_tok_stride, float softmax_scale, const float* k_norm_max,
+                           const magi_attn_slice* slices, int32_t num_slices,
+                           const magi_work_item* work, int32_t num_work,
+                           const int32_t* tile_slices, int32_t num_tile_slices,
+                           void* stream, void* start_event, void* stop_event);
+
+/*
  * magi_ffa_fwd_qknorm -- magi_ffa_fwd with the QK-Norm + 3D RoPE of Q done
  * inside the attention kernel.                          [device, async]
  *

@@ -455,6 +455,34 @@ def test_kv_layouts_give_identical_results(d, bound):
     assert torch.equal(O1, O2) and torch.equal(L1, L2)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_timed_forward_identical_and_events_bracket_kernel(dtype):
+    # magi_ffa_fwd_timed launches the same kernel, so the outputs agree bit
+    # for bit; the events its dispatch records give a positive duration no
+    # longer than the host's wall time around the call
+    import time
+    note(f"ffa timed entry point {dtype}")
+    d, hkv, G = 24, 2, 16
+    seqs = [W.SeqDesc(70, 3, 3, 0, 0, (-1, -1, 1), 1, 1, 70)]
+    plan = ops.make_plan(ops.build_slices(seqs), 210, 210, G * hkv, hkv, d, dtype)
+    q, k, v = (torch.from_numpy(x).to(dtype).to(DEV) for x in
+               (rand((210, G * hkv, d), 50), rand((210, hkv, d), 51), rand((210, hkv, d), 52)))
+    O1, L1 = ops.ffa_fwd(q, k, v, plan)
+    evs = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    O2, L2 = ops.ffa_fwd(q, k, v, plan, events=evs)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+    ms = evs[0].elapsed_time(evs[1])
+    assert 0.0 < ms <= wall_ms
+    with pytest.raises(ValueError):
+        ops.ffa_fwd(q, k, v, plan, events=(torch.cuda.Event(enable_timing=True),) * 2)  # never recorded
+
+
 def test_kv_layouts_fp32_identical():
     note("ffa fp32 K/V group-major vs token-major")
     wl = W.make_workload("tiny")

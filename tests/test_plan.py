@@ -23,7 +23,7 @@ def header_functions():
 def test_library_exports_every_header_symbol():
     L = _lib.lib()
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -515,6 +515,24 @@ def test_fused_forward_entry_validates_q_prologue():
     assert fq(eps=-1.0) == _lib.MAGI_ERR_INVALID_ARG
     assert fq(qsc=0.0) == _lib.MAGI_ERR_INVALID_ARG
     assert fq(qhat=p, qhs=100) == _lib.MAGI_ERR_INVALID_ARG   # q_hat row stride < heads * d
+
+
+def test_timed_forward_entry_validates_like_the_forward():
+    """magi_ffa_fwd_timed checks its arguments exactly as magi_ffa_fwd, before
+    any HIP call (the events are never touched when validation fails)."""
+    L = _lib.lib()
+    p = C.c_void_p(4096)  # never dereferenced: every call below fails validation
+
+    def ft(**kw):
+        a = dict(q=p, nq=16, kvs=24, scale=0.0, w=p, ev=p)
+        a.update(kw)
+        return L.magi_ffa_fwd_timed(a["q"], p, p, p, None, a["nq"], 16, 16, 1, 24, 0, 384, a["kvs"], 24, 384,
+                                    a["scale"], None, p, 1, a["w"], 1, p, 1, None, a["ev"], a["ev"])
+    assert ft(q=None) == _lib.MAGI_ERR_INVALID_ARG
+    assert ft(kvs=20) == _lib.MAGI_ERR_INVALID_ARG
+    assert ft(scale=float("nan")) == _lib.MAGI_ERR_INVALID_ARG
+    assert ft(w=None) == _lib.MAGI_ERR_INVALID_ARG
+    assert ft(nq=-2, ev=None) == _lib.MAGI_ERR_INVALID_ARG
 
 
 def test_backward_entry_validates_split_workspace():
