@@ -143,6 +143,20 @@ def window_pairs(wl, window) -> int:
 LAST_LAUNCHES_MS = []  # per-launch attention times of the last run_gpu call
 
 
+def event_pool(steps, stream):
+    """Timing event pairs for ``steps`` attention launches, to be recorded by
+    the kernel's own dispatch (ops.ffa_fwd(..., events=pair), i.e.
+    magi_ffa_fwd_timed), so that no marker packets of their own sit between
+    the kernels; each is recorded once here, so that the HIP event exists
+    before it is handed to the library."""
+    import torch
+    pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for pair in pool:
+        for e in pair:
+            e.record(stream)
+    return pool
+
+
 def run_gpu(wl, steps, warmup, seed=0, window=None):
     """One step = plan build and upload, prologue, forward.  With ``window``
     the mask is causal sliding-window attention of that many tokens over
@@ -169,14 +183,7 @@ def run_gpu(wl, steps, warmup, seed=0, window=None):
 
     spec = None if window is None else [(s.num_q_chunks * s.chunk_len, window, s.q_offset, s.k_offset)
                                          for s in wl.seqs]
-    # Timing events of the timed steps, recorded by the attention kernel's
-    # own dispatch (magi_ffa_fwd_timed), so that no marker packets of their
-    # own sit between the kernels; each is recorded once here, so that the
-    # HIP event exists before it is handed to the library.
-    pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for pair in pool:
-        for e in pair:
-            e.record(stream)
+    pool = event_pool(steps, stream)
 
     # A streaming step's cached keys and values were processed by earlier
     # steps: they are written once here, and a step's prologue covers the
@@ -284,23 +291,19 @@ def run_cross(wl, steps, warmup, seed=0):
     lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     ev = []
+    pool = event_pool(steps, stream)
 
     def step(record):
         sl = ops.build_cross_slices([(0, wl.nq, 0, TEXT_TOKENS)])
         plan = ops.make_plan(sl, wl.nq, TEXT_TOKENS, wl.hq, wl.hkv, wl.head_dim, q.dtype, dev)
         ops.qknorm_rope(q, k, gq, gk, zq, zk, base, wl.eps, q_out=qh, k_out=kh,
                         k_scale=wl.softmax_scale * ops.LOG2E, k_norm_max=knm, v=v, v_out=vh)
+        # the events bracket the attention kernel alone (the wait for the
+        # plan upload comes before it, inside the step time)
+        evs = pool[len(ev)] if record else None
+        ops.ffa_fwd(qh, kh, vh, plan, out=out, lse=lse, softmax_scale=ops.LN2, k_norm_max=knm, events=evs)
         if record:
-            # the wait for the plan upload (a side stream) goes before the
-            # start event, so that the events bracket the attention kernel
-            # alone; the step time still includes it
-            plan.wait(stream)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-        ops.ffa_fwd(qh, kh, vh, plan, out=out, lse=lse, softmax_scale=ops.LN2, k_norm_max=knm)
-        if record:
-            b.record(stream)
-            ev.append((a, b))
+            ev.append(evs)
 
     with steady_timing():
         warm_up(step, warmup)
@@ -464,6 +467,7 @@ def run_ring(steps, warmup, seed=0):
     stream = torch.cuda.current_stream()
     runs = ops.ring_slot_runs(S, first + count - n, n)
     ev = []
+    pool = event_pool(steps, stream)
     visible = 0
 
     def step(record):
@@ -479,16 +483,14 @@ def run_ring(steps, warmup, seed=0):
                             k_scale=scale * ops.LOG2E, k_norm_max=knm, v=vnew[done * C:(done + m) * C],
                             v_out=ring_v[s0 * C:(s0 + m) * C])
             done += m
-        if record:
-            plan.wait(stream)  # the upload wait stays outside the kernel's events
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
         # the bound on key norms follows from the QK-Norm gains, so it holds
-        # for the cached keys as well as for this step's
-        ops.ffa_fwd(qh, ring_k, ring_v, plan, out=out, lse=lse, softmax_scale=ops.LN2, k_norm_max=knm)
+        # for the cached keys as well as for this step's; the events bracket
+        # the kernel alone (the upload wait comes before it)
+        evs = pool[len(ev)] if record else None
+        ops.ffa_fwd(qh, ring_k, ring_v, plan, out=out, lse=lse, softmax_scale=ops.LN2, k_norm_max=knm,
+                    events=evs)
         if record:
-            b.record(stream)
-            ev.append((a, b))
+            ev.append(evs)
 
     with steady_timing():
         warm_up(step, warmup)
