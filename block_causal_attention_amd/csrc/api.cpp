@@ -350,8 +350,8 @@ int32_t bwd_args(BwdArgs& a, const void* q, const void* k, const void* v, const 
 // needs: 2 (dK, dV) x 128 keys x head_dim per slot, the dK/dV kernel's layout
 int64_t partial_need(int32_t num_slots, int32_t head_dim) { return (int64_t)num_slots * 2 * 128 * head_dim; }
 
-int32_t bwd_launch(const BwdArgs& a, void* stream) {
-  const hipError_t e = launch_ffa_bwd(a, reinterpret_cast<hipStream_t>(stream));
+int32_t bwd_launch(const BwdArgs& a, void* stream, bool two_streams) {
+  const hipError_t e = launch_ffa_bwd(a, reinterpret_cast<hipStream_t>(stream), two_streams);
   if (e != hipSuccess) return fail(MAGI_ERR_HIP, "ffa_bwd launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -386,7 +386,7 @@ extern "C" int32_t magi_ffa_bwd(const void* q, const void* k, const void* v, con
   }
   a.delta = delta;
   a.partial = partial;
-  return bwd_launch(a, stream);
+  return bwd_launch(a, stream, true);
 }
 
 extern "C" int32_t magi_ffa_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
@@ -419,5 +419,5 @@ extern "C" int32_t magi_ffa_bwd_noalloc(const void* q, const void* k, const void
   if (e != hipSuccess) return fail(MAGI_ERR_HIP, "scratch lookup: %s", hipGetErrorString(e));
   a.delta = base;
   a.partial = base + delta_floats;
-  return bwd_launch(a, stream);
+  return bwd_launch(a, stream, false);
 }

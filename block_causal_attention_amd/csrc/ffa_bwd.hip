@@ -32,6 +32,8 @@
 // a multiple of 16: 24 -> 32 (free), 48 -> 64.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "ffa_common.h"
 #include "kernels.h"
 
@@ -1189,8 +1191,44 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
   dst[3] = (T)acc.w;
 }
 
+// The side stream and the two events that fork it from the caller's stream
+// and join it back, one set per device, created on first use and kept until
+// the process ends.  The lock spans a whole launch sequence, so that each
+// wait pairs with the record just before it even when several host threads
+// launch backward passes at once.
+struct SideStream {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+hipError_t side_stream_for(hipStream_t stream, SideStream** out) {
+  int dev = 0;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream& s = g_side[dev];
+  if (s.side == nullptr) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    SideStream t;
+    e = hipStreamCreateWithFlags(&t.side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&t.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&t.join, hipEventDisableTiming);
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
+    s = t;
+  }
+  *out = &s;
+  return hipSuccess;
+}
+
 template <int D>
-hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_d(const BwdArgs& a, hipStream_t stream, bool two_streams) {
   constexpr int KB = D == 24 ? KB24 : KB48;
   constexpr int RBQ = D == 24 ? RBQ24 : RBQ48;
   const bool bf = a.dtype == MAGI_DTYPE_BF16;
@@ -1203,39 +1241,62 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((bwd_delta<D, float>), grid, dim3(256), 0, stream, a);
   }
   const bool pre = fabsf(a.scale * kLog2e - 1.0f) < 1e-6f;
-  if (a.num_qwork > 0) {
+  auto dq_pass = [&](hipStream_t s) {
     const dim3 grid(a.num_qwork);
     if (!bf)
-      hipLaunchKernelGGL((bwd_dq_f32<D>), grid, dim3(kThreads32), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_f32<D>), grid, dim3(kThreads32), 0, s, a);
     else if (pre)
-      hipLaunchKernelGGL((bwd_dq_bf16<D, true, RBQ>), grid, dim3(NT / RBQ), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_bf16<D, true, RBQ>), grid, dim3(NT / RBQ), 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_dq_bf16<D, false, RBQ>), grid, dim3(NT / RBQ), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_bf16<D, false, RBQ>), grid, dim3(NT / RBQ), 0, s, a);
+  };
+  // the dK/dV pass, then the sums of its split key tiles
+  auto dkdv_pass = [&](hipStream_t s) {
+    if (a.num_kwork > 0) {
+      const dim3 grid(a.num_kwork);
+      if (!bf)
+        hipLaunchKernelGGL((bwd_dkdv_f32<D>), grid, dim3(kThreads32), 0, s, a);
+      else if (pre)
+        hipLaunchKernelGGL((bwd_dkdv_bf16<D, true, KB>), grid, dim3(2 * kKeys / KB), 0, s, a);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_bf16<D, false, KB>), grid, dim3(2 * kKeys / KB), 0, s, a);
+    }
+    if (a.num_reduce > 0) {
+      // gridDim.y covers the 2 x kKeys x D / 4 float4 outputs of a full tile
+      const dim3 grid(a.num_reduce, (2 * kKeys * (D / 4) + 255) / 256);
+      if (bf)
+        hipLaunchKernelGGL((bwd_reduce<D, __bf16>), grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((bwd_reduce<D, float>), grid, dim3(256), 0, s, a);
+    }
+  };
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (two_streams && a.num_qwork > 0 && (a.num_kwork > 0 || a.num_reduce > 0)) {
+    // The two passes read the same inputs and write disjoint outputs, so
+    // they may run at once: the side stream takes the dK/dV pass after
+    // delta, and `stream` waits for it after the dQ pass.
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* ss = nullptr;
+    if ((e = side_stream_for(stream, &ss)) != hipSuccess) return e;
+    if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ss->side, ss->fork, 0)) != hipSuccess) return e;
+    dkdv_pass(ss->side);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipEventRecord(ss->join, ss->side)) != hipSuccess) return e;
+    dq_pass(stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return hipStreamWaitEvent(stream, ss->join, 0);
   }
-  if (a.num_kwork > 0) {
-    const dim3 grid(a.num_kwork);
-    if (!bf)
-      hipLaunchKernelGGL((bwd_dkdv_f32<D>), grid, dim3(kThreads32), 0, stream, a);
-    else if (pre)
-      hipLaunchKernelGGL((bwd_dkdv_bf16<D, true, KB>), grid, dim3(2 * kKeys / KB), 0, stream, a);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_bf16<D, false, KB>), grid, dim3(2 * kKeys / KB), 0, stream, a);
-  }
-  if (a.num_reduce > 0) {
-    // gridDim.y covers the 2 x kKeys x D / 4 float4 outputs of a full tile
-    const dim3 grid(a.num_reduce, (2 * kKeys * (D / 4) + 255) / 256);
-    if (bf)
-      hipLaunchKernelGGL((bwd_reduce<D, __bf16>), grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((bwd_reduce<D, float>), grid, dim3(256), 0, stream, a);
-  }
+  if (a.num_qwork > 0) dq_pass(stream);
+  dkdv_pass(stream);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_ffa_bwd(const BwdArgs& a, hipStream_t stream) {
-  return a.head_dim == 24 ? launch_d<24>(a, stream) : launch_d<48>(a, stream);
+hipError_t launch_ffa_bwd(const BwdArgs& a, hipStream_t stream, bool two_streams) {
+  return a.head_dim == 24 ? launch_d<24>(a, stream, two_streams) : launch_d<48>(a, stream, two_streams);
 }
 
 }  // namespace magi

@@ -101,7 +101,11 @@ struct BwdArgs {
   float* partial;                // [num_slots][2][kKeys][head_dim] fp32 (dK, then dV)
 };
 
-hipError_t launch_ffa_bwd(const BwdArgs& a, hipStream_t stream);
+// With two_streams the dK/dV pass and its reduce run on a side stream of the
+// library (one per device, default priority, created on first use) beside
+// the dQ pass on `stream`; `stream` waits for them before it returns to the
+// caller's later work.  Without, all launches go to `stream` in order.
+hipError_t launch_ffa_bwd(const BwdArgs& a, hipStream_t stream, bool two_streams = false);
 
 // The static device workspace of the entry points that allocate nothing:
 // kScratchFloats fp32 values (64 MiB) per GPU, held until the process ends.

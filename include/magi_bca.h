@@ -512,6 +512,14 @@ int32_t magi_schedule_kv(const magi_attn_slice* slices, int32_t num_slices,
  *              128 x head_dim values, 16-byte aligned (caller owned, no
  *              contents needed), for the parts of split key tiles; a last
  *              launch sums them into dk, dv
+ * stream       the caller's stream.  delta and the dq pass run on it; the
+ *              dk/dv pass and its sums run at the same time on a side stream
+ *              of the library (one per device, default priority, created
+ *              with two events on the first call and kept until the process
+ *              ends), forked from `stream` after delta and joined back before
+ *              the call returns, so later work on `stream` sees dq, dk, dv.
+ *              Calls from several host threads are serialised around the
+ *              fork and join.
  * Supported: head_dim 24 or 48; hq % hkv == 0; hq/hkv <= 64;
  * kv_tok_stride, q_tok_stride and o_tok_stride < 2^23 (MAGI_ERR_UNSUPPORTED
  * otherwise).  Errors as magi_ffa_fwd.
